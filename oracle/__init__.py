@@ -1,0 +1,203 @@
+"""Plain CPU oracle (ctypes wrapper around ``oracle/oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package; the HIP library and
+its Python binding never do, and share no code with it.
+
+Every function takes bf16 inputs as ``numpy.uint16`` bit patterns (any
+strides) and returns freshly allocated numpy outputs in *logical* index order:
+``q[i, j]`` is the e4m3 byte of element ``(i, j)`` whatever memory layout the
+GPU writes.  The C code follows the definitions cited in ``oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
+             "-Wall", "-Wextra"]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile ``oracle.c`` with gcc into ``liboracle.so`` (always rebuilds)."""
+    cmd = ["gcc", *GCC_FLAGS, "-o", _LIB_PATH + ".tmp", _SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_decode.restype = ctypes.c_double
+    lib.oracle_e4m3_encode_array.argtypes = [_vp, _i64, _vp]
+    lib.oracle_e4m3_encode_array.restype = None
+    lib.oracle_fp32_scale.argtypes = [ctypes.c_float]
+    lib.oracle_fp32_scale.restype = ctypes.c_float
+    lib.oracle_e8m0_floor.argtypes = [ctypes.c_float]
+    lib.oracle_e8m0_floor.restype = ctypes.c_uint8
+    jag = [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _i64, _i64, _vp, _i64, _i64]
+    lib.oracle_quantize_jagged_rowwise.argtypes = jag
+    lib.oracle_quantize_jagged_colwise.argtypes = jag
+    lib.oracle_quantize_mx_3d_colwise.argtypes = [_vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                                  _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64]
+    lib.oracle_quantize_mx_rowwise.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64,
+                                               _vp, _i64, _i64]
+    lib.oracle_quantize_blockwise.argtypes = [_vp, _i64, _i64, _i64, _i64, _i32, _i32, _vp,
+                                              _i64, _i64, _vp, _i64, _i64]
+    for name in ("oracle_quantize_jagged_rowwise", "oracle_quantize_jagged_colwise",
+                 "oracle_quantize_mx_3d_colwise", "oracle_quantize_mx_rowwise",
+                 "oracle_quantize_blockwise"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _estrides(a: np.ndarray):
+    return tuple(s // a.itemsize for s in a.strides)
+
+
+def _check_bf16(x: np.ndarray, ndim: int) -> None:
+    if x.dtype != np.uint16 or x.ndim != ndim:
+        raise TypeError(f"expected a {ndim}-D uint16 (bf16 bit pattern) array, got {x.dtype} {x.shape}")
+
+
+def _call(status: int, what: str) -> None:
+    if status != 0:
+        raise ValueError(f"oracle rejected the arguments of {what}")
+
+
+# ------------------------------------------------------------------ numerics
+
+def e4m3_encode(y) -> np.ndarray:
+    """Saturating RNE encode of float32 values into E4M3FN bytes."""
+    y = np.ascontiguousarray(np.asarray(y, dtype=np.float32))
+    out = np.empty(y.shape, dtype=np.uint8)
+    _load().oracle_e4m3_encode_array(_ptr(y), y.size, _ptr(out))
+    return out
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    codes = np.asarray(codes, dtype=np.uint8)
+    lib = _load()
+    flat = [lib.oracle_e4m3_decode(int(c)) for c in codes.ravel()]
+    return np.array(flat, dtype=np.float64).reshape(codes.shape)
+
+
+def fp32_scale(amax) -> np.ndarray:
+    lib = _load()
+    a = np.asarray(amax, dtype=np.float32)
+    flat = [lib.oracle_fp32_scale(float(v)) for v in a.ravel()]
+    return np.array(flat, dtype=np.float32).reshape(a.shape)
+
+
+def e8m0_floor(amax) -> np.ndarray:
+    lib = _load()
+    a = np.asarray(amax, dtype=np.float32)
+    flat = [lib.oracle_e8m0_floor(float(v)) for v in a.ravel()]
+    return np.array(flat, dtype=np.uint8).reshape(a.shape)
+
+
+# ---------------------------------------------------------- quantization ops
+
+def quantize_jagged_rowwise(x: np.ndarray, offs, canary: int = 0):
+    """x: (rows, cols) bf16 bits, groups along dim 1.  Returns (q, scales)
+    with q (rows, cols) uint8 and scales (rows, G) float32.  Bytes in no group
+    (at or past offs[-1]) keep ``canary``."""
+    _check_bf16(x, 2)
+    offs = np.ascontiguousarray(np.asarray(offs, dtype=np.int32))
+    rows, cols = x.shape
+    G = offs.size
+    q = np.full((rows, cols), canary, dtype=np.uint8)
+    s = np.zeros((rows, G), dtype=np.float32)
+    sx = _estrides(x)
+    _call(_load().oracle_quantize_jagged_rowwise(_ptr(x), rows, cols, sx[0], sx[1], _ptr(offs), G,
+                                                 _ptr(q), cols, 1, _ptr(s), G, 1),
+          "jagged_rowwise")
+    return q, s
+
+
+def quantize_jagged_colwise(x: np.ndarray, offs, canary: int = 0):
+    """x: (rows, cols) bf16 bits, groups along dim 0.  Returns (q, scales)
+    with q (rows, cols) uint8 and scales (G, cols) float32."""
+    _check_bf16(x, 2)
+    offs = np.ascontiguousarray(np.asarray(offs, dtype=np.int32))
+    rows, cols = x.shape
+    G = offs.size
+    q = np.full((rows, cols), canary, dtype=np.uint8)
+    s = np.zeros((G, cols), dtype=np.float32)
+    sx = _estrides(x)
+    _call(_load().oracle_quantize_jagged_colwise(_ptr(x), rows, cols, sx[0], sx[1], _ptr(offs), G,
+                                                 _ptr(q), cols, 1, _ptr(s), cols, 1),
+          "jagged_colwise")
+    return q, s
+
+
+def quantize_mx_3d_colwise(w: np.ndarray):
+    """w: (E, N, K) bf16 bits.  Returns q (E, N, K) uint8 and e8m0 scales
+    (E, N/32, K) uint8, both in logical index order."""
+    _check_bf16(w, 3)
+    E, N, K = w.shape
+    q = np.zeros((E, N, K), dtype=np.uint8)
+    s = np.zeros((E, N // 32, K), dtype=np.uint8)
+    sw = _estrides(w)
+    _call(_load().oracle_quantize_mx_3d_colwise(_ptr(w), E, N, K, sw[0], sw[1], sw[2], _ptr(q),
+                                                N * K, K, 1, _ptr(s), (N // 32) * K, K, 1),
+          "mx_3d_colwise")
+    return q, s
+
+
+def quantize_mx_rowwise(x: np.ndarray):
+    """x: (rows, cols) bf16 bits, 1x32 blocks along dim 1.  Returns q (rows,
+    cols) uint8 and e8m0 scales (rows, cols/32) uint8."""
+    _check_bf16(x, 2)
+    rows, cols = x.shape
+    q = np.zeros((rows, cols), dtype=np.uint8)
+    s = np.zeros((rows, cols // 32), dtype=np.uint8)
+    sx = _estrides(x)
+    _call(_load().oracle_quantize_mx_rowwise(_ptr(x), rows, cols, sx[0], sx[1], _ptr(q), cols, 1,
+                                             _ptr(s), cols // 32, 1),
+          "mx_rowwise")
+    return q, s
+
+
+def quantize_blockwise(x: np.ndarray, block_r: int, block_c: int):
+    """x: (rows, cols) bf16 bits, block_r x block_c blocks.  Returns q (rows,
+    cols) uint8 and scales (rows/block_r, cols/block_c) float32."""
+    _check_bf16(x, 2)
+    rows, cols = x.shape
+    q = np.zeros((rows, cols), dtype=np.uint8)
+    nrb, ncb = rows // block_r, cols // block_c
+    s = np.zeros((nrb, ncb), dtype=np.float32)
+    sx = _estrides(x)
+    _call(_load().oracle_quantize_blockwise(_ptr(x), rows, cols, sx[0], sx[1], block_r, block_c,
+                                            _ptr(q), cols, 1, _ptr(s), ncb, 1),
+          "blockwise")
+    return q, s
