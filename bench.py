@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of the fp8 quantization hot path on one MI355X.
+
+Default workload (``moe_bwd``): the MoE backward grad_weight operands — jagged
+rowwise quantization of grad_out^T (4096, 16384) plus jagged colwise
+quantization of x (16384, 4096), the same 8 token groups for both, bf16 in,
+e4m3 + fp32 per-group scales out.  One step = both launches.  Other
+workloads (``--workload``): ``mx3d`` (E=8 expert weights, 32x1 MXFP8),
+``mx3d_e{1,2,4,16,64}``, ``blockwise`` (1x128 activations + 128x128 weights).
+
+Metric: algorithmic HBM bytes (2 B bf16 read + 1 B e4m3 write + scale bytes
+per launch) divided by time.  Inputs are resident in HBM before the timed
+region; outputs are preallocated; every launch goes through the C ABI.
+
+Prints one JSON line (rank 0).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0
+METRIC = "achieved HBM GB/s (bf16 read + fp8/scale write) and % of MI355X peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="moe_bwd")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-rows", type=int, default=0,
+                   help="rows/columns per tensor for the CPU-oracle sample (0 = auto)")
+    return p.parse_args()
+
+
+def csrc_digest() -> str:
+    d = os.path.join(ROOT, "mxfp8_quantization_moe_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------- workloads
+
+class Launch:
+    """One C-ABI call with preallocated device buffers."""
+
+    def __init__(self, name, kernel, fn, args, nbytes, numel):
+        self.name, self.kernel, self.fn, self.args = name, kernel, fn, args
+        self.nbytes, self.numel = nbytes, numel
+
+    def __call__(self, stream_handle):
+        code = self.fn(*self.args, stream_handle)
+        if code != 0:
+            raise RuntimeError(f"{self.name}: status {code}")
+
+
+def bf16_dev(torch, bits):
+    import numpy as np
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def build_moe_bwd(torch, mxq, workloads):
+    go_t = workloads.moe_grad_out_t()
+    x = workloads.moe_x()
+    offs = workloads.moe_offsets()
+    G = offs.size
+    d_go, d_x = bf16_dev(torch, go_t), bf16_dev(torch, x)
+    d_offs = torch.from_numpy(offs).cuda()
+    R1, C1 = go_t.shape
+    R2, C2 = x.shape
+    q1 = torch.empty(R1 * C1, dtype=torch.uint8, device="cuda")
+    s1 = torch.empty(R1 * G, dtype=torch.float32, device="cuda")
+    q2 = torch.empty(R2 * C2, dtype=torch.uint8, device="cuda")
+    s2 = torch.empty(G * C2, dtype=torch.float32, device="cuda")
+    keep = [d_go, d_x, d_offs, q1, s1, q2, s2]
+    l1 = Launch("jagged_rowwise grad_out^T (4096,16384)", "jagged_contig_kernel",
+                mxq.mxq_quantize_jagged_rowwise,
+                (d_go.data_ptr(), R1, C1, C1, 1, d_offs.data_ptr(), G, q1.data_ptr(), C1, 1,
+                 s1.data_ptr(), G, 1), 3 * R1 * C1 + 4 * R1 * G, R1 * C1)
+    l2 = Launch("jagged_colwise x (16384,4096)", "jagged_strided_kernel",
+                mxq.mxq_quantize_jagged_colwise,
+                (d_x.data_ptr(), R2, C2, C2, 1, d_offs.data_ptr(), G, q2.data_ptr(), 1, R2,
+                 s2.data_ptr(), C2, 1), 3 * R2 * C2 + 4 * G * C2, R2 * C2)
+    desc = {"workload": "moe_bwd_jagged",
+            "tensors": "grad_out^T bf16 (4096,16384) rowwise -> row-major e4m3; "
+                       "x bf16 (16384,4096) colwise -> column-major e4m3",
+            "groups": int(G), "group_sizes": [int(v) for v in
+                                              (offs - __import__("numpy").concatenate([[0], offs[:-1]]))],
+            "scales": "fp32 per (row, group) and per (group, column)"}
+
+    def cpu_sample(oracle, n):
+        # the same two ops on n rows of grad_out^T and n columns of x
+        t0 = time.perf_counter()
+        oracle.quantize_jagged_rowwise(go_t[:n], offs)
+        oracle.quantize_jagged_colwise(x[:, :n], offs)
+        dt = time.perf_counter() - t0
+        nbytes = 3 * n * C1 + 4 * n * G + 3 * R2 * n + 4 * G * n
+        return dt, nbytes, (f"jagged rowwise on {n} of 4096 rows of grad_out^T and jagged colwise "
+                            f"on {n} of 4096 columns of x (all 16384 tokens, same 8 groups)")
+
+    return [l1, l2], keep, desc, cpu_sample
+
+
+def build_mx3d(torch, mxq, workloads, E, sweep):
+    import numpy as np
+
+    N, K = 8192, 5120
+    w = torch.empty((E, N, K), dtype=torch.bfloat16, device="cuda")
+    for e in range(E):
+        bits = workloads.mx3d_sweep_expert(e) if sweep else workloads.mx3d_expert(e)
+        w[e].copy_(bf16_dev(torch, bits))
+    q = torch.empty(E * N * K, dtype=torch.uint8, device="cuda")
+    s = torch.empty(E * (N // 32) * K, dtype=torch.uint8, device="cuda")
+    l = Launch(f"mx_3d_colwise ({E},{N},{K})", "block_strided_kernel<32,1,e8m0>",
+               mxq.mxq_quantize_mx_3d_colwise,
+               (w.data_ptr(), E, N, K, N * K, K, 1, q.data_ptr(), N * K, 1, N, s.data_ptr(),
+                (N // 32) * K, K, 1, 0), 3 * E * N * K + E * (N // 32) * K, E * N * K)
+    desc = {"workload": f"mx3d_E{E}" + ("_sweep" if sweep else ""),
+            "tensors": f"W bf16 ({E},{N},{K}) -> e4m3 per-expert column-major (N*K,1,N)",
+            "scales": "e8m0 floor, (E, N/32, K)"}
+
+    def cpu_sample(oracle, n):
+        bits = workloads.mx3d_sweep_expert(0) if sweep else workloads.mx3d_expert(0)
+        t0 = time.perf_counter()
+        oracle.quantize_mx_3d_colwise(bits[None, :, :n])
+        dt = time.perf_counter() - t0
+        return dt, 3 * N * n + (N // 32) * n, f"expert 0, all N, {n} of {K} columns"
+
+    return [l], [w, q, s], desc, cpu_sample
+
+
+def build_blockwise(torch, mxq, workloads):
+    a = workloads.blockwise_act()
+    wt = workloads.blockwise_weight()
+    da, dw = bf16_dev(torch, a), bf16_dev(torch, wt)
+    M, Kd = a.shape
+    R, C = wt.shape
+    qa = torch.empty(M * Kd, dtype=torch.uint8, device="cuda")
+    sa = torch.empty(M * (Kd // 128), dtype=torch.float32, device="cuda")
+    qw = torch.empty(R * C, dtype=torch.uint8, device="cuda")
+    sw = torch.empty((R // 128) * (C // 128), dtype=torch.float32, device="cuda")
+    l1 = Launch("blockwise 1x128 act (8192,4096)", "block_contig_kernel<128>",
+                mxq.mxq_quantize_blockwise,
+                (da.data_ptr(), M, Kd, Kd, 1, 1, 128, qa.data_ptr(), Kd, 1, sa.data_ptr(),
+                 Kd // 128, 1), 3 * M * Kd + 4 * M * (Kd // 128), M * Kd)
+    l2 = Launch("blockwise 128x128 W (4096,4096)", "block_strided_kernel<128,128>",
+                mxq.mxq_quantize_blockwise,
+                (dw.data_ptr(), R, C, C, 1, 128, 128, qw.data_ptr(), 1, R, sw.data_ptr(),
+                 C // 128, 1), 3 * R * C + 4 * (R // 128) * (C // 128), R * C)
+    desc = {"workload": "blockwise",
+            "tensors": "act bf16 (8192,4096) 1x128 -> row-major e4m3; "
+                       "W bf16 (4096,4096) 128x128 -> column-major e4m3",
+            "scales": "fp32 per block"}
+
+    def cpu_sample(oracle, n):
+        t0 = time.perf_counter()
+        oracle.quantize_blockwise(a[:n], 1, 128)
+        oracle.quantize_blockwise(wt[: (n // 128) * 128 or 128], 128, 128)
+        dt = time.perf_counter() - t0
+        nw = (n // 128) * 128 or 128
+        return dt, 3 * n * Kd + 4 * n * (Kd // 128) + 3 * nw * C + 4 * (nw // 128) * (C // 128), \
+            f"{n} rows of act and {nw} rows of W"
+
+    return [l1, l2], [da, dw, qa, sa, qw, sw], desc, cpu_sample
+
+
+def build(name, torch, mxq, workloads):
+    if name == "moe_bwd":
+        return build_moe_bwd(torch, mxq, workloads)
+    if name == "mx3d":
+        return build_mx3d(torch, mxq, workloads, 8, sweep=False)
+    if name.startswith("mx3d_e"):
+        return build_mx3d(torch, mxq, workloads, int(name[len("mx3d_e"):]), sweep=True)
+    if name == "blockwise":
+        return build_blockwise(torch, mxq, workloads)
+    raise SystemExit(f"unknown workload {name}")
+
+
+# -------------------------------------------------------------------- run
+
+def traffic_for(kernel_name: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if data.get("csrc_digest") != csrc_digest():
+        return None
+    entry = data.get("kernels", {}).get(f"{workload}:{kernel_name}")
+    if not entry:
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        raise SystemExit(2)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if world != 1:
+        raise SystemExit("one process, one GPU: run without torch.distributed")
+
+    import numpy as np
+    import torch
+
+    import mxfp8_quantization_moe_amd as mxq
+    import workloads
+
+    mxq._capi.load()
+    torch.cuda.init()
+    print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
+    launches, keep, desc, cpu_sample = build(args.workload, torch, mxq, workloads)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    for _ in range(args.warmup):
+        for l in launches:
+            l(sh)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record(stream)
+        for i, l in enumerate(launches):
+            l(sh)
+            ev[k][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_kernel_ms = []
+    for i, l in enumerate(launches):
+        ms = [ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(K)]
+        per_kernel_ms.append(float(np.mean(ms)))
+    step_bytes = sum(l.nbytes for l in launches)
+    ms_per_step = wall * 1e3 / K
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    dom = int(np.argmax(per_kernel_ms))
+    dl = launches[dom]
+    achieved = dl.nbytes / (per_kernel_ms[dom] * 1e-3) / 1e9
+    traffic = traffic_for(dl.kernel, desc["workload"])
+    kernels = {l.name: {"avg_us": round(per_kernel_ms[i] * 1e3, 2),
+                        "algorithmic_bytes": l.nbytes,
+                        "GBps": round(l.nbytes / (per_kernel_ms[i] * 1e-3) / 1e9, 1),
+                        "frac_of_peak": round(l.nbytes / (per_kernel_ms[i] * 1e-3) / 1e9 / PEAK_GBPS, 4)}
+               for i, l in enumerate(launches)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        n = args.cpu_sample_rows or {"moe_bwd": 4096, "blockwise": 2048}.get(desc["workload"], 128)
+        print(f"[bench] timing the CPU oracle on a sample (n={n})", file=sys.stderr, flush=True)
+        dt, nbytes, what = cpu_sample(oracle, n)
+        cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": what, "seconds": round(dt, 2)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / PEAK_GBPS, 2),
+        "config": desc,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": dl.kernel, "algorithmic_bytes_per_launch": dl.nbytes,
+                     "avg_launch_us": round(per_kernel_ms[dom] * 1e3, 2)},
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "csrc_digest": csrc_digest(),
+    }
+    print(json.dumps(out), flush=True)
+    del keep
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+/*
+ * mxq — dynamic float8 (OCP E4M3FN) quantization of MoE grouped-GEMM operands
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every entry point takes DEVICE pointers, extents and strides counted
+ * in ELEMENTS (int64), and a HIP stream passed as `void*` (NULL = the null
+ * stream).  Work is enqueued on that stream and the call returns without
+ * synchronising; nothing is read back to the host, in particular not the
+ * group offsets.
+ *
+ * Numerics shared by all entry points (the pages name the formats, the
+ * readings below fix the arithmetic):
+ *   - input elements are bf16 bit patterns;
+ *   - fp32-scale paths store the quantize multiplier
+ *       s = RN32(448 / max(amax, RN32(1e-12)))
+ *     and write q = E4M3FN(clamp(RN32(x * s), -448, 448)), rounding to nearest
+ *     even, -0 kept (a negative value that rounds to zero gives 0x80);
+ *   - e8m0 paths ("floor" mode) store code = clamp(floor(log2 amax) - 8,
+ *     -127, 127) + 127 (0 for an all-zero block) and write
+ *       q = E4M3FN(clamp(x * 2^(127 - code), -448, 448)).
+ *   The result is unique: for finite inputs exactly one byte string and one
+ *   scale string is correct.  NaN / Inf inputs are outside the contract.
+ *
+ * Ownership: the caller allocates and owns every buffer; outputs must not
+ * alias inputs.  The library allocates nothing, keeps no state, and is
+ * reentrant.
+ *
+ * Errors (returned before any launch unless stated):
+ *   MXQ_ERR_INVALID_ARG  null pointer with a non-empty extent, negative
+ *                        extent, num_groups outside [1, MXQ_MAX_GROUPS],
+ *                        extent not divisible by the block, a pointer or a
+ *                        non-unit stride that breaks 16-byte alignment, or a
+ *                        unit-stride extent of a column-major store that is
+ *                        not a multiple of 8.
+ *   MXQ_ERR_UNSUPPORTED  a layout combination with no kernel (see each call),
+ *                        or MXQ_SCALE_RCEIL.
+ *   MXQ_ERR_LAUNCH       the launch failed (hipGetLastError after launch).
+ * A zero extent is not an error: the call writes whatever scales the
+ * definition still assigns (an empty group's scale) and returns MXQ_OK.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXQ_ABI_VERSION 1
+#define MXQ_MAX_GROUPS 4096
+
+typedef enum mxq_status {
+    MXQ_OK = 0,
+    MXQ_ERR_INVALID_ARG = 1,
+    MXQ_ERR_UNSUPPORTED = 2,
+    MXQ_ERR_LAUNCH = 3
+} mxq_status;
+
+typedef enum mxq_scale_mode { MXQ_SCALE_FLOOR = 0, MXQ_SCALE_RCEIL = 1 } mxq_scale_mode;
+
+/* Version of this ABI (MXQ_ABI_VERSION). */
+int mxq_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char *mxq_status_string(int status);
+
+/*
+ * Jagged per-group ROWWISE quantization.
+ * Source: "[scaled grouped mm] add triton kernels for float8 rowwise
+ * quantization with per-group/jagged scales", Summary (first kernel): one
+ * scale per row for each token group, output row-major, feeding the left
+ * operand of the grad_weight grouped GEMM; Motivation: offsets stay on the
+ * device, one launch covers every group.
+ *
+ * x       (rows, cols) bf16, strides (sx_r, sx_c).  Groups run along dim 1.
+ * offs    int32[num_groups] on the device: cumulative group ends; group g is
+ *         columns [offs[g-1], offs[g]) with offs[-1] = 0.  Precondition (not
+ *         checkable without a sync): non-decreasing, 0 <= offs[g] <= cols.
+ *         Columns at or past offs[num_groups-1] belong to no group and their
+ *         q bytes are not written.
+ * q       (rows, cols) e4m3 bytes, strides (sq_r, sq_c).
+ * scales  (rows, num_groups) fp32, strides (ss_r, ss_g); every entry is
+ *         written, an empty group gets 448 / RN32(1e-12).
+ * Layouts with a kernel: sx_c == 1 && sq_c == 1 (row-major in and out), and
+ * sx_r == 1 && sq_c == 1 (a transposed view of a row-major tensor, e.g.
+ * grad_out^T, into a row-major q).
+ */
+mxq_status mxq_quantize_jagged_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t sx_r,
+                                       int64_t sx_c, const int32_t *offs, int32_t num_groups,
+                                       uint8_t *q, int64_t sq_r, int64_t sq_c, float *scales,
+                                       int64_t ss_r, int64_t ss_g, void *stream);
+
+/*
+ * Jagged per-group COLWISE quantization.
+ * Source: same page, Summary (second kernel): scales computed over the
+ * logical columns of each token group, output column-major, feeding the
+ * right operand of the grad_weight grouped GEMM.
+ *
+ * x       (rows, cols) bf16, strides (sx_r, sx_c).  Groups run along dim 0:
+ *         group g is rows [offs[g-1], offs[g]); same precondition as above
+ *         with `rows` as the extent.
+ * q       (rows, cols) e4m3, strides (sq_r, sq_c).
+ * scales  (num_groups, cols) fp32, strides (ss_g, ss_c).
+ * Layouts with a kernel: sx_c == 1 && sq_r == 1 (row-major in, column-major
+ * out), and sx_r == 1 && sq_r == 1 (column-major in and out).
+ */
+mxq_status mxq_quantize_jagged_colwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t sx_r,
+                                       int64_t sx_c, const int32_t *offs, int32_t num_groups,
+                                       uint8_t *q, int64_t sq_r, int64_t sq_c, float *scales,
+                                       int64_t ss_g, int64_t ss_c, void *stream);
+
+/*
+ * MXFP8 quantization of 3D expert weights along N ("colwise", 32 x 1 blocks).
+ * Source: "[mxfp8 moe training] add CUDA kernel to quantize 3d tensor
+ * colwise", Summary: weights (E, N, K) scaled along N and written directly in
+ * per-expert column-major layout, no separate transpose pass; the author's
+ * comment names the floor / rceil scale modes.
+ *
+ * w       (E, N, K) bf16, strides (sw_e, sw_n, sw_k); N % 32 == 0.
+ * q       (E, N, K) e4m3, strides (sq_e, sq_n, sq_k); default per-expert
+ *         column-major is (N*K, 1, N).
+ * scales  (E, N/32, K) e8m0 bytes, strides (ss_e, ss_nb, ss_k).
+ * Layout with a kernel: sw_k == 1 && sq_n == 1 (K % 8 == 0).
+ * scale_mode: MXQ_SCALE_FLOOR.
+ */
+mxq_status mxq_quantize_mx_3d_colwise(const uint16_t *w, int64_t E, int64_t N, int64_t K,
+                                      int64_t sw_e, int64_t sw_n, int64_t sw_k, uint8_t *q,
+                                      int64_t sq_e, int64_t sq_n, int64_t sq_k, uint8_t *scales,
+                                      int64_t ss_e, int64_t ss_nb, int64_t ss_k,
+                                      int32_t scale_mode, void *stream);
+
+/*
+ * MXFP8 quantization along the last dim (1 x 32 blocks), the layout `to_mx`
+ * produces.  Source: same page, Summary (the `to_mx` route along the
+ * contiguous dim).
+ *
+ * x       (rows, cols) bf16, strides (sx_r, sx_c); cols % 32 == 0.
+ * q       (rows, cols) e4m3, strides (sq_r, sq_c).
+ * scales  (rows, cols/32) e8m0, strides (ss_r, ss_b).
+ * Layout with a kernel: sx_c == 1 && sq_c == 1.
+ */
+mxq_status mxq_quantize_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t sx_r,
+                                   int64_t sx_c, uint8_t *q, int64_t sq_r, int64_t sq_c,
+                                   uint8_t *scales, int64_t ss_r, int64_t ss_b,
+                                   int32_t scale_mode, void *stream);
+
+/*
+ * Blockwise ("groupwise") fp8 quantization with one fp32 multiplier per
+ * block_r x block_c block.  Source: "[fp8 blockwise] load 2d chunks for
+ * groupwise quant to enable coalesced gmem accesses", body: 1 x blocksize
+ * blocks for activations, blocksize x blocksize for weights, loaded as 2D
+ * chunks so both directions coalesce.
+ *
+ * x       (rows, cols) bf16, strides (sx_r, sx_c); rows % block_r == 0 and
+ *         cols % block_c == 0.
+ * q       (rows, cols) e4m3, strides (sq_r, sq_c).
+ * scales  (rows/block_r, cols/block_c) fp32, strides (ss_rb, ss_cb).
+ * Blocks and layouts with a kernel:
+ *   (1, 128)   sx_c == 1 && sq_c == 1   row-major in and out;
+ *   (128, 128) sx_c == 1 && sq_r == 1   row-major in, column-major out;
+ *   (128, 1)   sx_c == 1 && sq_r == 1   row-major in, column-major out.
+ */
+mxq_status mxq_quantize_blockwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t sx_r,
+                                  int64_t sx_c, int32_t block_r, int32_t block_c, uint8_t *q,
+                                  int64_t sq_r, int64_t sq_c, float *scales, int64_t ss_rb,
+                                  int64_t ss_cb, void *stream);
+
+/*
+ * Diagnostic: apply the library's own device cast (saturate to +-448, then
+ * the hardware round-to-nearest-even E4M3FN conversion) to n fp32 values.
+ * Used to check the device conversion against the CPU definition over whole
+ * fp32 ranges.  y: n floats, out: n bytes, both device pointers.
+ */
+mxq_status mxq_debug_cast_e4m3(const float *y, int64_t n, uint8_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

@@ -1,0 +1,304 @@
+// C-ABI entry points of libmxq: argument validation, layout dispatch and
+// kernel launches.  No allocation, no synchronisation, no read-back.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mxq.h"
+#include "block_kernels.hpp"
+#include "jagged_kernels.hpp"
+
+namespace {
+
+using namespace mxq;
+
+constexpr int kJaggedStridedCG = 4;   // 32-column strips, 1024-row passes
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+mxq_status launch_status()
+{
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? MXQ_OK : MXQ_ERR_LAUNCH;
+}
+
+// jagged, reduction along the unit-stride dim of a (nrows, ext) view
+mxq_status run_jagged_contig(const uint16_t *x, int64_t nrows, int64_t ext, int64_t ldx,
+                             const int32_t *offs, int32_t G, uint8_t *q, int64_t ldq,
+                             float *scales, int64_t ss_row, int64_t ss_g, hipStream_t st)
+{
+    if (nrows == 0)
+        return MXQ_OK;
+    if (nrows > INT32_MAX)
+        return MXQ_ERR_INVALID_ARG;
+    const size_t lds = (size_t)3 * G * sizeof(uint32_t);
+    const dim3 grid((unsigned)nrows), block(kThreads);
+    const int cols = (int)ext;
+    if (ext <= 2048)
+        jagged_contig_kernel<1><<<grid, block, lds, st>>>(x, ldx, cols, offs, G, q, ldq, scales, ss_row, ss_g);
+    else if (ext <= 4096)
+        jagged_contig_kernel<2><<<grid, block, lds, st>>>(x, ldx, cols, offs, G, q, ldq, scales, ss_row, ss_g);
+    else if (ext <= 8192)
+        jagged_contig_kernel<4><<<grid, block, lds, st>>>(x, ldx, cols, offs, G, q, ldq, scales, ss_row, ss_g);
+    else
+        jagged_contig_kernel<8><<<grid, block, lds, st>>>(x, ldx, cols, offs, G, q, ldq, scales, ss_row, ss_g);
+    return launch_status();
+}
+
+// jagged, reduction across rows of a (ext, ncols) row-major view, column-major q
+mxq_status run_jagged_strided(const uint16_t *x, int64_t ext, int64_t ncols, int64_t ldx,
+                              const int32_t *offs, int32_t G, uint8_t *q, int64_t ldq,
+                              float *scales, int64_t ss_g, int64_t ss_col, hipStream_t st)
+{
+    if (ncols == 0)
+        return MXQ_OK;
+    if (ncols % 8 != 0 || ncols > INT32_MAX)
+        return MXQ_ERR_INVALID_ARG;
+    constexpr int SW = 8 * kJaggedStridedCG;
+    const int64_t nstrips = (ncols + SW - 1) / SW;
+    const int64_t nblocks = nstrips * G;
+    if (nblocks > INT32_MAX)
+        return MXQ_ERR_INVALID_ARG;
+    jagged_strided_kernel<kJaggedStridedCG><<<dim3((unsigned)nblocks), dim3(kThreads), 0, st>>>(
+        x, ldx, (int)ext, (int)ncols, offs, G, q, ldq, scales, ss_g, ss_col, (int)nstrips);
+    return launch_status();
+}
+
+mxq_status check_jagged_common(const uint16_t *x, int64_t rows, int64_t cols, const int32_t *offs,
+                               int32_t G, const uint8_t *q, const float *scales)
+{
+    if (rows < 0 || cols < 0 || G < 1 || G > MXQ_MAX_GROUPS)
+        return MXQ_ERR_INVALID_ARG;
+    if (rows > INT32_MAX || cols > INT32_MAX)
+        return MXQ_ERR_INVALID_ARG;
+    if (!offs || !scales)
+        return MXQ_ERR_INVALID_ARG;
+    if ((rows > 0 && cols > 0) && (!x || !q))
+        return MXQ_ERR_INVALID_ARG;
+    if (x && !aligned16(x))
+        return MXQ_ERR_INVALID_ARG;
+    if (q && !aligned16(q))
+        return MXQ_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
+        return MXQ_ERR_INVALID_ARG;
+    return MXQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mxq_abi_version(void) { return MXQ_ABI_VERSION; }
+
+const char *mxq_status_string(int status)
+{
+    switch (status) {
+    case MXQ_OK: return "MXQ_OK";
+    case MXQ_ERR_INVALID_ARG: return "MXQ_ERR_INVALID_ARG";
+    case MXQ_ERR_UNSUPPORTED: return "MXQ_ERR_UNSUPPORTED";
+    case MXQ_ERR_LAUNCH: return "MXQ_ERR_LAUNCH";
+    default: return "MXQ_ERR_UNKNOWN";
+    }
+}
+
+mxq_status mxq_quantize_jagged_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t sx_r,
+                                       int64_t sx_c, const int32_t *offs, int32_t num_groups,
+                                       uint8_t *q, int64_t sq_r, int64_t sq_c, float *scales,
+                                       int64_t ss_r, int64_t ss_g, void *stream)
+{
+    mxq_status s = check_jagged_common(x, rows, cols, offs, num_groups, q, scales);
+    if (s != MXQ_OK)
+        return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (rows == 0)
+        return MXQ_OK;
+    if (sx_c == 1 && sq_c == 1) {
+        if (rows > 1 && cols >= 8 && (sx_r % 8 != 0 || sq_r % 16 != 0))
+            return MXQ_ERR_INVALID_ARG;
+        return run_jagged_contig(x, rows, cols, sx_r, offs, num_groups, q, sq_r, scales, ss_r, ss_g, st);
+    }
+    if (sx_r == 1 && sq_c == 1) {
+        // x is the transpose of a row-major (cols, rows) tensor: reduce across
+        // its rows, store column-major of that tensor == row-major q
+        if (sx_c % 8 != 0 || sq_r % 16 != 0)
+            return MXQ_ERR_INVALID_ARG;
+        return run_jagged_strided(x, cols, rows, sx_c, offs, num_groups, q, sq_r, scales, ss_g, ss_r, st);
+    }
+    return MXQ_ERR_UNSUPPORTED;
+}
+
+mxq_status mxq_quantize_jagged_colwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t sx_r,
+                                       int64_t sx_c, const int32_t *offs, int32_t num_groups,
+                                       uint8_t *q, int64_t sq_r, int64_t sq_c, float *scales,
+                                       int64_t ss_g, int64_t ss_c, void *stream)
+{
+    mxq_status s = check_jagged_common(x, rows, cols, offs, num_groups, q, scales);
+    if (s != MXQ_OK)
+        return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (cols == 0)
+        return MXQ_OK;
+    if (sx_c == 1 && sq_r == 1) {
+        if (sx_r % 8 != 0 || sq_c % 16 != 0)
+            return MXQ_ERR_INVALID_ARG;
+        return run_jagged_strided(x, rows, cols, sx_r, offs, num_groups, q, sq_c, scales, ss_g, ss_c, st);
+    }
+    if (sx_r == 1 && sq_r == 1) {
+        // column-major in and out: the rowwise pattern on the transpose
+        if (cols > 1 && rows >= 8 && (sx_c % 8 != 0 || sq_c % 16 != 0))
+            return MXQ_ERR_INVALID_ARG;
+        return run_jagged_contig(x, cols, rows, sx_c, offs, num_groups, q, sq_c, scales, ss_c, ss_g, st);
+    }
+    return MXQ_ERR_UNSUPPORTED;
+}
+
+mxq_status mxq_quantize_mx_3d_colwise(const uint16_t *w, int64_t E, int64_t N, int64_t K,
+                                      int64_t sw_e, int64_t sw_n, int64_t sw_k, uint8_t *q,
+                                      int64_t sq_e, int64_t sq_n, int64_t sq_k, uint8_t *scales,
+                                      int64_t ss_e, int64_t ss_nb, int64_t ss_k,
+                                      int32_t scale_mode, void *stream)
+{
+    if (E < 0 || N < 0 || K < 0 || N % 32 != 0)
+        return MXQ_ERR_INVALID_ARG;
+    if (scale_mode == MXQ_SCALE_RCEIL)
+        return MXQ_ERR_UNSUPPORTED;
+    if (scale_mode != MXQ_SCALE_FLOOR)
+        return MXQ_ERR_INVALID_ARG;
+    if (E == 0 || N == 0 || K == 0)
+        return MXQ_OK;
+    if (!w || !q || !scales)
+        return MXQ_ERR_INVALID_ARG;
+    if (!(sw_k == 1 && sq_n == 1))
+        return MXQ_ERR_UNSUPPORTED;
+    if (!aligned16(w) || !aligned16(q) || K % 8 != 0 || sw_n % 8 != 0 || sw_e % 8 != 0 ||
+        sq_k % 16 != 0 || sq_e % 16 != 0)
+        return MXQ_ERR_INVALID_ARG;
+    if (N > INT32_MAX || K > INT32_MAX)
+        return MXQ_ERR_INVALID_ARG;
+    const int64_t tiles_r = (N + 127) / 128, tiles_c = (K + 255) / 256;
+    const int64_t nblocks = E * tiles_r * tiles_c;
+    if (nblocks > INT32_MAX)
+        return MXQ_ERR_INVALID_ARG;
+    block_strided_kernel<32, 1, true><<<dim3((unsigned)nblocks), dim3(kBlockThreads), 0,
+                                         reinterpret_cast<hipStream_t>(stream)>>>(
+        w, sw_e, sw_n, (int)N, (int)K, q, sq_e, sq_k, scales, ss_e, ss_nb, ss_k, (int)tiles_r,
+        (int)tiles_c);
+    return launch_status();
+}
+
+mxq_status mxq_quantize_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t sx_r,
+                                   int64_t sx_c, uint8_t *q, int64_t sq_r, int64_t sq_c,
+                                   uint8_t *scales, int64_t ss_r, int64_t ss_b,
+                                   int32_t scale_mode, void *stream)
+{
+    if (rows < 0 || cols < 0 || cols % 32 != 0)
+        return MXQ_ERR_INVALID_ARG;
+    if (scale_mode == MXQ_SCALE_RCEIL)
+        return MXQ_ERR_UNSUPPORTED;
+    if (scale_mode != MXQ_SCALE_FLOOR)
+        return MXQ_ERR_INVALID_ARG;
+    if (rows == 0 || cols == 0)
+        return MXQ_OK;
+    if (!x || !q || !scales)
+        return MXQ_ERR_INVALID_ARG;
+    if (!(sx_c == 1 && sq_c == 1))
+        return MXQ_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(q) || sx_r % 8 != 0 || sq_r % 16 != 0)
+        return MXQ_ERR_INVALID_ARG;
+    constexpr int U = 4, LPB = 4;
+    const int64_t nbpr = cols / 32, nblocks = rows * nbpr;
+    const int64_t per_wg = (int64_t)U * (kBlockThreads / LPB);
+    const int64_t grid = (nblocks + per_wg - 1) / per_wg;
+    if (grid > INT32_MAX)
+        return MXQ_ERR_INVALID_ARG;
+    block_contig_kernel<32, LPB, true, U><<<dim3((unsigned)grid), dim3(kBlockThreads), 0,
+                                            reinterpret_cast<hipStream_t>(stream)>>>(
+        x, sx_r, nbpr, nblocks, q, sq_r, scales, ss_r, ss_b);
+    return launch_status();
+}
+
+mxq_status mxq_quantize_blockwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t sx_r,
+                                  int64_t sx_c, int32_t block_r, int32_t block_c, uint8_t *q,
+                                  int64_t sq_r, int64_t sq_c, float *scales, int64_t ss_rb,
+                                  int64_t ss_cb, void *stream)
+{
+    if (rows < 0 || cols < 0 || block_r <= 0 || block_c <= 0)
+        return MXQ_ERR_INVALID_ARG;
+    if (rows % block_r != 0 || cols % block_c != 0)
+        return MXQ_ERR_INVALID_ARG;
+    const bool b1x128 = block_r == 1 && block_c == 128;
+    const bool b128x128 = block_r == 128 && block_c == 128;
+    const bool b128x1 = block_r == 128 && block_c == 1;
+    if (!b1x128 && !b128x128 && !b128x1)
+        return MXQ_ERR_UNSUPPORTED;
+    if (rows == 0 || cols == 0)
+        return MXQ_OK;
+    if (!x || !q || !scales)
+        return MXQ_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
+        return MXQ_ERR_INVALID_ARG;
+    if (rows > INT32_MAX || cols > INT32_MAX)
+        return MXQ_ERR_INVALID_ARG;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (b1x128) {
+        if (!(sx_c == 1 && sq_c == 1))
+            return MXQ_ERR_UNSUPPORTED;
+        if (!aligned16(x) || !aligned16(q) || sx_r % 8 != 0 || sq_r % 16 != 0)
+            return MXQ_ERR_INVALID_ARG;
+        constexpr int U = 4, LPB = 8;
+        const int64_t nbpr = cols / 128, nblocks = rows * nbpr;
+        const int64_t per_wg = (int64_t)U * (kBlockThreads / LPB);
+        const int64_t grid = (nblocks + per_wg - 1) / per_wg;
+        if (grid > INT32_MAX)
+            return MXQ_ERR_INVALID_ARG;
+        block_contig_kernel<128, LPB, false, U><<<dim3((unsigned)grid), dim3(kBlockThreads), 0, st>>>(
+            x, sx_r, nbpr, nblocks, q, sq_r, scales, ss_rb, ss_cb);
+        return launch_status();
+    }
+    // (128, 128) and (128, 1): row-major in, column-major out
+    if (!(sx_c == 1 && sq_r == 1))
+        return MXQ_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(q) || cols % 8 != 0 || sx_r % 8 != 0 || sq_c % 16 != 0)
+        return MXQ_ERR_INVALID_ARG;
+    const int64_t tiles_r = rows / 128, tiles_c = (cols + 255) / 256;
+    const int64_t nblocks = tiles_r * tiles_c;
+    if (nblocks > INT32_MAX)
+        return MXQ_ERR_INVALID_ARG;
+    if (b128x128)
+        block_strided_kernel<128, 128, false><<<dim3((unsigned)nblocks), dim3(kBlockThreads), 0, st>>>(
+            x, 0, sx_r, (int)rows, (int)cols, q, 0, sq_c, scales, 0, ss_rb, ss_cb, (int)tiles_r,
+            (int)tiles_c);
+    else
+        block_strided_kernel<128, 1, false><<<dim3((unsigned)nblocks), dim3(kBlockThreads), 0, st>>>(
+            x, 0, sx_r, (int)rows, (int)cols, q, 0, sq_c, scales, 0, ss_rb, ss_cb, (int)tiles_r,
+            (int)tiles_c);
+    return launch_status();
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ diagnostics
+
+namespace {
+__global__ void debug_cast_kernel(const float *__restrict__ y, int64_t n, uint8_t *__restrict__ out)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t k = i; k < n; k += stride)
+        out[k] = (uint8_t)mxq::cvt1(y[k]);
+}
+}  // namespace
+
+extern "C" mxq_status mxq_debug_cast_e4m3(const float *y, int64_t n, uint8_t *out, void *stream)
+{
+    if (n < 0)
+        return MXQ_ERR_INVALID_ARG;
+    if (n == 0)
+        return MXQ_OK;
+    if (!y || !out)
+        return MXQ_ERR_INVALID_ARG;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 65536)
+        blocks = 65536;
+    debug_cast_kernel<<<dim3((unsigned)blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream)>>>(y, n, out);
+    return launch_status();
+}

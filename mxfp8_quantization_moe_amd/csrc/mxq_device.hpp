@@ -1,0 +1,130 @@
+// Device-side building blocks shared by the gfx950 quantization kernels.
+//
+// Every element goes through the same four steps:
+//   1. bf16 -> fp32 by a shift (exact; a subnormal stays subnormal),
+//   2. amax on the bf16 bit patterns: for finite values |a| <= |b| iff
+//      (a & 0x7FFF) <= (b & 0x7FFF) as unsigned, so two elements per
+//      v_pk_max_u16,
+//   3. one fp32 multiply by the scale (kernels are built with IEEE fp32
+//      denormals, so a subnormal input times 2^127 is exact),
+//   4. v_med3_f32 clamp to +-448, then v_cvt_pk_fp8_f32 (OCP E4M3FN, round to
+//      nearest even) packing two results per instruction.
+// The scale is either the fp32 multiplier 448 / max(amax, 1e-12) computed by
+// the compiler's correctly rounded division, or an e8m0 code whose multiplier
+// 2^(127 - code) is built directly from its exponent bits.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kE4M3Max = 448.0f;
+constexpr float kAmaxEps = 1e-12f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// packed running max of |bf16| over the two halves of a dword
+__device__ __forceinline__ uint32_t absmax2(uint32_t m, uint32_t v)
+{
+    u16x2 a = __builtin_bit_cast(u16x2, m);
+    u16x2 b = __builtin_bit_cast(u16x2, v & 0x7fff7fffu);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+}
+
+// max of the two 16-bit halves
+__device__ __forceinline__ uint32_t fold2(uint32_t m)
+{
+    uint32_t lo = m & 0xffffu, hi = m >> 16;
+    return lo > hi ? lo : hi;
+}
+
+__device__ __forceinline__ uint32_t absmax_u4(const uint4 &v)
+{
+    uint32_t m = absmax2(absmax2(v.x & 0x7fff7fffu, v.y), absmax2(v.z & 0x7fff7fffu, v.w));
+    return m;
+}
+
+// fp32 quantize multiplier from the |bf16| bit pattern of amax
+__device__ __forceinline__ float fp32_scale(uint32_t amax16)
+{
+    float a = __uint_as_float(amax16 << 16);
+    return kE4M3Max / fmaxf(a, kAmaxEps);
+}
+
+// e8m0 "floor" code from the |bf16| bit pattern of amax:
+// floor(log2 amax) = exponent field - 127 for normal amax, and anything
+// below 2^-118 clamps to code 0, so code = max(field - 8, 0).
+__device__ __forceinline__ uint32_t e8m0_floor_code(uint32_t amax16)
+{
+    int f = (int)((amax16 >> 7) & 0xffu);
+    return f > 8 ? (uint32_t)(f - 8) : 0u;
+}
+
+// element multiplier 2^(127 - code) for code in [0, 246] (always normal)
+__device__ __forceinline__ float e8m0_multiplier(uint32_t code)
+{
+    return __uint_as_float((254u - code) << 23);
+}
+
+__device__ __forceinline__ float sat(float y) { return __builtin_amdgcn_fmed3f(y, -kE4M3Max, kE4M3Max); }
+
+// four fp32 values -> four e4m3 bytes, a in the lowest byte
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d)
+{
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), r, true);
+    return (uint32_t)r;
+}
+
+// one element -> one byte
+__device__ __forceinline__ uint32_t cvt1(float a)
+{
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat(a), 0.0f, 0, false) & 0xffu;
+}
+
+// eight bf16 (one 16-byte load) times one multiplier -> eight bytes
+__device__ __forceinline__ uint2 quant8(const uint4 &v, float s)
+{
+    uint2 r;
+    r.x = cvt4(bf16_lo(v.x) * s, bf16_hi(v.x) * s, bf16_lo(v.y) * s, bf16_hi(v.y) * s);
+    r.y = cvt4(bf16_lo(v.z) * s, bf16_hi(v.z) * s, bf16_lo(v.w) * s, bf16_hi(v.w) * s);
+    return r;
+}
+
+// bf16 element j (0..7) of a 16-byte load, as fp32
+__device__ __forceinline__ float elem8(const uint4 &v, int j)
+{
+    uint32_t d = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
+    return (j & 1) ? bf16_hi(d) : bf16_lo(d);
+}
+
+__device__ __forceinline__ uint32_t elem8_bits(const uint4 &v, int j)
+{
+    uint32_t d = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
+    return (j & 1) ? (d >> 16) : (d & 0xffffu);
+}
+
+// packed |bf16| max of the column pair (2d, 2d+1) of a 16-byte load
+__device__ __forceinline__ uint32_t dword_of(const uint4 &v, int d)
+{
+    return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
+}
+
+// wave-level max over lanes that differ in the bits of `mask` (power of two
+// steps), via ds_swizzle-free cross-lane shuffles
+__device__ __forceinline__ uint32_t xor_max(uint32_t v, int lanemask)
+{
+    uint32_t o = (uint32_t)__shfl_xor((int)v, lanemask, 64);
+    return v > o ? v : o;
+}
+
+// global memory access helpers: 16-byte loads, 16/8-byte stores
+__device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void st16(uint8_t *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+__device__ __forceinline__ void st8(uint8_t *p, uint2 v) { *reinterpret_cast<uint2 *>(p) = v; }
+
+}  // namespace mxq

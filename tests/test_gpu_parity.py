@@ -1,0 +1,205 @@
+"""GPU parity of every C-ABI entry point against the CPU oracle, byte for
+byte, on small and adversarial inputs: ragged group boundaries, empty groups,
+offsets that stop short of the extent (bytes past the last group must keep
+the canary), single groups, many groups, tails that are not tile multiples,
+zero / subnormal / huge MX blocks, transposed views, a side stream, and
+repeat-run determinism."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import (CANARY, assert_same_bytes, bf16_dev, blockwise, i32_dev, jagged_colwise,
+                         jagged_rowwise, mx_3d_colwise, mx_rowwise)
+
+pytestmark = pytest.mark.gpu
+
+
+def adversarial(shape, seed):
+    g = np.random.default_rng(seed)
+    bits = workloads.normal_bf16(shape, seed)
+    flat = bits.reshape(-1)
+    pick = g.choice(flat.size, size=max(1, flat.size // 16), replace=False)
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x7F7F, 0xFF7F,
+                         0x3F80, 0xBF80, 0x43E0, 0x3C00], dtype=np.uint16)
+    flat[pick] = specials[g.integers(specials.size, size=pick.size)]
+    return bits
+
+
+def random_offsets(extent, G, seed, multiple=1, empties=1, short_tail=0):
+    g = np.random.default_rng(seed)
+    cuts = np.sort(g.integers(0, (extent - short_tail) // multiple + 1, size=G - 1)) * multiple
+    offs = np.concatenate([cuts, [extent - short_tail]]).astype(np.int64)
+    for _ in range(empties):                   # force some empty groups
+        j = int(g.integers(1, G)) if G > 1 else 0
+        if j > 0:
+            offs[j] = offs[j - 1]
+    offs = np.maximum.accumulate(offs)
+    return offs.astype(np.int32)
+
+
+def check_rowwise(bits, offs, canary_tail=True):
+    q, s = jagged_rowwise(bf16_dev(bits), i32_dev(offs))
+    oq, os_ = oracle.quantize_jagged_rowwise(bits, offs, canary=CANARY)
+    assert_same_bytes(q, oq, "jagged rowwise q")
+    assert_same_bytes(s, os_, "jagged rowwise scales")
+
+
+def check_colwise(bits, offs):
+    q, s = jagged_colwise(bf16_dev(bits), i32_dev(offs))
+    oq, os_ = oracle.quantize_jagged_colwise(bits, offs, canary=CANARY)
+    assert_same_bytes(q, oq, "jagged colwise q")
+    assert_same_bytes(s, os_, "jagged colwise scales")
+
+
+# ------------------------------------------------------------------ jagged
+
+def test_small_workloads():
+    a, offs = workloads.small_rowwise()
+    check_rowwise(a, offs)
+    b, offs_b = workloads.small_colwise()
+    check_colwise(b, offs_b)
+
+
+@pytest.mark.parametrize("rows,cols,G,mult,tail,seed", [
+    (5, 1000, 4, 1, 0, 1),
+    (3, 4099, 7, 1, 5, 2),
+    (2, 20000, 8, 16, 0, 3),       # longer than the register window: chunked re-read
+    (9, 40000, 13, 1, 33, 4),
+    (4, 77, 1, 1, 0, 5),
+    (6, 300, 64, 1, 0, 6),
+    (2, 5000, 300, 1, 7, 7),       # many groups: binary-search group lookup
+    (1, 1, 2, 1, 0, 8),
+    (7, 8, 3, 1, 1, 9),
+])
+def test_jagged_rowwise_ragged(rows, cols, G, mult, tail, seed):
+    bits = adversarial((rows, cols), 100 + seed)
+    offs = random_offsets(cols, G, seed, multiple=mult, short_tail=tail)
+    check_rowwise(bits, offs)
+
+
+def test_jagged_rowwise_empty_extent_writes_empty_group_scales():
+    bits = np.zeros((4, 0), dtype=np.uint16)
+    x = torch.zeros((4, 8), dtype=torch.bfloat16, device="cuda")[:, :0]
+    q, s = jagged_rowwise(x, i32_dev([0, 0, 0]))
+    assert np.all(s.view(np.uint32) == 0x57CBBA10)
+    _, os_ = oracle.quantize_jagged_rowwise(bits, np.array([0, 0, 0], dtype=np.int32))
+    assert_same_bytes(s, os_, "scales")
+
+
+@pytest.mark.parametrize("rows,cols,G,mult,tail,seed", [
+    (1000, 64, 4, 1, 0, 11),
+    (4099, 40, 7, 1, 3, 12),
+    (20000, 8, 8, 16, 0, 13),
+    (3000, 96, 1, 1, 0, 14),
+    (5000, 16, 64, 1, 9, 15),      # G <= 64: largest-group-first order
+    (7000, 24, 100, 1, 0, 16),     # G > 64: identity order
+    (17, 264, 5, 1, 0, 17),
+    (33, 8, 3, 1, 1, 18),
+])
+def test_jagged_colwise_ragged(rows, cols, G, mult, tail, seed):
+    bits = adversarial((rows, cols), 200 + seed)
+    offs = random_offsets(rows, G, seed, multiple=mult, short_tail=tail)
+    check_colwise(bits, offs)
+
+
+def test_jagged_colwise_empty_extent():
+    x = torch.zeros((16, 16), dtype=torch.bfloat16, device="cuda")[:0]
+    q, s = jagged_colwise(x, i32_dev([0, 0]))
+    assert np.all(s.view(np.uint32) == 0x57CBBA10)
+
+
+def test_rowwise_on_transposed_view_matches_row_major():
+    """grad_out^T given as a transposed view of a row-major tensor."""
+    rows, cols = 96, 3000
+    bits = adversarial((rows, cols), 31)
+    offs = random_offsets(cols, 6, 31, short_tail=5)
+    base = bf16_dev(np.ascontiguousarray(bits.T))         # (cols, rows) row-major
+    view = base.t()                                        # (rows, cols), strides (1, rows)
+    assert view.stride() == (1, rows)
+    q, s = jagged_rowwise(view, i32_dev(offs))
+    oq, os_ = oracle.quantize_jagged_rowwise(bits, offs, canary=CANARY)
+    assert_same_bytes(q, oq, "rowwise (transposed view) q")
+    assert_same_bytes(s, os_, "rowwise (transposed view) scales")
+
+
+def test_colwise_on_column_major_input():
+    rows, cols = 2500, 48
+    bits = adversarial((rows, cols), 41)
+    offs = random_offsets(rows, 5, 41, short_tail=4)
+    base = bf16_dev(np.ascontiguousarray(bits.T))         # (cols, rows) row-major
+    view = base.t()                                        # (rows, cols) column-major
+    q, s = jagged_colwise(view, i32_dev(offs))
+    oq, os_ = oracle.quantize_jagged_colwise(bits, offs, canary=CANARY)
+    assert_same_bytes(q, oq, "colwise (column-major in) q")
+    assert_same_bytes(s, os_, "colwise (column-major in) scales")
+
+
+def test_side_stream_and_determinism():
+    a, offs = workloads.small_rowwise()
+    x, o = bf16_dev(a), i32_dev(offs)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        q1, s1 = jagged_rowwise(x, o, stream=side)
+    q2, s2 = jagged_rowwise(x, o)
+    assert np.array_equal(q1, q2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+
+
+# ---------------------------------------------------------------------- MX
+
+@pytest.mark.parametrize("E,N,K,seed", [(1, 128, 256, 1), (3, 96, 200, 2), (2, 512, 1032, 3)])
+def test_mx_3d_colwise(E, N, K, seed):
+    w = np.stack([adversarial((N, K), 300 + seed * 10 + e) for e in range(E)])
+    w[0, 0:32, 3] = 0                                           # zero block
+    w[-1, 32:64, 5] = 0x8000                                    # negative zeros
+    w[-1, N - 32:N, 7] = (np.arange(32, dtype=np.uint16) * 3) & 0x7F   # subnormal block
+    w[0, 0:32, 9] = workloads.to_bf16_bits(
+        np.random.default_rng(seed).standard_normal(32).astype(np.float32) * np.float32(2.0 ** 100))
+    q, s = mx_3d_colwise(bf16_dev(w))
+    oq, os_ = oracle.quantize_mx_3d_colwise(w)
+    assert_same_bytes(q, oq, "mx 3d q")
+    assert_same_bytes(s, os_, "mx 3d scales")
+
+
+def test_mx_3d_sweep_pattern_small():
+    w = np.stack([workloads.mx3d_sweep_expert(e, N=256, K=512) for e in range(2)])
+    q, s = mx_3d_colwise(bf16_dev(w))
+    oq, os_ = oracle.quantize_mx_3d_colwise(w)
+    assert_same_bytes(q, oq, "mx 3d sweep q")
+    assert_same_bytes(s, os_, "mx 3d sweep scales")
+    assert (s == 0).sum() > 0
+
+
+@pytest.mark.parametrize("rows,cols,seed", [(64, 256, 1), (5, 96, 2), (300, 4096, 3)])
+def test_mx_rowwise(rows, cols, seed):
+    x = adversarial((rows, cols), 400 + seed)
+    x[0, :32] = 0
+    x[-1, 32:64] = np.arange(32, dtype=np.uint16) + 1
+    q, s = mx_rowwise(bf16_dev(x))
+    oq, os_ = oracle.quantize_mx_rowwise(x)
+    assert_same_bytes(q, oq, "mx rowwise q")
+    assert_same_bytes(s, os_, "mx rowwise scales")
+
+
+# --------------------------------------------------------------- blockwise
+
+@pytest.mark.parametrize("br,bc,rows,cols", [
+    (1, 128, 3, 128), (1, 128, 256, 512), (1, 128, 77, 1152),
+    (128, 128, 128, 128), (128, 128, 256, 384), (128, 128, 384, 1024),
+    (128, 1, 128, 8), (128, 1, 256, 328),
+])
+def test_blockwise(br, bc, rows, cols):
+    x = adversarial((rows, cols), 500 + rows + cols + br)
+    x[:br, :bc] = 0                                             # zero block
+    q, s = blockwise(bf16_dev(x), br, bc)
+    oq, os_ = oracle.quantize_blockwise(x, br, bc)
+    assert_same_bytes(q, oq, f"blockwise {br}x{bc} q")
+    assert_same_bytes(s, os_, f"blockwise {br}x{bc} scales")
+
+
+def test_no_nan_codes_anywhere():
+    x = adversarial((256, 1024), 9)
+    for br, bc in ((1, 128), (128, 128)):
+        q, _ = blockwise(bf16_dev(x), br, bc)
+        assert not np.any((q & 0x7F) == 0x7F)
