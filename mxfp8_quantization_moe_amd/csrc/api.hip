@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/mxq.h"
 #include "block_kernels.hpp"
 #include "jagged_kernels.hpp"
@@ -11,7 +13,8 @@ namespace {
 
 using namespace mxq;
 
-constexpr int kJaggedStridedCG = 4;   // 32-column strips, 1024-row passes
+constexpr int kJaggedStridedCG = 4;     // 32-column strips (64-byte row pieces), 1024-row tiles
+constexpr int kJaggedStridedTiles = 3;  // groups up to 3072 rows are read once
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -19,6 +22,22 @@ mxq_status launch_status()
 {
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? MXQ_OK : MXQ_ERR_LAUNCH;
+}
+
+// number of compute units of the current device (queried once per device)
+int device_cu_count()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 // jagged, reduction along the unit-stride dim of a (nrows, ext) view
@@ -31,16 +50,30 @@ mxq_status run_jagged_contig(const uint16_t *x, int64_t nrows, int64_t ext, int6
     if (nrows > INT32_MAX)
         return MXQ_ERR_INVALID_ARG;
     const size_t lds = (size_t)3 * G * sizeof(uint32_t);
-    const dim3 grid((unsigned)nrows), block(kThreads);
-    const int cols = (int)ext;
-    if (ext <= 2048)
-        jagged_contig_kernel<1><<<grid, block, lds, st>>>(x, ldx, cols, offs, G, q, ldq, scales, ss_row, ss_g);
-    else if (ext <= 4096)
-        jagged_contig_kernel<2><<<grid, block, lds, st>>>(x, ldx, cols, offs, G, q, ldq, scales, ss_row, ss_g);
-    else if (ext <= 8192)
-        jagged_contig_kernel<4><<<grid, block, lds, st>>>(x, ldx, cols, offs, G, q, ldq, scales, ss_row, ss_g);
-    else
-        jagged_contig_kernel<8><<<grid, block, lds, st>>>(x, ldx, cols, offs, G, q, ldq, scales, ss_row, ss_g);
+    // persistent grid: a few workgroups per compute unit, each walking rows
+    const int64_t per_cu = 4;
+    const int64_t nwg = std::min<int64_t>(nrows, per_cu * device_cu_count());
+    const dim3 grid((unsigned)nwg), block(kThreads);
+    const int rows = (int)nrows, cols = (int)ext;
+    if (ext > 8 * kThreads * 8) {
+        jagged_contig_long_kernel<8><<<dim3((unsigned)nrows), block, lds, st>>>(
+            x, ldx, cols, offs, G, q, ldq, scales, ss_row, ss_g);
+        return launch_status();
+    }
+#define MXQ_CONTIG(NR, TAIL)                                                                       \
+    jagged_contig_kernel<NR, TAIL><<<grid, block, lds, st>>>(x, ldx, rows, cols, offs, G, q, ldq,  \
+                                                            scales, ss_row, ss_g)
+    const bool tail = (ext % 8) != 0;
+    if (ext <= 2048) {
+        if (tail) MXQ_CONTIG(1, true); else MXQ_CONTIG(1, false);
+    } else if (ext <= 4096) {
+        if (tail) MXQ_CONTIG(2, true); else MXQ_CONTIG(2, false);
+    } else if (ext <= 8192) {
+        if (tail) MXQ_CONTIG(4, true); else MXQ_CONTIG(4, false);
+    } else {
+        if (tail) MXQ_CONTIG(8, true); else MXQ_CONTIG(8, false);
+    }
+#undef MXQ_CONTIG
     return launch_status();
 }
 
@@ -55,11 +88,13 @@ mxq_status run_jagged_strided(const uint16_t *x, int64_t ext, int64_t ncols, int
         return MXQ_ERR_INVALID_ARG;
     constexpr int SW = 8 * kJaggedStridedCG;
     const int64_t nstrips = (ncols + SW - 1) / SW;
-    const int64_t nblocks = nstrips * G;
+    const int64_t nsuper = (nstrips + 3) / 4;
+    const int64_t nblocks = 32 * ((G * nsuper + 7) / 8);
     if (nblocks > INT32_MAX)
         return MXQ_ERR_INVALID_ARG;
-    jagged_strided_kernel<kJaggedStridedCG><<<dim3((unsigned)nblocks), dim3(kThreads), 0, st>>>(
-        x, ldx, (int)ext, (int)ncols, offs, G, q, ldq, scales, ss_g, ss_col, (int)nstrips);
+    jagged_strided_kernel<kJaggedStridedCG, kJaggedStridedTiles>
+        <<<dim3((unsigned)nblocks), dim3(kThreads), 0, st>>>(x, ldx, (int)ext, (int)ncols, offs, G, q,
+                                                             ldq, scales, ss_g, ss_col, (int)nsuper);
     return launch_status();
 }
 

@@ -46,6 +46,8 @@ __global__ __launch_bounds__(kBlockThreads) void block_contig_kernel(
     const int t = threadIdx.x;
     const int j = t % LPB;
 
+    // issue every load of the workgroup's U slots before consuming any
+    uint4 v[U][L];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t blk = ((int64_t)blockIdx.x * U + u) * BPW + t / LPB;
@@ -53,15 +55,23 @@ __global__ __launch_bounds__(kBlockThreads) void block_contig_kernel(
         const int64_t r = ok ? blk / nbpr : 0;
         const int64_t b = ok ? blk % nbpr : 0;
         const uint16_t *xp = x + r * ldx + b * B;
+#pragma unroll
+        for (int l = 0; l < L; ++l)
+            v[u][l] = ok ? ld16_nt(xp + 8 * (j + LPB * l)) : make_uint4(0u, 0u, 0u, 0u);
+    }
+
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t blk = ((int64_t)blockIdx.x * U + u) * BPW + t / LPB;
+        const bool ok = blk < nblocks;
+        const int64_t r = ok ? blk / nbpr : 0;
+        const int64_t b = ok ? blk % nbpr : 0;
         uint8_t *qp = q + r * ldq + b * B;
 
-        uint4 v[L];
         uint32_t m = 0u;
 #pragma unroll
-        for (int l = 0; l < L; ++l) {
-            v[l] = ok ? ld16(xp + 8 * (j + LPB * l)) : make_uint4(0u, 0u, 0u, 0u);
-            m = pkmax(m, absmax_u4(v[l]));
-        }
+        for (int l = 0; l < L; ++l)
+            m = pkmax(m, absmax_u4(v[u][l]));
         m = group_max<LPB>(fold2(m));
 
         float s;
@@ -78,7 +88,7 @@ __global__ __launch_bounds__(kBlockThreads) void block_contig_kernel(
         if (ok) {
 #pragma unroll
             for (int l = 0; l < L; ++l)
-                st8(qp + 8 * (j + LPB * l), quant8(v[l], s));
+                st8_nt(qp + 8 * (j + LPB * l), quant8(v[u][l], s));
         }
     }
 }
@@ -122,7 +132,7 @@ __global__ __launch_bounds__(kBlockThreads) void block_strided_kernel(
     uint4 v[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-        v[i] = ok ? ld16(xp + (int64_t)i * ldx) : make_uint4(0u, 0u, 0u, 0u);
+        v[i] = ok ? ld16_nt(xp + (int64_t)i * ldx) : make_uint4(0u, 0u, 0u, 0u);
 
     uint32_t mx[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -206,7 +216,7 @@ __global__ __launch_bounds__(kBlockThreads) void block_strided_kernel(
                    elem8(v[11], jj) * sc[jj]);
         o.w = cvt4(elem8(v[12], jj) * sc[jj], elem8(v[13], jj) * sc[jj], elem8(v[14], jj) * sc[jj],
                    elem8(v[15], jj) * sc[jj]);
-        st16(qp + (int64_t)jj * ldq, o);
+        st16_nt(qp + (int64_t)jj * ldq, o);
     }
 }
 

@@ -70,10 +70,197 @@ __device__ __forceinline__ uint4 load_seg(const uint16_t *xr, int e0, int n)
 
 // ---------------------------------------------------------------- contig
 
+// Per-segment group bookkeeping of the contig kernels.  A segment is the
+// 8 elements [e0, e0 + 8) one lane loads with one 16-byte access.
+struct SegInfo {
+    int g;       // group of element e0 (G if e0 is past every group)
+    bool inb;    // e0 < cols
+    bool fast;   // the whole segment lies inside group g (and inside cols)
+};
+
+__device__ __forceinline__ SegInfo seg_info(const int32_t *s_offs, int G, int g_hint, int e0, int cols)
+{
+    SegInfo si;
+    si.inb = e0 < cols;
+    si.g = advance_group(s_offs, G, g_hint, e0);
+    si.fast = si.inb && si.g < G && e0 + 8 <= s_offs[si.g] && e0 + 8 <= cols;
+    return si;
+}
+
+// Reduce one segment's |x| max into s_amax for every group it touches.
+// `uni`: the caller knows every lane of the wave has a fast segment of the
+// same group gw (one wave max, one atomic); otherwise lanes are grouped by a
+// ballot loop (lanes hold consecutive segments, so few iterations), and the
+// segments that straddle a group boundary fall back to per-element atomics.
+__device__ __forceinline__ void reduce_segment(uint32_t *s_amax, const int32_t *s_offs, int G,
+                                               const uint16_t *xr, const uint4 &v, const SegInfo &si,
+                                               int e0, int cols, bool uni, int gw_uni, int lane)
+{
+    const uint32_t m = si.fast ? fold2(absmax_u4(v)) : 0u;
+    if (uni) {
+        const uint32_t wm = wave_max(m);
+        if (lane == 0 && wm != 0u)
+            atomicMax(&s_amax[gw_uni], wm);
+        return;
+    }
+    bool pending = si.fast;
+#pragma unroll 1
+    while (true) {
+        const uint64_t mask = __ballot(pending);
+        if (mask == 0)
+            break;
+        const int first = __ffsll((unsigned long long)mask) - 1;
+        const int gw = __builtin_amdgcn_readlane(si.g, first);
+        const bool mine = pending && si.g == gw;
+        const uint32_t wm = wave_max(mine ? m : 0u);
+        if (lane == first && wm != 0u)
+            atomicMax(&s_amax[gw], wm);
+        pending = pending && !mine;
+    }
+    if (si.inb && !si.fast) {
+        // rare: re-read the elements one by one (the line is in cache) rather
+        // than index the segment's registers with a runtime element number
+        int gj = si.g;
+#pragma unroll 1
+        for (int j = 0; j < 8 && e0 + j < cols; ++j) {
+            gj = advance_group(s_offs, G, gj, e0 + j);
+            if (gj < G)
+                atomicMax(&s_amax[gj], (uint32_t)xr[e0 + j] & 0x7fffu);
+        }
+    }
+}
+
+// Scale and store one segment (row-major q row qr).
+__device__ __forceinline__ void store_segment(uint8_t *qr, const float *s_scale, const int32_t *s_offs,
+                                              int G, const uint16_t *xr, const uint4 &v,
+                                              const SegInfo &si, int e0, int cols)
+{
+    if (!si.inb)
+        return;
+    if (si.fast) {
+        st8_nt(qr + e0, quant8(v, s_scale[si.g]));
+        return;
+    }
+    int gj = si.g;
+#pragma unroll 1
+    for (int j = 0; j < 8 && e0 + j < cols; ++j) {
+        gj = advance_group(s_offs, G, gj, e0 + j);
+        if (gj < G)
+            qr[e0 + j] = (uint8_t)cvt1(__uint_as_float((uint32_t)xr[e0 + j] << 16) * s_scale[gj]);
+    }
+}
+
 // x row r at x + r*ldx (unit column stride); q row r at q + r*ldq;
-// scales[r*ss_r + g*ss_g].  Dynamic LDS: 3*G words.  Grid: rows.
-template <int NR>
+// scales[r*ss_r + g*ss_g].  Dynamic LDS: 3*G words.  cols <= 2048*NR.
+//
+// Persistent: workgroup b handles rows b, b + gridDim.x, ...  A row is one
+// register chunk (NR 16-byte segments per lane, segment i of lane t at
+// columns 8*(256*i + t)), so the group of every segment is the same for all
+// rows: it is worked out once per workgroup, together with which
+// (wave, segment-slot) pairs are uniform.  Two register buffers alternate:
+// the loads of the next row are in flight while the current row is reduced,
+// scaled and stored.
+template <int NR, bool TAIL>
 __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
+    const uint16_t *__restrict__ x, int64_t ldx, int rows, int cols,
+    const int32_t *__restrict__ offs, int G, uint8_t *__restrict__ q, int64_t ldq,
+    float *__restrict__ scales, int64_t ss_r, int64_t ss_g)
+{
+    extern __shared__ uint32_t smem[];
+    int32_t *s_offs = reinterpret_cast<int32_t *>(smem);
+    uint32_t *s_amax = smem + G;
+    float *s_scale = reinterpret_cast<float *>(smem + 2 * G);
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+
+    auto load_row = [&](uint4 (&d)[NR], int r) __attribute__((always_inline)) {
+        const uint16_t *xr = x + (int64_t)r * ldx;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int e0 = 8 * (i * kThreads + t);
+            d[i] = e0 + 8 <= cols ? ld16_nt(xr + e0) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        if constexpr (TAIL) {
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                const int e0 = 8 * (i * kThreads + t);
+                if (e0 < cols && e0 + 8 > cols)
+                    d[i] = load_seg(xr, e0, cols);
+            }
+        }
+    };
+
+    uint4 va[NR], vb[NR];
+    int row = blockIdx.x;
+    // the first row's loads do not depend on the offsets: issue them before
+    // the offsets are staged in LDS so both latencies overlap
+    if (row < rows)
+        load_row(va, row);
+    for (int g = t; g < G; g += kThreads) {
+        int o = offs[g];
+        s_offs[g] = o < 0 ? 0 : (o > cols ? cols : o);
+        s_amax[g] = 0u;
+    }
+    __syncthreads();
+
+    SegInfo si[NR];
+    uint32_t uni = 0u;   // bit i: every lane of this wave has a fast segment i of one group
+    int gw[NR];
+    {
+        int g = advance_group(s_offs, G, 0, 8 * t);
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int e0 = 8 * (i * kThreads + t);
+            si[i] = seg_info(s_offs, G, g, e0, cols);
+            g = si[i].g;
+            gw[i] = __builtin_amdgcn_readfirstlane(si[i].g);
+            const bool same = si[i].fast && si[i].g == gw[i];
+            if (__ballot(same) == ~0ull)
+                uni |= 1u << i;
+        }
+    }
+
+    auto process_row = [&](uint4 (&cur)[NR], uint4 (&nxt)[NR], int r) __attribute__((always_inline)) {
+        const int next = r + (int)gridDim.x;
+        if (next < rows)
+            load_row(nxt, next);
+        const uint16_t *xr = x + (int64_t)r * ldx;
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+            reduce_segment(s_amax, s_offs, G, xr, cur[i], si[i], 8 * (i * kThreads + t), cols,
+                           (uni >> i) & 1u, gw[i], lane);
+        __syncthreads();
+        // scales; s_amax is reset for the next row, whose atomics come after
+        // the barrier below
+        for (int g = t; g < G; g += kThreads) {
+            const float s = fp32_scale(s_amax[g]);
+            s_amax[g] = 0u;
+            s_scale[g] = s;
+            scales[(int64_t)r * ss_r + (int64_t)g * ss_g] = s;
+        }
+        __syncthreads();
+        uint8_t *qr = q + (int64_t)r * ldq;
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+            store_segment(qr, s_scale, s_offs, G, xr, cur[i], si[i], 8 * (i * kThreads + t), cols);
+    };
+
+    while (row < rows) {
+        process_row(va, vb, row);
+        row += gridDim.x;
+        if (row >= rows)
+            break;
+        process_row(vb, va, row);
+        row += gridDim.x;
+    }
+}
+
+// Rows longer than one register chunk (cols > 2048*NR): one workgroup per
+// row; the row is reduced chunk by chunk, then re-read for the scaling pass
+// (last chunk first: it is still in registers).
+template <int NR>
+__global__ __launch_bounds__(kThreads) void jagged_contig_long_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int cols, const int32_t *__restrict__ offs, int G,
     uint8_t *__restrict__ q, int64_t ldq, float *__restrict__ scales, int64_t ss_r, int64_t ss_g)
 {
@@ -85,6 +272,10 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int64_t row = blockIdx.x;
+    const uint16_t *xr = x + row * ldx;
+    uint8_t *qr = q + row * ldq;
+    constexpr int kChunk = 8 * kThreads * NR;
+    const int nchunks = (cols + kChunk - 1) / kChunk;
 
     for (int g = t; g < G; g += kThreads) {
         int o = offs[g];
@@ -93,101 +284,110 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
     }
     __syncthreads();
 
-    const uint16_t *xr = x + row * ldx;
-    uint8_t *qr = q + row * ldq;
-    constexpr int kChunk = 8 * kThreads * NR;
-    const int nchunks = (cols + kChunk - 1) / kChunk;
-
     uint4 v[NR];
+    auto load_chunk = [&](int cbase) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int e0 = cbase + 8 * (i * kThreads + t);
+            v[i] = e0 + 8 <= cols ? ld16(xr + e0) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int e0 = cbase + 8 * (i * kThreads + t);
+            if (e0 < cols && e0 + 8 > cols)
+                v[i] = load_seg(xr, e0, cols);
+        }
+    };
 
-    // pass 1: amax per group
     for (int c = 0; c < nchunks; ++c) {
         const int cbase = c * kChunk;
+        load_chunk(cbase);
         int g = advance_group(s_offs, G, 0, cbase + 8 * t);
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
             const int e0 = cbase + 8 * (i * kThreads + t);
-            const bool inb = e0 < cols;
-            v[i] = inb ? load_seg(xr, e0, cols) : make_uint4(0u, 0u, 0u, 0u);
-            g = advance_group(s_offs, G, g, e0);
-            const bool fast = inb && g < G && e0 + 8 <= s_offs[g] && e0 + 8 <= cols;
-            const uint32_t m = fast ? fold2(absmax_u4(v[i])) : 0u;
-            const int gw = __builtin_amdgcn_readfirstlane(g);
-            const bool mine = fast && g == gw;
-            const uint32_t wm = wave_max(mine ? m : 0u);
-            if (lane == 0 && gw < G && wm != 0u)
-                atomicMax(&s_amax[gw], wm);
-            if (fast && !mine) {
-                atomicMax(&s_amax[g], m);
-            } else if (inb && !fast) {
-                int gj = g;
-#pragma unroll 1
-                for (int j = 0; j < 8 && e0 + j < cols; ++j) {
-                    gj = advance_group(s_offs, G, gj, e0 + j);
-                    if (gj < G)
-                        atomicMax(&s_amax[gj], elem8_bits(v[i], j) & 0x7fffu);
-                }
-            }
+            const SegInfo si = seg_info(s_offs, G, g, e0, cols);
+            g = si.g;
+            reduce_segment(s_amax, s_offs, G, xr, v[i], si, e0, cols, false, 0, lane);
         }
     }
     __syncthreads();
-
     for (int g = t; g < G; g += kThreads) {
         const float s = fp32_scale(s_amax[g]);
         s_scale[g] = s;
         scales[row * ss_r + (int64_t)g * ss_g] = s;
     }
     __syncthreads();
-
-    // pass 2: scale and store, last chunk first (it is still in registers)
     for (int c = nchunks - 1; c >= 0; --c) {
         const int cbase = c * kChunk;
+        if (c != nchunks - 1)
+            load_chunk(cbase);
         int g = advance_group(s_offs, G, 0, cbase + 8 * t);
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
             const int e0 = cbase + 8 * (i * kThreads + t);
-            const bool inb = e0 < cols;
-            if (c != nchunks - 1 && inb)
-                v[i] = load_seg(xr, e0, cols);
-            g = advance_group(s_offs, G, g, e0);
-            if (!inb)
-                continue;
-            const bool fast = g < G && e0 + 8 <= s_offs[g] && e0 + 8 <= cols;
-            if (fast) {
-                st8(qr + e0, quant8(v[i], s_scale[g]));
-            } else {
-                int gj = g;
-#pragma unroll 1
-                for (int j = 0; j < 8 && e0 + j < cols; ++j) {
-                    gj = advance_group(s_offs, G, gj, e0 + j);
-                    if (gj < G)
-                        qr[e0 + j] = (uint8_t)cvt1(elem8(v[i], j) * s_scale[gj]);
-                }
-            }
+            const SegInfo si = seg_info(s_offs, G, g, e0, cols);
+            g = si.g;
+            store_segment(qr, s_scale, s_offs, G, xr, v[i], si, e0, cols);
         }
     }
 }
 
 // --------------------------------------------------------------- strided
 
+// Mapping of workgroups to (group rank, column strip).  Four strips of 8*CG
+// columns make one "superstrip"; the four workgroups of a superstrip get
+// block ids that differ by 8, so with the round-robin placement of
+// workgroups on the 8 XCDs they share one XCD (and its L2) and are
+// dispatched back to back: the 8*CG*2-byte row pieces they read complete
+// each other's cache lines.  Superstrips are numbered rank-major, ranks
+// ordered largest group first.
+struct StripMap {
+    int rank, strip;
+    bool valid;
+};
+
+__device__ __forceinline__ StripMap map_strip(int b, int nsuper, int G)
+{
+    const int x = b & 7;             // XCD slot
+    const int k = b >> 3;
+    const int sub = k & 3;           // strip within the superstrip
+    const int S = (k >> 2) * 8 + x;  // logical superstrip index
+    StripMap m;
+    m.rank = S / nsuper;
+    m.strip = (S % nsuper) * 4 + sub;
+    m.valid = m.rank < G;
+    return m;
+}
+
 // x: (rows, cols), row r at x + r*ldx, unit column stride, cols % 8 == 0.
 // q: column-major, element (r, c) at q[c*ldq + r].
 // scales[g*ss_g + c*ss_c].
-// Grid: G * nstrips workgroups; CG column groups of 8 per wave.
-template <int CG>
+// Each lane holds a 16-row x 8-column piece; a wave stacks 64/CG pieces
+// down the rows and CG across; four waves stack down the rows, so one
+// register tile covers TROWS = 4*16*64/CG rows x 8*CG columns.  Up to T
+// tiles stay resident: a group of at most T*TROWS rows is read from HBM
+// once.  Longer groups stream their tiles beyond the first T-1 through the
+// last buffer and re-read them in the scaling pass.
+// Grid: 32 * ceil(G * nsuper / 8) workgroups (see map_strip).
+template <int CG, int T>
 __global__ __launch_bounds__(kThreads) void jagged_strided_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int rows, int cols,
     const int32_t *__restrict__ offs, int G, uint8_t *__restrict__ q, int64_t ldq,
-    float *__restrict__ scales, int64_t ss_g, int64_t ss_c, int nstrips)
+    float *__restrict__ scales, int64_t ss_g, int64_t ss_c, int nsuper)
 {
-    constexpr int QD = 64 / CG;       // 16-row blocks per wave
+    constexpr int QD = 64 / CG;       // 16-row pieces per wave
     constexpr int WROWS = 16 * QD;    // rows per wave
-    constexpr int TROWS = 4 * WROWS;  // rows per workgroup pass
+    constexpr int TROWS = 4 * WROWS;  // rows per register tile
     constexpr int SW = 8 * CG;        // strip width in columns
 
     __shared__ int s_group;
     __shared__ uint32_t s_red[4][SW];
     __shared__ float s_scale[SW];
+
+    const StripMap sm = map_strip(blockIdx.x, nsuper, G);
+    if (!sm.valid)
+        return;
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -195,75 +395,129 @@ __global__ __launch_bounds__(kThreads) void jagged_strided_kernel(
     const int cg = lane % CG;
     const int qd = lane / CG;
 
-    const int rank = blockIdx.x / nstrips;
-    const int strip = blockIdx.x % nstrips;
-
-    // largest group first (ties by index) when G is small enough to rank here
+    // group of this rank: largest first (ties by index) when G is small
+    // enough to rank here, identity otherwise.  The offsets are read from
+    // global memory once (one load per thread) and ranked from LDS.
+    __shared__ int s_lo[64], s_hi[64];
     if (G <= 64) {
         if (t < G) {
-            auto len = [&](int g) {
-                int lo = g == 0 ? 0 : offs[g - 1];
-                int hi = offs[g];
-                lo = lo < 0 ? 0 : (lo > rows ? rows : lo);
-                hi = hi < lo ? lo : (hi > rows ? rows : hi);
-                return hi - lo;
-            };
-            const int mine = len(t);
+            int lo_t = t == 0 ? 0 : offs[t - 1];
+            int hi_t = offs[t];
+            lo_t = lo_t < 0 ? 0 : (lo_t > rows ? rows : lo_t);
+            hi_t = hi_t < lo_t ? lo_t : (hi_t > rows ? rows : hi_t);
+            s_lo[t] = lo_t;
+            s_hi[t] = hi_t;
+        }
+        __syncthreads();
+        if (t < G) {
+            const int mine = s_hi[t] - s_lo[t];
             int r = 0;
             for (int h = 0; h < G; ++h) {
-                const int lh = len(h);
+                const int lh = s_hi[h] - s_lo[h];
                 r += (lh > mine) || (lh == mine && h < t);
             }
-            if (r == rank)
+            if (r == sm.rank)
                 s_group = t;
         }
     } else if (t == 0) {
-        s_group = rank;
+        const int gg = sm.rank;
+        int lo_t = gg == 0 ? 0 : offs[gg - 1];
+        int hi_t = offs[gg];
+        lo_t = lo_t < 0 ? 0 : (lo_t > rows ? rows : lo_t);
+        hi_t = hi_t < lo_t ? lo_t : (hi_t > rows ? rows : hi_t);
+        s_group = 0;
+        s_lo[0] = lo_t;
+        s_hi[0] = hi_t;
     }
     __syncthreads();
-    const int g = s_group;
+    const int g = G <= 64 ? s_group : sm.rank;
+    const int slot = G <= 64 ? g : 0;
+    const int lo = s_lo[slot];
+    const int hi = s_hi[slot];
 
-    int lo = g == 0 ? 0 : offs[g - 1];
-    int hi = offs[g];
-    lo = lo < 0 ? 0 : (lo > rows ? rows : lo);
-    hi = hi < lo ? lo : (hi > rows ? rows : hi);
-
-    const int cbase = strip * SW + 8 * cg;
+    const int cbase = sm.strip * SW + 8 * cg;
     const bool col_ok = cbase < cols;
     const int rbeg = lo & ~15;
     const int nit = hi > lo ? (hi - rbeg + TROWS - 1) / TROWS : 0;
 
-    uint4 v[16];
-    auto load_tile = [&](int it) {
+    uint4 v[T][16];
+
+    // one register tile: 16 rows x 8 columns per lane; rows outside [lo, hi)
+    // are neither read nor counted.  Tiles that will be read again (keep)
+    // use ordinary loads, the others the streaming hint.
+    auto load_tile = [&](uint4 (&d)[16], int it, bool keep) {
         const int rb = rbeg + it * TROWS + w * WROWS + 16 * qd;
         const bool full = rb >= lo && rb + 16 <= hi;
         const uint16_t *p = x + (int64_t)rb * ldx + cbase;
         if (col_ok && full) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                v[i] = ld16(p + (int64_t)i * ldx);
+                d[i] = keep ? ld16(p + (int64_t)i * ldx) : ld16_nt(p + (int64_t)i * ldx);
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int r = rb + i;
-                v[i] = (col_ok && r >= lo && r < hi) ? ld16(p + (int64_t)i * ldx)
+                d[i] = (col_ok && r >= lo && r < hi) ? ld16(p + (int64_t)i * ldx)
                                                       : make_uint4(0u, 0u, 0u, 0u);
             }
         }
     };
-
-    // pass 1: per-column amax over the group's rows
-    uint32_t mx[4] = {0u, 0u, 0u, 0u};
-    for (int it = 0; it < nit; ++it) {
-        load_tile(it);
+    auto accumulate = [&](uint32_t (&mx)[4], const uint4 (&d)[16]) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            mx[0] = absmax2(mx[0], v[i].x);
-            mx[1] = absmax2(mx[1], v[i].y);
-            mx[2] = absmax2(mx[2], v[i].z);
-            mx[3] = absmax2(mx[3], v[i].w);
+            mx[0] = absmax2(mx[0], d[i].x);
+            mx[1] = absmax2(mx[1], d[i].y);
+            mx[2] = absmax2(mx[2], d[i].z);
+            mx[3] = absmax2(mx[3], d[i].w);
         }
+    };
+    auto store_tile = [&](const uint4 (&d)[16], int it, const float (&sc)[8]) {
+        if (!col_ok)
+            return;
+        const int rb = rbeg + it * TROWS + w * WROWS + 16 * qd;
+        const bool full = rb >= lo && rb + 16 <= hi;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint4 o;
+            o.x = cvt4(elem8(d[0], j) * sc[j], elem8(d[1], j) * sc[j], elem8(d[2], j) * sc[j],
+                       elem8(d[3], j) * sc[j]);
+            o.y = cvt4(elem8(d[4], j) * sc[j], elem8(d[5], j) * sc[j], elem8(d[6], j) * sc[j],
+                       elem8(d[7], j) * sc[j]);
+            o.z = cvt4(elem8(d[8], j) * sc[j], elem8(d[9], j) * sc[j], elem8(d[10], j) * sc[j],
+                       elem8(d[11], j) * sc[j]);
+            o.w = cvt4(elem8(d[12], j) * sc[j], elem8(d[13], j) * sc[j], elem8(d[14], j) * sc[j],
+                       elem8(d[15], j) * sc[j]);
+            uint8_t *p = q + (int64_t)(cbase + j) * ldq + rb;
+            if (full) {
+                st16_nt(p, o);
+            } else {
+                const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = rb + i;
+                    if (r >= lo && r < hi)
+                        p[i] = (uint8_t)(ow[i >> 2] >> (8 * (i & 3)));
+                }
+            }
+        }
+    };
+
+    // pass 1: issue the loads of every resident tile, then reduce
+    uint32_t mx[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt)
+        if (tt < nit)
+            load_tile(v[tt], tt, tt == T - 1 && nit > T);
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt)
+        if (tt < nit)
+            accumulate(mx, v[tt]);
+    // tiles beyond the register window stream through the last buffer
+    for (int it = T; it < nit; ++it) {
+        load_tile(v[T - 1], it, true);
+        accumulate(mx, v[T - 1]);
     }
+
 #pragma unroll
     for (int d = 0; d < 4; ++d)
         mx[d] = strided_pkmax<CG>(mx[d]);
@@ -279,7 +533,7 @@ __global__ __launch_bounds__(kThreads) void jagged_strided_kernel(
         const uint32_t a = umax(umax(s_red[0][t], s_red[1][t]), umax(s_red[2][t], s_red[3][t]));
         const float s = fp32_scale(a);
         s_scale[t] = s;
-        const int c = strip * SW + t;
+        const int c = sm.strip * SW + t;
         if (c < cols)
             scales[(int64_t)g * ss_g + (int64_t)c * ss_c] = s;
     }
@@ -290,39 +544,19 @@ __global__ __launch_bounds__(kThreads) void jagged_strided_kernel(
     for (int j = 0; j < 8; ++j)
         sc[j] = s_scale[8 * cg + j];
 
-    // pass 2: scale, transpose in registers, store 16-byte column pieces;
-    // the last pass-1 tile is still in registers
-    for (int it = nit - 1; it >= 0; --it) {
-        if (it != nit - 1)
-            load_tile(it);
-        if (!col_ok)
+    // pass 2: scale, transpose in registers, store 16-byte column pieces
+#pragma unroll
+    for (int tt = 0; tt < T - 1; ++tt)
+        if (tt < nit)
+            store_tile(v[tt], tt, sc);
+    // the last buffer holds tile nit-1 (or T-1); walk the streamed tiles
+    // backwards so the most recently read ones are re-read first
+    for (int it = (nit > T ? nit : T) - 1; it >= T - 1; --it) {
+        if (it >= nit)
             continue;
-        const int rb = rbeg + it * TROWS + w * WROWS + 16 * qd;
-        const bool full = rb >= lo && rb + 16 <= hi;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            uint4 o;
-            o.x = cvt4(elem8(v[0], j) * sc[j], elem8(v[1], j) * sc[j], elem8(v[2], j) * sc[j],
-                       elem8(v[3], j) * sc[j]);
-            o.y = cvt4(elem8(v[4], j) * sc[j], elem8(v[5], j) * sc[j], elem8(v[6], j) * sc[j],
-                       elem8(v[7], j) * sc[j]);
-            o.z = cvt4(elem8(v[8], j) * sc[j], elem8(v[9], j) * sc[j], elem8(v[10], j) * sc[j],
-                       elem8(v[11], j) * sc[j]);
-            o.w = cvt4(elem8(v[12], j) * sc[j], elem8(v[13], j) * sc[j], elem8(v[14], j) * sc[j],
-                       elem8(v[15], j) * sc[j]);
-            uint8_t *p = q + (int64_t)(cbase + j) * ldq + rb;
-            if (full) {
-                st16(p, o);
-            } else {
-                const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = rb + i;
-                    if (r >= lo && r < hi)
-                        p[i] = (uint8_t)(ow[i >> 2] >> (8 * (i & 3)));
-                }
-            }
-        }
+        if (it != nit - 1)
+            load_tile(v[T - 1], it, true);
+        store_tile(v[T - 1], it, sc);
     }
 }
 

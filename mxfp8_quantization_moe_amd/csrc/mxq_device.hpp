@@ -122,9 +122,29 @@ __device__ __forceinline__ uint32_t xor_max(uint32_t v, int lanemask)
     return v > o ? v : o;
 }
 
-// global memory access helpers: 16-byte loads, 16/8-byte stores
+// global memory access helpers: 16-byte loads, 16/8-byte stores.  The
+// streaming ("nt") forms carry the nontemporal hint: data read or written
+// once should not displace lines that are still wanted in L2 / the MALL.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint4 ld16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ uint4 ld16_nt(const uint16_t *p)
+{
+    u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ void st16(uint8_t *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+__device__ __forceinline__ void st16_nt(uint8_t *p, uint4 v)
+{
+    u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t *>(p));
+}
 __device__ __forceinline__ void st8(uint8_t *p, uint2 v) { *reinterpret_cast<uint2 *>(p) = v; }
+__device__ __forceinline__ void st8_nt(uint8_t *p, uint2 v)
+{
+    u32x2_t w = {v.x, v.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t *>(p));
+}
 
 }  // namespace mxq
