@@ -178,7 +178,27 @@ def build_blockwise(torch, mxq, workloads):
     return [l1, l2], [da, dw, qa, sa, qw, sw], desc, cpu_sample
 
 
+def build_copy(torch):
+    """Calibration: a plain device-to-device copy of 256 MiB (torch's copy,
+    i.e. the runtime's copy kernel).  Its FETCH_SIZE / WRITE_SIZE counters
+    against the known 256 MiB read and written give the scale factors that
+    turn those counters into HBM bytes."""
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+
+    class CopyLaunch(Launch):
+        def __call__(self, stream_handle):
+            dst.copy_(src)
+
+    l = CopyLaunch("d2d copy 256 MiB", "copyBuffer", None, (), 2 * n, n)
+    desc = {"workload": "copy_256MiB", "tensors": "uint8 256 MiB -> 256 MiB (calibration)"}
+    return [l], [src, dst], desc, None
+
+
 def build(name, torch, mxq, workloads):
+    if name == "copy":
+        return build_copy(torch)
     if name == "moe_bwd":
         return build_moe_bwd(torch, mxq, workloads)
     if name == "mx3d":
@@ -270,10 +290,10 @@ def main():
                for i, l in enumerate(launches)}
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and cpu_sample is not None:
         import oracle
 
-        n = args.cpu_sample_rows or {"moe_bwd": 4096, "blockwise": 2048}.get(desc["workload"], 128)
+        n = args.cpu_sample_rows or {"moe_bwd": 4096, "blockwise": 2048}.get(args.workload, 256)
         print(f"[bench] timing the CPU oracle on a sample (n={n})", file=sys.stderr, flush=True)
         dt, nbytes, what = cpu_sample(oracle, n)
         cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",

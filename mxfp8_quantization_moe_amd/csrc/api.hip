@@ -5,7 +5,7 @@
 
 #include <algorithm>
 
-#include "../../include/mxq.h"
+#include "mxq.h"
 #include "block_kernels.hpp"
 #include "jagged_kernels.hpp"
 

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kBlockThreads) void block_contig_kernel(
         if (ok) {
 #pragma unroll
             for (int l = 0; l < L; ++l)
-                st8_nt(qp + 8 * (j + LPB * l), quant8(v[u][l], s));
+                st8_nt(qp + 8 * (j + LPB * l), E8M0 ? quant8(v[u][l], s) : quant8_fp32scale(v[u][l], s));
         }
     }
 }
@@ -208,13 +208,13 @@ __global__ __launch_bounds__(kBlockThreads) void block_strided_kernel(
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
         uint4 o;
-        o.x = cvt4(elem8(v[0], jj) * sc[jj], elem8(v[1], jj) * sc[jj], elem8(v[2], jj) * sc[jj],
+        o.x = cvt4_sel<E8M0>(elem8(v[0], jj) * sc[jj], elem8(v[1], jj) * sc[jj], elem8(v[2], jj) * sc[jj],
                    elem8(v[3], jj) * sc[jj]);
-        o.y = cvt4(elem8(v[4], jj) * sc[jj], elem8(v[5], jj) * sc[jj], elem8(v[6], jj) * sc[jj],
+        o.y = cvt4_sel<E8M0>(elem8(v[4], jj) * sc[jj], elem8(v[5], jj) * sc[jj], elem8(v[6], jj) * sc[jj],
                    elem8(v[7], jj) * sc[jj]);
-        o.z = cvt4(elem8(v[8], jj) * sc[jj], elem8(v[9], jj) * sc[jj], elem8(v[10], jj) * sc[jj],
+        o.z = cvt4_sel<E8M0>(elem8(v[8], jj) * sc[jj], elem8(v[9], jj) * sc[jj], elem8(v[10], jj) * sc[jj],
                    elem8(v[11], jj) * sc[jj]);
-        o.w = cvt4(elem8(v[12], jj) * sc[jj], elem8(v[13], jj) * sc[jj], elem8(v[14], jj) * sc[jj],
+        o.w = cvt4_sel<E8M0>(elem8(v[12], jj) * sc[jj], elem8(v[13], jj) * sc[jj], elem8(v[14], jj) * sc[jj],
                    elem8(v[15], jj) * sc[jj]);
         st16_nt(qp + (int64_t)jj * ldq, o);
     }

@@ -138,7 +138,7 @@ __device__ __forceinline__ void store_segment(uint8_t *qr, const float *s_scale,
     if (!si.inb)
         return;
     if (si.fast) {
-        st8_nt(qr + e0, quant8(v, s_scale[si.g]));
+        st8_nt(qr + e0, quant8_fp32scale(v, s_scale[si.g]));
         return;
     }
     int gj = si.g;
@@ -206,6 +206,7 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
 
     SegInfo si[NR];
     uint32_t uni = 0u;   // bit i: every lane of this wave has a fast segment i of one group
+    bool lane_fast = true;  // every segment of this lane is fast
     int gw[NR];
     {
         int g = advance_group(s_offs, G, 0, 8 * t);
@@ -218,6 +219,7 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
             const bool same = si[i].fast && si[i].g == gw[i];
             if (__ballot(same) == ~0ull)
                 uni |= 1u << i;
+            lane_fast = lane_fast && si[i].fast;
         }
     }
 
@@ -226,10 +228,38 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
         if (next < rows)
             load_row(nxt, next);
         const uint16_t *xr = x + (int64_t)r * ldx;
+        if (uni == (1u << NR) - 1u) {
+            // every slot uniform: all wave maxima first (independent chains),
+            // then one lane merges consecutive slots of the same group and
+            // issues one LDS atomic per run
+            uint32_t wm[NR];
 #pragma unroll
-        for (int i = 0; i < NR; ++i)
-            reduce_segment(s_amax, s_offs, G, xr, cur[i], si[i], 8 * (i * kThreads + t), cols,
-                           (uni >> i) & 1u, gw[i], lane);
+            for (int i = 0; i < NR; ++i)
+                wm[i] = wave_max(fold2(absmax_u4(cur[i])));
+            if (lane == 0) {
+                uint32_t acc = wm[0];
+#pragma unroll
+                for (int i = 1; i < NR; ++i) {
+                    if (gw[i] == gw[i - 1]) {
+                        acc = umax(acc, wm[i]);
+                    } else {
+                        if (acc != 0u)
+                            atomicMax(&s_amax[gw[i - 1]], acc);
+                        acc = wm[i];
+                    }
+                }
+                if (acc != 0u)
+                    atomicMax(&s_amax[gw[NR - 1]], acc);
+            }
+        } else {
+            // a group boundary falls inside this wave's window of some slot:
+            // uniform slots keep the single wave max, the others take the
+            // general path
+#pragma unroll
+            for (int i = 0; i < NR; ++i)
+                reduce_segment(s_amax, s_offs, G, xr, cur[i], si[i], 8 * (i * kThreads + t), cols,
+                               (uni >> i) & 1u, gw[i], lane);
+        }
         __syncthreads();
         // scales; s_amax is reset for the next row, whose atomics come after
         // the barrier below
@@ -241,9 +271,19 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
         }
         __syncthreads();
         uint8_t *qr = q + (int64_t)r * ldq;
+        if (lane_fast) {
+            float sc[NR];
 #pragma unroll
-        for (int i = 0; i < NR; ++i)
-            store_segment(qr, s_scale, s_offs, G, xr, cur[i], si[i], 8 * (i * kThreads + t), cols);
+            for (int i = 0; i < NR; ++i)
+                sc[i] = s_scale[si[i].g];
+#pragma unroll
+            for (int i = 0; i < NR; ++i)
+                st8_nt(qr + 8 * (i * kThreads + t), quant8_fp32scale(cur[i], sc[i]));
+        } else {
+#pragma unroll
+            for (int i = 0; i < NR; ++i)
+                store_segment(qr, s_scale, s_offs, G, xr, cur[i], si[i], 8 * (i * kThreads + t), cols);
+        }
     };
 
     while (row < rows) {
@@ -479,13 +519,13 @@ __global__ __launch_bounds__(kThreads) void jagged_strided_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             uint4 o;
-            o.x = cvt4(elem8(d[0], j) * sc[j], elem8(d[1], j) * sc[j], elem8(d[2], j) * sc[j],
+            o.x = cvt4_nosat(elem8(d[0], j) * sc[j], elem8(d[1], j) * sc[j], elem8(d[2], j) * sc[j],
                        elem8(d[3], j) * sc[j]);
-            o.y = cvt4(elem8(d[4], j) * sc[j], elem8(d[5], j) * sc[j], elem8(d[6], j) * sc[j],
+            o.y = cvt4_nosat(elem8(d[4], j) * sc[j], elem8(d[5], j) * sc[j], elem8(d[6], j) * sc[j],
                        elem8(d[7], j) * sc[j]);
-            o.z = cvt4(elem8(d[8], j) * sc[j], elem8(d[9], j) * sc[j], elem8(d[10], j) * sc[j],
+            o.z = cvt4_nosat(elem8(d[8], j) * sc[j], elem8(d[9], j) * sc[j], elem8(d[10], j) * sc[j],
                        elem8(d[11], j) * sc[j]);
-            o.w = cvt4(elem8(d[12], j) * sc[j], elem8(d[13], j) * sc[j], elem8(d[14], j) * sc[j],
+            o.w = cvt4_nosat(elem8(d[12], j) * sc[j], elem8(d[13], j) * sc[j], elem8(d[14], j) * sc[j],
                        elem8(d[15], j) * sc[j]);
             uint8_t *p = q + (int64_t)(cbase + j) * ldq + rb;
             if (full) {

@@ -86,12 +86,48 @@ __device__ __forceinline__ uint32_t cvt1(float a)
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat(a), 0.0f, 0, false) & 0xffu;
 }
 
+// Unclamped form for the fp32-multiplier paths.  With s = RN32(448 / m),
+// m = max(amax, eps) >= |x|, every product obeys
+// |RN32(x * s)| <= RN32(448 * (1 + 2^-24)) <= 448 + 2^-15 < 464, and
+// v_cvt_pk_fp8_f32 rounds to nearest even exactly below the 448/480 midpoint
+// 464 (checked on gfx950 over every fp32 pattern in [2^-13, 1024] and a
+// sample of the rest), so a clamp would never change a result there.  The
+// conversion writes only the selected half of its destination; `a` is dead
+// after the call, so its register serves as the destination without a move.
+__device__ __forceinline__ uint32_t cvt4_nosat(float a, float b, float c, float d)
+{
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)__float_as_uint(a), false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+    return (uint32_t)r;
+}
+
+// SAT: e8m0 paths (scaled values reach 512 and need the clamp); !SAT: fp32
+// multiplier paths
+template <bool SAT>
+__device__ __forceinline__ uint32_t cvt4_sel(float a, float b, float c, float d)
+{
+    if constexpr (SAT)
+        return cvt4(a, b, c, d);
+    else
+        return cvt4_nosat(a, b, c, d);
+}
+
 // eight bf16 (one 16-byte load) times one multiplier -> eight bytes
 __device__ __forceinline__ uint2 quant8(const uint4 &v, float s)
 {
     uint2 r;
     r.x = cvt4(bf16_lo(v.x) * s, bf16_hi(v.x) * s, bf16_lo(v.y) * s, bf16_hi(v.y) * s);
     r.y = cvt4(bf16_lo(v.z) * s, bf16_hi(v.z) * s, bf16_lo(v.w) * s, bf16_hi(v.w) * s);
+    return r;
+}
+
+// the same for an fp32 multiplier s = 448 / max(amax, eps) of a group or
+// block containing every element of v (no clamp needed, see cvt4_nosat)
+__device__ __forceinline__ uint2 quant8_fp32scale(const uint4 &v, float s)
+{
+    uint2 r;
+    r.x = cvt4_nosat(bf16_lo(v.x) * s, bf16_hi(v.x) * s, bf16_lo(v.y) * s, bf16_hi(v.y) * s);
+    r.y = cvt4_nosat(bf16_lo(v.z) * s, bf16_hi(v.z) * s, bf16_lo(v.w) * s, bf16_hi(v.w) * s);
     return r;
 }
 
@@ -106,20 +142,6 @@ __device__ __forceinline__ uint32_t elem8_bits(const uint4 &v, int j)
 {
     uint32_t d = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
     return (j & 1) ? (d >> 16) : (d & 0xffffu);
-}
-
-// packed |bf16| max of the column pair (2d, 2d+1) of a 16-byte load
-__device__ __forceinline__ uint32_t dword_of(const uint4 &v, int d)
-{
-    return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
-}
-
-// wave-level max over lanes that differ in the bits of `mask` (power of two
-// steps), via ds_swizzle-free cross-lane shuffles
-__device__ __forceinline__ uint32_t xor_max(uint32_t v, int lanemask)
-{
-    uint32_t o = (uint32_t)__shfl_xor((int)v, lanemask, 64);
-    return v > o ? v : o;
 }
 
 // global memory access helpers: 16-byte loads, 16/8-byte stores.  The
