@@ -125,7 +125,7 @@ def build_mx3d(torch, mxq, workloads, E, sweep):
         w[e].copy_(bf16_dev(torch, bits))
     q = torch.empty(E * N * K, dtype=torch.uint8, device="cuda")
     s = torch.empty(E * (N // 32) * K, dtype=torch.uint8, device="cuda")
-    l = Launch(f"mx_3d_colwise ({E},{N},{K})", "block_strided_kernel<32,1,e8m0>",
+    l = Launch(f"mx_3d_colwise ({E},{N},{K})", "block_strided_kernel<32, 1, true>",
                mxq.mxq_quantize_mx_3d_colwise,
                (w.data_ptr(), E, N, K, N * K, K, 1, q.data_ptr(), N * K, 1, N, s.data_ptr(),
                 (N // 32) * K, K, 1, 0), 3 * E * N * K + E * (N // 32) * K, E * N * K)
@@ -153,11 +153,11 @@ def build_blockwise(torch, mxq, workloads):
     sa = torch.empty(M * (Kd // 128), dtype=torch.float32, device="cuda")
     qw = torch.empty(R * C, dtype=torch.uint8, device="cuda")
     sw = torch.empty((R // 128) * (C // 128), dtype=torch.float32, device="cuda")
-    l1 = Launch("blockwise 1x128 act (8192,4096)", "block_contig_kernel<128>",
+    l1 = Launch("blockwise 1x128 act (8192,4096)", "block_contig_kernel<128, 8, false",
                 mxq.mxq_quantize_blockwise,
                 (da.data_ptr(), M, Kd, Kd, 1, 1, 128, qa.data_ptr(), Kd, 1, sa.data_ptr(),
                  Kd // 128, 1), 3 * M * Kd + 4 * M * (Kd // 128), M * Kd)
-    l2 = Launch("blockwise 128x128 W (4096,4096)", "block_strided_kernel<128,128>",
+    l2 = Launch("blockwise 128x128 W (4096,4096)", "block_strided_kernel<128, 128, false>",
                 mxq.mxq_quantize_blockwise,
                 (dw.data_ptr(), R, C, C, 1, 128, 128, qw.data_ptr(), 1, R, sw.data_ptr(),
                  C // 128, 1), 3 * R * C + 4 * (R // 128) * (C // 128), R * C)
@@ -213,8 +213,9 @@ def build(name, torch, mxq, workloads):
 # -------------------------------------------------------------------- run
 
 def traffic_for(kernel_name: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel sources; else None."""
+    """HBM bytes per launch of `kernel_name` in `workload` from the committed
+    rocprofv3 counter summary (profiles/traffic.json), if it was taken on the
+    current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -224,10 +225,11 @@ def traffic_for(kernel_name: str, workload: str):
         return None
     if data.get("csrc_digest") != csrc_digest():
         return None
-    entry = data.get("kernels", {}).get(f"{workload}:{kernel_name}")
-    if not entry:
-        return None
-    return entry.get("hbm_bytes_per_launch")
+    for key, entry in data.get("kernels", {}).items():
+        wl, _, kern = key.partition(":")
+        if wl == workload and kern.startswith("mxq::" + kernel_name):
+            return entry.get("hbm_bytes_per_launch")
+    return None
 
 
 def main():
@@ -282,7 +284,7 @@ def main():
     dom = int(np.argmax(per_kernel_ms))
     dl = launches[dom]
     achieved = dl.nbytes / (per_kernel_ms[dom] * 1e-3) / 1e9
-    traffic = traffic_for(dl.kernel, desc["workload"])
+    traffic = traffic_for(dl.kernel, args.workload)
     kernels = {l.name: {"avg_us": round(per_kernel_ms[i] * 1e3, 2),
                         "algorithmic_bytes": l.nbytes,
                         "GBps": round(l.nbytes / (per_kernel_ms[i] * 1e-3) / 1e9, 1),
