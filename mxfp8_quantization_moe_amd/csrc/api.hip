@@ -13,8 +13,9 @@ namespace {
 
 using namespace mxq;
 
-constexpr int kJaggedStridedCG = 4;     // 32-column strips (64-byte row pieces), 1024-row tiles
-constexpr int kJaggedStridedTiles = 3;  // groups up to 3072 rows are read once
+constexpr int kJaggedStridedCG = 8;     // 64-column strips (full 128-byte row pieces)
+constexpr int kJaggedStridedTiles = 2;  // register tiles per lane
+constexpr int kJaggedStridedWaves = 8;  // waves per workgroup: tile = 8*16*64/CG = 1024 rows
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -86,15 +87,15 @@ mxq_status run_jagged_strided(const uint16_t *x, int64_t ext, int64_t ncols, int
         return MXQ_OK;
     if (ncols % 8 != 0 || ncols > INT32_MAX)
         return MXQ_ERR_INVALID_ARG;
-    constexpr int SW = 8 * kJaggedStridedCG;
-    const int64_t nstrips = (ncols + SW - 1) / SW;
-    const int64_t nsuper = (nstrips + 3) / 4;
-    const int64_t nblocks = 32 * ((G * nsuper + 7) / 8);
+    constexpr int CG = kJaggedStridedCG, SPS = 8 / CG, NW = kJaggedStridedWaves;
+    const int64_t nstrips = (ncols + 8 * CG - 1) / (8 * CG);
+    const int64_t nsuper = (nstrips + SPS - 1) / SPS;
+    const int64_t nblocks = 8 * SPS * ((G * nsuper + 7) / 8);
     if (nblocks > INT32_MAX)
         return MXQ_ERR_INVALID_ARG;
-    jagged_strided_kernel<kJaggedStridedCG, kJaggedStridedTiles>
-        <<<dim3((unsigned)nblocks), dim3(kThreads), 0, st>>>(x, ldx, (int)ext, (int)ncols, offs, G, q,
-                                                             ldq, scales, ss_g, ss_col, (int)nsuper);
+    jagged_strided_kernel<CG, kJaggedStridedTiles, NW>
+        <<<dim3((unsigned)nblocks), dim3(64 * NW), 0, st>>>(x, ldx, (int)ext, (int)ncols, offs, G, q,
+                                                           ldq, scales, ss_g, ss_col, (int)nsuper);
     return launch_status();
 }
 

@@ -375,27 +375,28 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_long_kernel(
 
 // --------------------------------------------------------------- strided
 
-// Mapping of workgroups to (group rank, column strip).  Four strips of 8*CG
-// columns make one "superstrip"; the four workgroups of a superstrip get
-// block ids that differ by 8, so with the round-robin placement of
-// workgroups on the 8 XCDs they share one XCD (and its L2) and are
-// dispatched back to back: the 8*CG*2-byte row pieces they read complete
-// each other's cache lines.  Superstrips are numbered rank-major, ranks
-// ordered largest group first.
+// Mapping of workgroups to (group rank, column strip).  SPS = 8 / CG strips
+// of 8*CG columns (16*CG bytes of a row) make one 128-byte "superstrip"; the
+// SPS workgroups of a superstrip get block ids that differ by 8, so with the
+// round-robin placement of workgroups on the 8 XCDs they share one XCD (and
+// its L2) and are dispatched back to back: their row pieces complete each
+// other's cache lines.  Superstrips are numbered rank-major, ranks ordered
+// largest group first.
 struct StripMap {
     int rank, strip;
     bool valid;
 };
 
+template <int SPS>
 __device__ __forceinline__ StripMap map_strip(int b, int nsuper, int G)
 {
-    const int x = b & 7;             // XCD slot
+    const int x = b & 7;               // XCD slot
     const int k = b >> 3;
-    const int sub = k & 3;           // strip within the superstrip
-    const int S = (k >> 2) * 8 + x;  // logical superstrip index
+    const int sub = k % SPS;           // strip within the superstrip
+    const int S = (k / SPS) * 8 + x;   // logical superstrip index
     StripMap m;
     m.rank = S / nsuper;
-    m.strip = (S % nsuper) * 4 + sub;
+    m.strip = (S % nsuper) * SPS + sub;
     m.valid = m.rank < G;
     return m;
 }
@@ -409,23 +410,23 @@ __device__ __forceinline__ StripMap map_strip(int b, int nsuper, int G)
 // tiles stay resident: a group of at most T*TROWS rows is read from HBM
 // once.  Longer groups stream their tiles beyond the first T-1 through the
 // last buffer and re-read them in the scaling pass.
-// Grid: 32 * ceil(G * nsuper / 8) workgroups (see map_strip).
-template <int CG, int T>
-__global__ __launch_bounds__(kThreads) void jagged_strided_kernel(
+// Grid: 8 * (8/CG) * ceil(G * nsuper / 8) workgroups (see map_strip).
+template <int CG, int T, int NW>
+__global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int rows, int cols,
     const int32_t *__restrict__ offs, int G, uint8_t *__restrict__ q, int64_t ldq,
     float *__restrict__ scales, int64_t ss_g, int64_t ss_c, int nsuper)
 {
     constexpr int QD = 64 / CG;       // 16-row pieces per wave
     constexpr int WROWS = 16 * QD;    // rows per wave
-    constexpr int TROWS = 4 * WROWS;  // rows per register tile
+    constexpr int TROWS = NW * WROWS; // rows per register tile
     constexpr int SW = 8 * CG;        // strip width in columns
 
     __shared__ int s_group;
-    __shared__ uint32_t s_red[4][SW];
+    __shared__ uint32_t s_red[NW][SW];
     __shared__ float s_scale[SW];
 
-    const StripMap sm = map_strip(blockIdx.x, nsuper, G);
+    const StripMap sm = map_strip<8 / CG>(blockIdx.x, nsuper, G);
     if (!sm.valid)
         return;
 
@@ -570,7 +571,10 @@ __global__ __launch_bounds__(kThreads) void jagged_strided_kernel(
     }
     __syncthreads();
     if (t < SW) {
-        const uint32_t a = umax(umax(s_red[0][t], s_red[1][t]), umax(s_red[2][t], s_red[3][t]));
+        uint32_t a = 0u;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww)
+            a = umax(a, s_red[ww][t]);
         const float s = fp32_scale(a);
         s_scale[t] = s;
         const int c = sm.strip * SW + t;

@@ -97,6 +97,10 @@ def test_jagged_rowwise_empty_extent_writes_empty_group_scales():
     (7000, 24, 100, 1, 0, 16),     # G > 64: identity order
     (17, 264, 5, 1, 0, 17),
     (33, 8, 3, 1, 1, 18),
+    (4100, 16, 1, 1, 0, 19),       # one group longer than the register window
+    (9300, 24, 1, 1, 7, 20),       # ring: several passes, ragged ends
+    (13000, 72, 2, 1, 0, 21),
+    (2049, 40, 2, 1, 0, 22),
 ])
 def test_jagged_colwise_ragged(rows, cols, G, mult, tail, seed):
     bits = adversarial((rows, cols), 200 + seed)
