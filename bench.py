@@ -6,7 +6,8 @@ rowwise quantization of grad_out^T (4096, 16384) plus jagged colwise
 quantization of x (16384, 4096), the same 8 token groups for both, bf16 in,
 e4m3 + fp32 per-group scales out.  One step = both launches.  Other
 workloads (``--workload``): ``mx3d`` (E=8 expert weights, 32x1 MXFP8),
-``mx3d_e{1,2,4,16,64}``, ``blockwise`` (1x128 activations + 128x128 weights).
+``mx3d_e{1,2,4,16,64}``, ``mx3d_rceil`` (E=8 with the rceil scale mode),
+``blockwise`` (1x128 activations + 128x128 weights).
 
 Metric: algorithmic HBM bytes (2 B bf16 read + 1 B e4m3 write + scale bytes
 per launch) divided by time.  Inputs are resident in HBM before the timed
@@ -115,7 +116,7 @@ def build_moe_bwd(torch, mxq, workloads):
     return [l1, l2], keep, desc, cpu_sample
 
 
-def build_mx3d(torch, mxq, workloads, E, sweep):
+def build_mx3d(torch, mxq, workloads, E, sweep, rceil=False):
     import numpy as np
 
     N, K = 8192, 5120
@@ -128,15 +129,16 @@ def build_mx3d(torch, mxq, workloads, E, sweep):
     l = Launch(f"mx_3d_colwise ({E},{N},{K})", "block_strided_kernel<32, 1, true>",
                mxq.mxq_quantize_mx_3d_colwise,
                (w.data_ptr(), E, N, K, N * K, K, 1, q.data_ptr(), N * K, 1, N, s.data_ptr(),
-                (N // 32) * K, K, 1, 0), 3 * E * N * K + E * (N // 32) * K, E * N * K)
-    desc = {"workload": f"mx3d_E{E}" + ("_sweep" if sweep else ""),
+                (N // 32) * K, K, 1, 1 if rceil else 0), 3 * E * N * K + E * (N // 32) * K, E * N * K)
+    mode = "rceil" if rceil else "floor"
+    desc = {"workload": f"mx3d_E{E}" + ("_sweep" if sweep else "") + ("_rceil" if rceil else ""),
             "tensors": f"W bf16 ({E},{N},{K}) -> e4m3 per-expert column-major (N*K,1,N)",
-            "scales": "e8m0 floor, (E, N/32, K)"}
+            "scales": f"e8m0 {mode}, (E, N/32, K)"}
 
     def cpu_sample(oracle, n):
         bits = workloads.mx3d_sweep_expert(0) if sweep else workloads.mx3d_expert(0)
         t0 = time.perf_counter()
-        oracle.quantize_mx_3d_colwise(bits[None, :, :n])
+        oracle.quantize_mx_3d_colwise(bits[None, :, :n], mode=mode)
         dt = time.perf_counter() - t0
         return dt, 3 * N * n + (N // 32) * n, f"expert 0, all N, {n} of {K} columns"
 
@@ -203,6 +205,8 @@ def build(name, torch, mxq, workloads):
         return build_moe_bwd(torch, mxq, workloads)
     if name == "mx3d":
         return build_mx3d(torch, mxq, workloads, 8, sweep=False)
+    if name == "mx3d_rceil":
+        return build_mx3d(torch, mxq, workloads, 8, sweep=False, rceil=True)
     if name.startswith("mx3d_e"):
         return build_mx3d(torch, mxq, workloads, int(name[len("mx3d_e"):]), sweep=True)
     if name == "blockwise":

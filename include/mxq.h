@@ -26,14 +26,14 @@
  * reentrant.
  *
  * Errors (returned before any launch unless stated):
- *   MXQ_ERR_INVALID_ARG  null pointer with a non-empty extent, negative
+ *   MXQ_ERR_INVALID_ARG  a scale_mode that is not an mxq_scale_mode value,
+ *                        null pointer with a non-empty extent, negative
  *                        extent, num_groups outside [1, MXQ_MAX_GROUPS],
  *                        extent not divisible by the block, a pointer or a
  *                        non-unit stride that breaks 16-byte alignment, or a
  *                        unit-stride extent of a column-major store that is
  *                        not a multiple of 8.
- *   MXQ_ERR_UNSUPPORTED  a layout combination with no kernel (see each call),
- *                        or MXQ_SCALE_RCEIL.
+ *   MXQ_ERR_UNSUPPORTED  a layout combination with no kernel (see each call).
  *   MXQ_ERR_LAUNCH       the launch failed (hipGetLastError after launch).
  * A zero extent is not an error: the call writes whatever scales the
  * definition still assigns (an empty group's scale) and returns MXQ_OK.
@@ -57,6 +57,17 @@ typedef enum mxq_status {
     MXQ_ERR_LAUNCH = 3
 } mxq_status;
 
+/*
+ * How an MX block's e8m0 shared exponent se (code se + 127, multiplier
+ * 2^-se) is derived from the block's amax.  Both modes are named, not
+ * defined, by "[mxfp8 moe training] add CUDA kernel to quantize 3d tensor
+ * colwise" (the author's comment); the readings implemented:
+ *   FLOOR  se = floor(log2 amax) - 8 (OCP MX v1.0 rule, emax(E4M3) = 8);
+ *          magnitudes in (448, 512) * 2^se saturate to 448.
+ *   RCEIL  se = the smallest integer with amax <= 448 * 2^se (amax / 448
+ *          rounded up to a power of two); nothing saturates.
+ * Both clamp se to [-127, 127]; a zero block gets code 0.
+ */
 typedef enum mxq_scale_mode { MXQ_SCALE_FLOOR = 0, MXQ_SCALE_RCEIL = 1 } mxq_scale_mode;
 
 /* Version of this ABI (MXQ_ABI_VERSION). */
@@ -122,7 +133,7 @@ mxq_status mxq_quantize_jagged_colwise(const uint16_t *x, int64_t rows, int64_t 
  *         column-major is (N*K, 1, N).
  * scales  (E, N/32, K) e8m0 bytes, strides (ss_e, ss_nb, ss_k).
  * Layout with a kernel: sw_k == 1 && sq_n == 1 (K % 8 == 0).
- * scale_mode: MXQ_SCALE_FLOOR.
+ * scale_mode: MXQ_SCALE_FLOOR or MXQ_SCALE_RCEIL.
  */
 mxq_status mxq_quantize_mx_3d_colwise(const uint16_t *w, int64_t E, int64_t N, int64_t K,
                                       int64_t sw_e, int64_t sw_n, int64_t sw_k, uint8_t *q,
@@ -139,6 +150,7 @@ mxq_status mxq_quantize_mx_3d_colwise(const uint16_t *w, int64_t E, int64_t N, i
  * q       (rows, cols) e4m3, strides (sq_r, sq_c).
  * scales  (rows, cols/32) e8m0, strides (ss_r, ss_b).
  * Layout with a kernel: sx_c == 1 && sq_c == 1.
+ * scale_mode: MXQ_SCALE_FLOOR or MXQ_SCALE_RCEIL.
  */
 mxq_status mxq_quantize_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t sx_r,
                                    int64_t sx_c, uint8_t *q, int64_t sq_r, int64_t sq_c,

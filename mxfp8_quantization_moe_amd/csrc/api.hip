@@ -195,9 +195,7 @@ mxq_status mxq_quantize_mx_3d_colwise(const uint16_t *w, int64_t E, int64_t N, i
 {
     if (E < 0 || N < 0 || K < 0 || N % 32 != 0)
         return MXQ_ERR_INVALID_ARG;
-    if (scale_mode == MXQ_SCALE_RCEIL)
-        return MXQ_ERR_UNSUPPORTED;
-    if (scale_mode != MXQ_SCALE_FLOOR)
+    if (scale_mode != MXQ_SCALE_FLOOR && scale_mode != MXQ_SCALE_RCEIL)
         return MXQ_ERR_INVALID_ARG;
     if (E == 0 || N == 0 || K == 0)
         return MXQ_OK;
@@ -217,7 +215,7 @@ mxq_status mxq_quantize_mx_3d_colwise(const uint16_t *w, int64_t E, int64_t N, i
     block_strided_kernel<32, 1, true><<<dim3((unsigned)nblocks), dim3(kBlockThreads), 0,
                                          reinterpret_cast<hipStream_t>(stream)>>>(
         w, sw_e, sw_n, (int)N, (int)K, q, sq_e, sq_k, scales, ss_e, ss_nb, ss_k, (int)tiles_r,
-        (int)tiles_c);
+        (int)tiles_c, scale_mode == MXQ_SCALE_RCEIL);
     return launch_status();
 }
 
@@ -228,9 +226,7 @@ mxq_status mxq_quantize_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols
 {
     if (rows < 0 || cols < 0 || cols % 32 != 0)
         return MXQ_ERR_INVALID_ARG;
-    if (scale_mode == MXQ_SCALE_RCEIL)
-        return MXQ_ERR_UNSUPPORTED;
-    if (scale_mode != MXQ_SCALE_FLOOR)
+    if (scale_mode != MXQ_SCALE_FLOOR && scale_mode != MXQ_SCALE_RCEIL)
         return MXQ_ERR_INVALID_ARG;
     if (rows == 0 || cols == 0)
         return MXQ_OK;
@@ -248,7 +244,7 @@ mxq_status mxq_quantize_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols
         return MXQ_ERR_INVALID_ARG;
     block_contig_kernel<32, LPB, true, U><<<dim3((unsigned)grid), dim3(kBlockThreads), 0,
                                             reinterpret_cast<hipStream_t>(stream)>>>(
-        x, sx_r, nbpr, nblocks, q, sq_r, scales, ss_r, ss_b);
+        x, sx_r, nbpr, nblocks, q, sq_r, scales, ss_r, ss_b, scale_mode == MXQ_SCALE_RCEIL);
     return launch_status();
 }
 
@@ -287,7 +283,7 @@ mxq_status mxq_quantize_blockwise(const uint16_t *x, int64_t rows, int64_t cols,
         if (grid > INT32_MAX)
             return MXQ_ERR_INVALID_ARG;
         block_contig_kernel<128, LPB, false, U><<<dim3((unsigned)grid), dim3(kBlockThreads), 0, st>>>(
-            x, sx_r, nbpr, nblocks, q, sq_r, scales, ss_rb, ss_cb);
+            x, sx_r, nbpr, nblocks, q, sq_r, scales, ss_rb, ss_cb, 0);
         return launch_status();
     }
     // (128, 128) and (128, 1): row-major in, column-major out
@@ -302,11 +298,11 @@ mxq_status mxq_quantize_blockwise(const uint16_t *x, int64_t rows, int64_t cols,
     if (b128x128)
         block_strided_kernel<128, 128, false><<<dim3((unsigned)nblocks), dim3(kBlockThreads), 0, st>>>(
             x, 0, sx_r, (int)rows, (int)cols, q, 0, sq_c, scales, 0, ss_rb, ss_cb, (int)tiles_r,
-            (int)tiles_c);
+            (int)tiles_c, 0);
     else
         block_strided_kernel<128, 1, false><<<dim3((unsigned)nblocks), dim3(kBlockThreads), 0, st>>>(
             x, 0, sx_r, (int)rows, (int)cols, q, 0, sq_c, scales, 0, ss_rb, ss_cb, (int)tiles_r,
-            (int)tiles_c);
+            (int)tiles_c, 0);
     return launch_status();
 }
 

@@ -37,7 +37,8 @@ constexpr int kBlockThreads = 256;
 template <int B, int LPB, bool E8M0, int U>
 __global__ __launch_bounds__(kBlockThreads) void block_contig_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int64_t nbpr, int64_t nblocks,
-    uint8_t *__restrict__ q, int64_t ldq, void *__restrict__ scales, int64_t ss_r, int64_t ss_b)
+    uint8_t *__restrict__ q, int64_t ldq, void *__restrict__ scales, int64_t ss_r, int64_t ss_b,
+    int rceil)
 {
     constexpr int L = B / (8 * LPB);           // 16-byte pieces per lane per block
     constexpr int BPW = kBlockThreads / LPB;   // blocks per workgroup slot
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(kBlockThreads) void block_contig_kernel(
 
         float s;
         if constexpr (E8M0) {
-            const uint32_t code = e8m0_floor_code(m);
+            const uint32_t code = e8m0_code(m, rceil != 0);
             s = e8m0_multiplier(code);
             if (ok && j == 0)
                 reinterpret_cast<uint8_t *>(scales)[r * ss_r + b * ss_b] = (uint8_t)code;
@@ -105,7 +106,7 @@ template <int BR, int BC, bool E8M0>
 __global__ __launch_bounds__(kBlockThreads) void block_strided_kernel(
     const uint16_t *__restrict__ x, int64_t sxe, int64_t ldx, int rows, int cols,
     uint8_t *__restrict__ q, int64_t sqe, int64_t ldq, void *__restrict__ scales, int64_t sse,
-    int64_t ss_rb, int64_t ss_cb, int tiles_r, int tiles_c)
+    int64_t ss_rb, int64_t ss_cb, int tiles_r, int tiles_c, int rceil)
 {
     static_assert(BR == 32 || BR == 128, "BR");
     static_assert(BC == 1 || (BC == 128 && BR == 128), "BC");
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(kBlockThreads) void block_strided_kernel(
         for (int jj = 0; jj < 8; ++jj) {
             const uint32_t a = (jj & 1) ? (mx[jj >> 1] >> 16) : (mx[jj >> 1] & 0xffffu);
             if constexpr (E8M0) {
-                codes[jj] = e8m0_floor_code(a);
+                codes[jj] = e8m0_code(a, rceil != 0);
                 sc[jj] = e8m0_multiplier(codes[jj]);
             } else {
                 sc[jj] = fp32_scale(a);

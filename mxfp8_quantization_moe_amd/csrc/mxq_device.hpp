@@ -64,6 +64,21 @@ __device__ __forceinline__ uint32_t e8m0_floor_code(uint32_t amax16)
     return f > 8 ? (uint32_t)(f - 8) : 0u;
 }
 
+// e8m0 "rceil" code: the smallest se with amax <= 448 * 2^se (the scale
+// amax / 448 rounded up to a power of two, so nothing saturates).  With
+// amax = (1 + m/128) * 2^(field - 127), 448 = 1.75 * 2^8 and 1.75 = 1 + 96/128:
+// se = field - 135 when m <= 96, else field - 134; clamped at code 0.
+__device__ __forceinline__ uint32_t e8m0_rceil_code(uint32_t amax16)
+{
+    int f = (int)((amax16 >> 7) & 0xffu) - 8 + ((amax16 & 0x7fu) > 96u ? 1 : 0);
+    return f > 0 ? (uint32_t)f : 0u;
+}
+
+__device__ __forceinline__ uint32_t e8m0_code(uint32_t amax16, bool rceil)
+{
+    return rceil ? e8m0_rceil_code(amax16) : e8m0_floor_code(amax16);
+}
+
 // element multiplier 2^(127 - code) for code in [0, 246] (always normal)
 __device__ __forceinline__ float e8m0_multiplier(uint32_t code)
 {

@@ -59,13 +59,16 @@ def _load():
     lib.oracle_fp32_scale.restype = ctypes.c_float
     lib.oracle_e8m0_floor.argtypes = [ctypes.c_float]
     lib.oracle_e8m0_floor.restype = ctypes.c_uint8
+    lib.oracle_e8m0_rceil.argtypes = [ctypes.c_float]
+    lib.oracle_e8m0_rceil.restype = ctypes.c_uint8
     jag = [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _i64, _i64, _vp, _i64, _i64]
     lib.oracle_quantize_jagged_rowwise.argtypes = jag
     lib.oracle_quantize_jagged_colwise.argtypes = jag
     lib.oracle_quantize_mx_3d_colwise.argtypes = [_vp, _i64, _i64, _i64, _i64, _i64, _i64,
-                                                  _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64]
+                                                  _vp, _i64, _i64, _i64, _vp, _i64, _i64, _i64,
+                                                  ctypes.c_int]
     lib.oracle_quantize_mx_rowwise.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64,
-                                               _vp, _i64, _i64]
+                                               _vp, _i64, _i64, ctypes.c_int]
     lib.oracle_quantize_blockwise.argtypes = [_vp, _i64, _i64, _i64, _i64, _i32, _i32, _vp,
                                               _i64, _i64, _vp, _i64, _i64]
     for name in ("oracle_quantize_jagged_rowwise", "oracle_quantize_jagged_colwise",
@@ -125,6 +128,16 @@ def e8m0_floor(amax) -> np.ndarray:
     return np.array(flat, dtype=np.uint8).reshape(a.shape)
 
 
+def e8m0_rceil(amax) -> np.ndarray:
+    lib = _load()
+    a = np.asarray(amax, dtype=np.float32)
+    flat = [lib.oracle_e8m0_rceil(float(v)) for v in a.ravel()]
+    return np.array(flat, dtype=np.uint8).reshape(a.shape)
+
+
+SCALE_MODES = {"floor": 0, "rceil": 1}
+
+
 # ---------------------------------------------------------- quantization ops
 
 def quantize_jagged_rowwise(x: np.ndarray, offs, canary: int = 0):
@@ -160,21 +173,22 @@ def quantize_jagged_colwise(x: np.ndarray, offs, canary: int = 0):
     return q, s
 
 
-def quantize_mx_3d_colwise(w: np.ndarray):
+def quantize_mx_3d_colwise(w: np.ndarray, mode: str = "floor"):
     """w: (E, N, K) bf16 bits.  Returns q (E, N, K) uint8 and e8m0 scales
-    (E, N/32, K) uint8, both in logical index order."""
+    (E, N/32, K) uint8, both in logical index order.  mode: floor | rceil."""
     _check_bf16(w, 3)
     E, N, K = w.shape
     q = np.zeros((E, N, K), dtype=np.uint8)
     s = np.zeros((E, N // 32, K), dtype=np.uint8)
     sw = _estrides(w)
     _call(_load().oracle_quantize_mx_3d_colwise(_ptr(w), E, N, K, sw[0], sw[1], sw[2], _ptr(q),
-                                                N * K, K, 1, _ptr(s), (N // 32) * K, K, 1),
+                                                N * K, K, 1, _ptr(s), (N // 32) * K, K, 1,
+                                                SCALE_MODES[mode]),
           "mx_3d_colwise")
     return q, s
 
 
-def quantize_mx_rowwise(x: np.ndarray):
+def quantize_mx_rowwise(x: np.ndarray, mode: str = "floor"):
     """x: (rows, cols) bf16 bits, 1x32 blocks along dim 1.  Returns q (rows,
     cols) uint8 and e8m0 scales (rows, cols/32) uint8."""
     _check_bf16(x, 2)
@@ -183,7 +197,7 @@ def quantize_mx_rowwise(x: np.ndarray):
     s = np.zeros((rows, cols // 32), dtype=np.uint8)
     sx = _estrides(x)
     _call(_load().oracle_quantize_mx_rowwise(_ptr(x), rows, cols, sx[0], sx[1], _ptr(q), cols, 1,
-                                             _ptr(s), cols // 32, 1),
+                                             _ptr(s), cols // 32, 1, SCALE_MODES[mode]),
           "mx_rowwise")
     return q, s
 

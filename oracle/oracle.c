@@ -34,7 +34,8 @@
  *   - e8m0 scales ("floor" mode, OCP Microscaling Formats v1.0 shared-exponent
  *     rule with emax(E4M3) = 8): se = clamp(floor(log2(amax)) - 8, -127, 127),
  *     code = se + 127; amax = 0 gives code 0.  Each element becomes
- *     enc(sat(RN32(x * 2^-se))).
+ *     enc(sat(RN32(x * 2^-se))).  "rceil" mode (named by the 3D colwise
+ *     page, not defined there): the smallest se with amax <= 448 * 2^se.
  *
  * Arithmetic is done in double precision, where every product and quotient
  * below is either exact or rounded exactly once to binary32 by an explicit
@@ -171,6 +172,35 @@ uint8_t oracle_e8m0_floor(float amax)
     return (uint8_t)(se + 127);
 }
 
+/* e8m0 "rceil" code.  The pages name an rceil scale-calculation mode next to
+ * floor without defining it; the reading taken here: the scale is rounded UP
+ * to a power of two, i.e. se is the smallest integer with
+ * amax <= 448 * 2^se (so no element saturates), clamped to [-127, 127];
+ * amax = 0 gives the minimum code 0. */
+uint8_t oracle_e8m0_rceil(float amax)
+{
+    if (amax == 0.0f)
+        return 0;
+    double a = (double)amax;
+    int e;
+    frexp(a / 448.0, &e);            /* a/448 = m * 2^e, m in [0.5, 1) */
+    int se = e;                      /* candidate: 448 * 2^e >= a */
+    while (448.0 * ldexp(1.0, se - 1) >= a)
+        --se;
+    while (448.0 * ldexp(1.0, se) < a)
+        ++se;
+    if (se < -127)
+        se = -127;
+    if (se > 127)
+        se = 127;
+    return (uint8_t)(se + 127);
+}
+
+static uint8_t e8m0_code(float amax, int mode)
+{
+    return mode == 1 ? oracle_e8m0_rceil(amax) : oracle_e8m0_floor(amax);
+}
+
 /* quantize one bf16 element with an fp32 multiplier */
 static uint8_t quant_fp32(uint16_t xbits, float s)
 {
@@ -258,9 +288,9 @@ int oracle_quantize_jagged_colwise(const uint16_t *x, int64_t rows, int64_t cols
 int oracle_quantize_mx_3d_colwise(const uint16_t *w, int64_t E, int64_t N, int64_t K, int64_t sw_e,
                                   int64_t sw_n, int64_t sw_k, uint8_t *q, int64_t sq_e,
                                   int64_t sq_n, int64_t sq_k, uint8_t *scales, int64_t ss_e,
-                                  int64_t ss_nb, int64_t ss_k)
+                                  int64_t ss_nb, int64_t ss_k, int mode)
 {
-    if (E < 0 || N < 0 || K < 0 || N % 32 != 0)
+    if (E < 0 || N < 0 || K < 0 || N % 32 != 0 || (mode != 0 && mode != 1))
         return ORACLE_BAD_ARG;
     for (int64_t e = 0; e < E; ++e)
         for (int64_t nb = 0; nb < N / 32; ++nb)
@@ -271,7 +301,7 @@ int oracle_quantize_mx_3d_colwise(const uint16_t *w, int64_t E, int64_t N, int64
                     if (a > amax)
                         amax = a;
                 }
-                uint8_t code = oracle_e8m0_floor((float)amax);
+                uint8_t code = e8m0_code((float)amax, mode);
                 scales[e * ss_e + nb * ss_nb + k * ss_k] = code;
                 for (int64_t n = 32 * nb; n < 32 * nb + 32; ++n)
                     q[e * sq_e + n * sq_n + k * sq_k] =
@@ -284,9 +314,9 @@ int oracle_quantize_mx_3d_colwise(const uint16_t *w, int64_t E, int64_t N, int64
  * scales[r * ss_r + b * ss_b] is the e8m0 code of block (r, b). */
 int oracle_quantize_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t sx_r,
                                int64_t sx_c, uint8_t *q, int64_t sq_r, int64_t sq_c,
-                               uint8_t *scales, int64_t ss_r, int64_t ss_b)
+                               uint8_t *scales, int64_t ss_r, int64_t ss_b, int mode)
 {
-    if (rows < 0 || cols < 0 || cols % 32 != 0)
+    if (rows < 0 || cols < 0 || cols % 32 != 0 || (mode != 0 && mode != 1))
         return ORACLE_BAD_ARG;
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t b = 0; b < cols / 32; ++b) {
@@ -296,7 +326,7 @@ int oracle_quantize_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols, in
                 if (a > amax)
                     amax = a;
             }
-            uint8_t code = oracle_e8m0_floor((float)amax);
+            uint8_t code = e8m0_code((float)amax, mode);
             scales[r * ss_r + b * ss_b] = code;
             for (int64_t c = 32 * b; c < 32 * b + 32; ++c)
                 q[r * sq_r + c * sq_c] = quant_e8m0(x[r * sx_r + c * sx_c], code);

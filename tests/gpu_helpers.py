@@ -87,7 +87,10 @@ def jagged_colwise(x: torch.Tensor, offs: torch.Tensor, colmajor_out=True, strea
     return _gather_u8(q, (rows, cols), (1, ldq)), _gather_f32(s, (G, cols), (cols, 1))
 
 
-def mx_3d_colwise(w: torch.Tensor, stream=None, expect=0):
+SCALE_MODES = {"floor": 0, "rceil": 1}
+
+
+def mx_3d_colwise(w: torch.Tensor, stream=None, expect=0, mode="floor"):
     """Per-expert column-major q (E, N, K) strides (K*ldn, 1, ldn); scales
     (E, N/32, K) contiguous."""
     E, N, K = w.shape
@@ -96,21 +99,22 @@ def mx_3d_colwise(w: torch.Tensor, stream=None, expect=0):
     s = u8_canary(E * (N // 32) * K)
     code = mxq.mxq_quantize_mx_3d_colwise(w.data_ptr(), E, N, K, w.stride(0), w.stride(1),
                                           w.stride(2), q.data_ptr(), K * ldn, 1, ldn, s.data_ptr(),
-                                          (N // 32) * K, K, 1, 0, stream_handle(stream))
+                                          (N // 32) * K, K, 1, SCALE_MODES[mode],
+                                          stream_handle(stream))
     assert code == expect, code
     torch.cuda.synchronize()
     return (_gather_u8(q, (E, N, K), (K * ldn, 1, ldn)),
             _gather_u8(s, (E, N // 32, K), ((N // 32) * K, K, 1)))
 
 
-def mx_rowwise(x: torch.Tensor, stream=None, expect=0):
+def mx_rowwise(x: torch.Tensor, stream=None, expect=0, mode="floor"):
     rows, cols = x.shape
     ldq = round16(cols)
     q = u8_canary(rows * ldq)
     s = u8_canary(rows * (cols // 32))
     code = mxq.mxq_quantize_mx_rowwise(x.data_ptr(), rows, cols, x.stride(0), x.stride(1),
-                                       q.data_ptr(), ldq, 1, s.data_ptr(), cols // 32, 1, 0,
-                                       stream_handle(stream))
+                                       q.data_ptr(), ldq, 1, s.data_ptr(), cols // 32, 1,
+                                       SCALE_MODES[mode], stream_handle(stream))
     assert code == expect, code
     torch.cuda.synchronize()
     return _gather_u8(q, (rows, cols), (ldq, 1)), _gather_u8(s, (rows, cols // 32), (cols // 32, 1))

@@ -93,7 +93,8 @@ def test_jagged_rejects_bad_arguments(lib):
 def test_mx_and_blockwise_reject_bad_arguments(lib):
     mx3 = lib.mxq_quantize_mx_3d_colwise
     assert mx3(A, 2, 48, 64, 48 * 64, 64, 1, A, 48 * 64, 1, 48, A, 64, 64, 1, 0, None) == 1  # N % 32
-    assert mx3(A, 2, 64, 64, 64 * 64, 64, 1, A, 64 * 64, 1, 64, A, 128, 64, 1, 1, None) == 2  # rceil
+    assert mx3(A, 0, 64, 64, 64 * 64, 64, 1, A, 64 * 64, 1, 64, A, 128, 64, 1, 1, None) == 0  # rceil
+    assert mx3(A, 2, 64, 64, 64 * 64, 64, 1, A, 64 * 64, 1, 64, A, 128, 64, 1, -1, None) == 1  # mode
     assert mx3(A, 2, 64, 64, 64 * 64, 64, 1, A, 64 * 64, 1, 64, A, 128, 64, 1, 7, None) == 1  # mode
     assert mx3(A, 2, 64, 64, 64 * 64, 1, 64, A, 64 * 64, 1, 64, A, 128, 64, 1, 0, None) == 2  # layout
     assert mx3(A, 2, 64, 12, 64 * 12, 12, 1, A, 64 * 16, 1, 16, A, 24, 12, 1, 0, None) == 1  # K % 8
@@ -101,7 +102,8 @@ def test_mx_and_blockwise_reject_bad_arguments(lib):
     assert mx3(A, 0, 64, 64, 64 * 64, 64, 1, A, 64 * 64, 1, 64, A, 128, 64, 1, 0, None) == 0  # E = 0
     mxr = lib.mxq_quantize_mx_rowwise
     assert mxr(A, 4, 48, 48, 1, A, 48, 1, A, 1, 1, 0, None) == 1                        # cols % 32
-    assert mxr(A, 4, 64, 64, 1, A, 64, 1, A, 2, 1, 1, None) == 2                        # rceil
+    assert mxr(A, 0, 64, 64, 1, A, 64, 1, A, 2, 1, 1, None) == 0                        # rceil
+    assert mxr(A, 4, 64, 64, 1, A, 64, 1, A, 2, 1, 2, None) == 1                        # mode
     bw = lib.mxq_quantize_blockwise
     assert bw(A, 128, 256, 256, 1, 1, 64, A, 256, 1, A, 4, 1, None) == 2                # 1x64
     assert bw(A, 100, 256, 256, 1, 128, 128, A, 1, 112, A, 2, 1, None) == 1             # rows % 128

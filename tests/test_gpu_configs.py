@@ -82,13 +82,14 @@ def test_moe_bwd_colwise_x():
     _no_nan_codes(q)
 
 
-def test_mx3d_e8():
+@pytest.mark.parametrize("mode", ["floor", "rceil"])
+def test_mx3d_e8(mode):
     E, N, K = 8, 8192, 5120
     w = np.stack([workloads.mx3d_expert(e) for e in range(E)])
-    q, s = mx_3d_colwise(bf16_dev(w))
+    q, s = mx_3d_colwise(bf16_dev(w), mode=mode)
     ks = _sample(K, 24, 3)
     for e in (0, 3, 7):
-        oq, os_ = oracle.quantize_mx_3d_colwise(np.ascontiguousarray(w[e:e + 1][:, :, ks]))
+        oq, os_ = oracle.quantize_mx_3d_colwise(np.ascontiguousarray(w[e:e + 1][:, :, ks]), mode=mode)
         assert_same_bytes(q[e:e + 1][:, :, ks], oq, f"mx3d q expert {e} (sampled columns)")
         assert_same_bytes(s[e:e + 1][:, :, ks], os_, f"mx3d scales expert {e} (sampled columns)")
     _no_nan_codes(q)

@@ -152,36 +152,39 @@ def test_side_stream_and_determinism():
 
 # ---------------------------------------------------------------------- MX
 
+@pytest.mark.parametrize("mode", ["floor", "rceil"])
 @pytest.mark.parametrize("E,N,K,seed", [(1, 128, 256, 1), (3, 96, 200, 2), (2, 512, 1032, 3)])
-def test_mx_3d_colwise(E, N, K, seed):
+def test_mx_3d_colwise(E, N, K, seed, mode):
     w = np.stack([adversarial((N, K), 300 + seed * 10 + e) for e in range(E)])
     w[0, 0:32, 3] = 0                                           # zero block
     w[-1, 32:64, 5] = 0x8000                                    # negative zeros
     w[-1, N - 32:N, 7] = (np.arange(32, dtype=np.uint16) * 3) & 0x7F   # subnormal block
     w[0, 0:32, 9] = workloads.to_bf16_bits(
         np.random.default_rng(seed).standard_normal(32).astype(np.float32) * np.float32(2.0 ** 100))
-    q, s = mx_3d_colwise(bf16_dev(w))
-    oq, os_ = oracle.quantize_mx_3d_colwise(w)
+    q, s = mx_3d_colwise(bf16_dev(w), mode=mode)
+    oq, os_ = oracle.quantize_mx_3d_colwise(w, mode=mode)
     assert_same_bytes(q, oq, "mx 3d q")
     assert_same_bytes(s, os_, "mx 3d scales")
 
 
-def test_mx_3d_sweep_pattern_small():
+@pytest.mark.parametrize("mode", ["floor", "rceil"])
+def test_mx_3d_sweep_pattern_small(mode):
     w = np.stack([workloads.mx3d_sweep_expert(e, N=256, K=512) for e in range(2)])
-    q, s = mx_3d_colwise(bf16_dev(w))
-    oq, os_ = oracle.quantize_mx_3d_colwise(w)
+    q, s = mx_3d_colwise(bf16_dev(w), mode=mode)
+    oq, os_ = oracle.quantize_mx_3d_colwise(w, mode=mode)
     assert_same_bytes(q, oq, "mx 3d sweep q")
     assert_same_bytes(s, os_, "mx 3d sweep scales")
     assert (s == 0).sum() > 0
 
 
+@pytest.mark.parametrize("mode", ["floor", "rceil"])
 @pytest.mark.parametrize("rows,cols,seed", [(64, 256, 1), (5, 96, 2), (300, 4096, 3)])
-def test_mx_rowwise(rows, cols, seed):
+def test_mx_rowwise(rows, cols, seed, mode):
     x = adversarial((rows, cols), 400 + seed)
     x[0, :32] = 0
     x[-1, 32:64] = np.arange(32, dtype=np.uint16) + 1
-    q, s = mx_rowwise(bf16_dev(x))
-    oq, os_ = oracle.quantize_mx_rowwise(x)
+    q, s = mx_rowwise(bf16_dev(x), mode=mode)
+    oq, os_ = oracle.quantize_mx_rowwise(x, mode=mode)
     assert_same_bytes(q, oq, "mx rowwise q")
     assert_same_bytes(s, os_, "mx rowwise scales")
 
@@ -207,3 +210,20 @@ def test_no_nan_codes_anywhere():
     for br, bc in ((1, 128), (128, 128)):
         q, _ = blockwise(bf16_dev(x), br, bc)
         assert not np.any((q & 0x7F) == 0x7F)
+
+
+@pytest.mark.parametrize("mode", ["floor", "rceil"])
+def test_mx_every_bf16_amax(mode):
+    """One 32-element block per positive finite bf16 value v, holding v and
+    31 smaller values: every e8m0 code each mode can produce, with the
+    rceil threshold mantissas 96 / 97 and the clamp at code 0."""
+    v = np.arange(0x7F80, dtype=np.uint16)              # 0 .. largest finite
+    n = v.size
+    g = np.random.default_rng(5)
+    frac = g.integers(0, 0x7F80, size=(n, 31)).astype(np.uint16)
+    frac = np.minimum(frac, v[:, None]) | (g.integers(0, 2, size=(n, 31)).astype(np.uint16) << 15)
+    x = np.ascontiguousarray(np.concatenate([v[:, None], frac], axis=1).reshape(n // 32, 1024))
+    q, s = mx_rowwise(bf16_dev(x), mode=mode)
+    oq, os_ = oracle.quantize_mx_rowwise(x, mode=mode)
+    assert_same_bytes(q, oq, f"mx rowwise {mode} q (every amax)")
+    assert_same_bytes(s, os_, f"mx rowwise {mode} scales (every amax)")

@@ -7,7 +7,10 @@
 * exact rational arithmetic (``fractions.Fraction``) with a hand-written
   correct rounding to binary32, for the fp32 quantize multiplier;
 * the defining property of the MX "floor" shared exponent
-  (amax / 2^se in [256, 512)) and its bit-field form, for the e8m0 code.
+  (amax / 2^se in [256, 512)) and its bit-field form, for the e8m0 code;
+* the defining property of the "rceil" reading (amax / 2^se in (224, 448],
+  the smallest non-saturating power of two), its mantissa-threshold form and
+  closed forms at 448 * 2^k, for the rceil e8m0 code.
 """
 import math
 import os
@@ -206,3 +209,50 @@ def test_e8m0_matches_bit_field_form():
 def test_e8m0_power_of_two_closed_form():
     for k in range(-118, 128):
         assert oracle.e8m0_floor([np.float32(2.0 ** k)])[0] == k - 8 + 127
+
+
+# ------------------------------------------------------------ e8m0 rceil
+
+def test_e8m0_rceil_defining_property_all_bf16():
+    """se is the smallest integer with amax <= 448 * 2^se: checked with exact
+    rationals for every finite non-negative bf16 amax."""
+    bits = all_finite_bf16_bits()
+    bits = bits[bits < 0x8000]
+    amax = bits_to_f32(bits)
+    codes = oracle.e8m0_rceil(amax).astype(np.int64)
+    assert codes.min() == 0 and codes.max() == 247
+    for a, c in zip(amax.tolist(), codes.tolist()):
+        se = c - 127
+        if a == 0.0:
+            assert c == 0
+            continue
+        ratio = Fraction(a) / Fraction(2) ** se
+        assert ratio <= 448, (a, c)                  # never saturates
+        if c > 0:
+            assert ratio > 224, (a, c)               # se - 1 would saturate
+
+
+def test_e8m0_rceil_mantissa_threshold_form():
+    """448 = 1.75 * 2^8 and 1.75 is the 7-bit mantissa 96/128, so rceil
+    exceeds floor by one exactly when the bf16 mantissa field is above 96."""
+    bits = all_finite_bf16_bits()
+    bits = bits[bits < 0x8000]
+    amax = bits_to_f32(bits)
+    field = (bits.astype(np.int64) >> 7) & 0xFF
+    mant = bits.astype(np.int64) & 0x7F
+    expect = np.clip(field - 135 + (mant > 96), -127, 127) + 127
+    expect[amax == 0] = 0
+    assert np.array_equal(oracle.e8m0_rceil(amax).astype(np.int64), expect)
+    floor = oracle.e8m0_floor(amax).astype(np.int64)
+    rceil = oracle.e8m0_rceil(amax).astype(np.int64)
+    assert np.all((rceil - floor >= 0) & (rceil - floor <= 1))
+
+
+def test_e8m0_rceil_closed_forms():
+    for k in range(-126, 119):
+        exact = np.float32(448.0 * 2.0 ** k)          # 1.75 * 2^(k+8): a bf16 value
+        assert oracle.e8m0_rceil([exact])[0] == k + 127
+        above = np.nextafter(exact, np.float32(np.inf))
+        assert oracle.e8m0_rceil([above])[0] == k + 128
+        assert oracle.e8m0_rceil([np.float32(2.0 ** (k + 8))])[0] == k + 127
+    assert oracle.e8m0_rceil([np.float32(2.0 ** -149)])[0] == 0   # clamps at code 0

@@ -74,23 +74,34 @@ def _mx_exponent(amax: torch.Tensor) -> torch.Tensor:
     return se.clamp(-127, 127)
 
 
-def twin_mx_blocks(x_bits, block_axis_len, reshape_fn, unshape_fn):
+def _mx_exponent_rceil(amax: torch.Tensor) -> torch.Tensor:
+    """rceil reading: ceil(log2(amax / 448)), via frexp of the float64 quotient
+    (an exact power of two has mantissa 0.5 and is its own ceiling); the
+    quotient of a bf16 by 448 = 7 * 64 is never within a rounding error of a
+    power of two unless it equals one."""
+    m, e = torch.frexp(amax.double() / 448.0)
+    se = torch.where(m == 0.5, e.to(torch.int64) - 1, e.to(torch.int64))
+    se = torch.where(amax == 0, torch.full_like(se, -127), se)
+    return se.clamp(-127, 127)
+
+
+def twin_mx_blocks(x_bits, block_axis_len, reshape_fn, unshape_fn, mode="floor"):
     x = _f32(x_bits)
     xb = reshape_fn(x)                       # (..., 32) with the block on the last axis
     amax = xb.abs().amax(dim=-1)
-    se = _mx_exponent(amax)
+    se = _mx_exponent(amax) if mode == "floor" else _mx_exponent_rceil(amax)
     mult = torch.ldexp(torch.ones_like(amax, dtype=torch.float64), -se).to(torch.float32)
     q = _cast(xb * mult[..., None])
     return unshape_fn(q), (se + 127).to(torch.uint8).numpy()
 
 
-def twin_mx_rowwise(x_bits):
+def twin_mx_rowwise(x_bits, mode="floor"):
     rows, cols = x_bits.shape
     return twin_mx_blocks(x_bits, 32, lambda x: x.reshape(rows, cols // 32, 32),
-                          lambda q: q.reshape(rows, cols))
+                          lambda q: q.reshape(rows, cols), mode)
 
 
-def twin_mx_3d(w_bits):
+def twin_mx_3d(w_bits, mode="floor"):
     E, N, K = w_bits.shape
 
     def shape(w):
@@ -99,7 +110,7 @@ def twin_mx_3d(w_bits):
     def unshape(q):
         return np.ascontiguousarray(q.transpose(0, 1, 3, 2).reshape(E, N, K))
 
-    return twin_mx_blocks(w_bits, 32, shape, unshape)
+    return twin_mx_blocks(w_bits, 32, shape, unshape, mode)
 
 
 # ------------------------------------------------------------------ inputs
@@ -303,3 +314,38 @@ def test_mx_power_of_two_shift():
         q2, s2 = oracle.quantize_mx_rowwise(y)
         assert np.array_equal(q, q2)
         assert np.array_equal(s2.astype(int), s.astype(int) + k)
+
+
+def test_mx_rceil_matches_twin():
+    x = adversarial_bf16((64, 256), 32)
+    x[3, :32] = 0
+    x[4, 32:64] = np.arange(32, dtype=np.uint16) + 1
+    q, s = oracle.quantize_mx_rowwise(x, mode="rceil")
+    tq, ts = twin_mx_rowwise(x, mode="rceil")
+    assert np.array_equal(q, tq) and np.array_equal(s, ts)
+    w = np.stack([adversarial_bf16((96, 40), 51 + e) for e in range(2)])
+    w[0, 0:32, 3] = 0
+    q3, s3 = oracle.quantize_mx_3d_colwise(w, mode="rceil")
+    tq3, ts3 = twin_mx_3d(w, mode="rceil")
+    assert np.array_equal(q3, tq3) and np.array_equal(s3, ts3)
+
+
+def test_mx_rceil_never_saturates_and_top_code_in_upper_half():
+    """Under rceil every block's amax element lands in (224, 448] before the
+    cast (e4m3 codes 0x76..0x7E); no element is clipped; floor and rceil agree
+    on a block exactly when its amax mantissa is at most 1.75."""
+    x = workloads.mx3d_sweep_expert(1, N=256, K=64)
+    xr = np.ascontiguousarray(x.T)                       # (64, 256): 1x32 blocks along dim 1
+    q, s = oracle.quantize_mx_rowwise(xr, mode="rceil")
+    qf, sf = oracle.quantize_mx_rowwise(xr)
+    v = workloads.bf16_bits_to_f32(xr).astype(np.float64).reshape(64, 8, 32)
+    se = s.astype(np.int64) - 127
+    scaled = np.abs(v) * np.ldexp(1.0, -se)[..., None]   # exact in float64
+    assert np.all(scaled <= 448.0)
+    top = (q.reshape(64, 8, 32) & 0x7F).max(axis=2)
+    nz = np.abs(v).max(axis=2) > 0
+    assert np.all((top[nz] >= 0x76) & (top[nz] <= 0x7E))
+    mant = (xr.reshape(64, 8, 32) & 0x7FFF).max(axis=2) & 0x7F
+    same = s == sf
+    assert np.array_equal(same[nz], (mant <= 96)[nz])
+    assert np.array_equal(q.reshape(64, 8, 32)[same], qf.reshape(64, 8, 32)[same])
