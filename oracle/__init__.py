@@ -69,11 +69,15 @@ def _load():
                                                   ctypes.c_int]
     lib.oracle_quantize_mx_rowwise.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64,
                                                _vp, _i64, _i64, ctypes.c_int]
+    jmx = [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _i64, _i64, _vp, _i64, _i64, ctypes.c_int]
+    lib.oracle_quantize_jagged_mx_rowwise.argtypes = jmx
+    lib.oracle_quantize_jagged_mx_colwise.argtypes = jmx
     lib.oracle_quantize_blockwise.argtypes = [_vp, _i64, _i64, _i64, _i64, _i32, _i32, _vp,
                                               _i64, _i64, _vp, _i64, _i64]
     for name in ("oracle_quantize_jagged_rowwise", "oracle_quantize_jagged_colwise",
                  "oracle_quantize_mx_3d_colwise", "oracle_quantize_mx_rowwise",
-                 "oracle_quantize_blockwise"):
+                 "oracle_quantize_blockwise", "oracle_quantize_jagged_mx_rowwise",
+                 "oracle_quantize_jagged_mx_colwise"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -199,6 +203,51 @@ def quantize_mx_rowwise(x: np.ndarray, mode: str = "floor"):
     _call(_load().oracle_quantize_mx_rowwise(_ptr(x), rows, cols, sx[0], sx[1], _ptr(q), cols, 1,
                                              _ptr(s), cols // 32, 1, SCALE_MODES[mode]),
           "mx_rowwise")
+    return q, s
+
+
+def jagged_mx_scale_capacity(extent: int, G: int) -> int:
+    """Upper bound of sum_g ceil(n_g / 32) over any G groups covering at most
+    ``extent`` elements: ceil(extent / 32) + G - 1."""
+    return (extent + 31) // 32 + G - 1
+
+
+def quantize_jagged_mx_rowwise(x: np.ndarray, offs, mode: str = "floor", canary: int = 0):
+    """x: (rows, cols) bf16 bits, groups along dim 1, 1x32 blocks restarting
+    at each group start.  Returns q (rows, cols) and e8m0 scales (rows,
+    capacity) uint8; bytes and scale entries the op does not write keep
+    ``canary``."""
+    _check_bf16(x, 2)
+    offs = np.ascontiguousarray(np.asarray(offs, dtype=np.int32))
+    rows, cols = x.shape
+    G = offs.size
+    nb = jagged_mx_scale_capacity(cols, G)
+    q = np.full((rows, cols), canary, dtype=np.uint8)
+    s = np.full((rows, nb), canary, dtype=np.uint8)
+    sx = _estrides(x)
+    _call(_load().oracle_quantize_jagged_mx_rowwise(_ptr(x), rows, cols, sx[0], sx[1], _ptr(offs), G,
+                                                    _ptr(q), cols, 1, _ptr(s), nb, 1,
+                                                    SCALE_MODES[mode]),
+          "jagged_mx_rowwise")
+    return q, s
+
+
+def quantize_jagged_mx_colwise(x: np.ndarray, offs, mode: str = "floor", canary: int = 0):
+    """x: (rows, cols) bf16 bits, groups along dim 0, 32x1 blocks restarting
+    at each group start.  Returns q (rows, cols) and e8m0 scales (capacity,
+    cols) uint8; unwritten entries keep ``canary``."""
+    _check_bf16(x, 2)
+    offs = np.ascontiguousarray(np.asarray(offs, dtype=np.int32))
+    rows, cols = x.shape
+    G = offs.size
+    nb = jagged_mx_scale_capacity(rows, G)
+    q = np.full((rows, cols), canary, dtype=np.uint8)
+    s = np.full((nb, cols), canary, dtype=np.uint8)
+    sx = _estrides(x)
+    _call(_load().oracle_quantize_jagged_mx_colwise(_ptr(x), rows, cols, sx[0], sx[1], _ptr(offs), G,
+                                                    _ptr(q), cols, 1, _ptr(s), cols, 1,
+                                                    SCALE_MODES[mode]),
+          "jagged_mx_colwise")
     return q, s
 
 

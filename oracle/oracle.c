@@ -23,6 +23,12 @@
  *     Summary and the author's comment: 3D expert weights (E,N,K) scaled along
  *     N in 32-element blocks and written column-major per expert; the "floor"
  *     scale-calculation mode.
+ *   - "[mxfp8 moe training] add CUDA kernel for per-group conversion of scale
+ *     factors to blocked layout", stacked PR list: MX scales of token groups
+ *     along the GEMM's K dimension.  Jagged MX blocks restart at each group
+ *     start (reading: the pages fix no padding of groups to 32; a block never
+ *     spans two groups, a group's last block may be short, and scale entries
+ *     are numbered group after group).
  *
  * Numeric readings (the pages name the formats but print no formula):
  *   - fp8 is OCP E4M3FN: bias 7, 3 mantissa bits, no infinities, max 448,
@@ -331,6 +337,77 @@ int oracle_quantize_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols, in
             for (int64_t c = 32 * b; c < 32 * b + 32; ++c)
                 q[r * sq_r + c * sq_c] = quant_e8m0(x[r * sx_r + c * sx_c], code);
         }
+    return ORACLE_OK;
+}
+
+/* ----------------------------------------------------------- jagged MX */
+
+/* Jagged MXFP8: 32-element blocks that restart at every group start, so no
+ * block mixes two groups; a group of n elements has ceil(n / 32) blocks and
+ * its last block holds n mod 32 elements when that is not zero.  Blocks are
+ * numbered group after group: block k of group g has scale index B_g + k,
+ * B_g = sum over j < g of ceil(n_j / 32).  Scale entries past the last block
+ * are not written. */
+
+/* Rowwise: groups along dim 1; scales[r * ss_r + b * ss_b]. */
+int oracle_quantize_jagged_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols,
+                                      int64_t sx_r, int64_t sx_c, const int32_t *offs,
+                                      int32_t G, uint8_t *q, int64_t sq_r, int64_t sq_c,
+                                      uint8_t *scales, int64_t ss_r, int64_t ss_b, int mode)
+{
+    if (rows < 0 || cols < 0 || check_offs_args(G) != ORACLE_OK || (mode != 0 && mode != 1))
+        return ORACLE_BAD_ARG;
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t b = 0;   /* running block index */
+        for (int32_t g = 0; g < G; ++g) {
+            int64_t lo = g == 0 ? 0 : offs[g - 1];
+            int64_t hi = offs[g];
+            for (int64_t c0 = lo; c0 < hi; c0 += 32, ++b) {
+                int64_t c1 = c0 + 32 < hi ? c0 + 32 : hi;
+                double amax = 0.0;
+                for (int64_t c = c0; c < c1; ++c) {
+                    double a = bf16_abs(x[r * sx_r + c * sx_c]);
+                    if (a > amax)
+                        amax = a;
+                }
+                uint8_t code = e8m0_code((float)amax, mode);
+                scales[r * ss_r + b * ss_b] = code;
+                for (int64_t c = c0; c < c1; ++c)
+                    q[r * sq_r + c * sq_c] = quant_e8m0(x[r * sx_r + c * sx_c], code);
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Colwise: groups along dim 0; scales[b * ss_b + c * ss_c]. */
+int oracle_quantize_jagged_mx_colwise(const uint16_t *x, int64_t rows, int64_t cols,
+                                      int64_t sx_r, int64_t sx_c, const int32_t *offs,
+                                      int32_t G, uint8_t *q, int64_t sq_r, int64_t sq_c,
+                                      uint8_t *scales, int64_t ss_b, int64_t ss_c, int mode)
+{
+    if (rows < 0 || cols < 0 || check_offs_args(G) != ORACLE_OK || (mode != 0 && mode != 1))
+        return ORACLE_BAD_ARG;
+    for (int64_t c = 0; c < cols; ++c) {
+        int64_t b = 0;
+        for (int32_t g = 0; g < G; ++g) {
+            int64_t lo = g == 0 ? 0 : offs[g - 1];
+            int64_t hi = offs[g];
+            for (int64_t r0 = lo; r0 < hi; r0 += 32, ++b) {
+                int64_t r1 = r0 + 32 < hi ? r0 + 32 : hi;
+                double amax = 0.0;
+                for (int64_t r = r0; r < r1; ++r) {
+                    double a = bf16_abs(x[r * sx_r + c * sx_c]);
+                    if (a > amax)
+                        amax = a;
+                }
+                uint8_t code = e8m0_code((float)amax, mode);
+                scales[b * ss_b + c * ss_c] = code;
+                for (int64_t r = r0; r < r1; ++r)
+                    q[r * sq_r + c * sq_c] = quant_e8m0(x[r * sx_r + c * sx_c], code);
+            }
+        }
+    }
     return ORACLE_OK;
 }
 

@@ -101,6 +101,8 @@ def test_jagged_rowwise_empty_extent_writes_empty_group_scales():
     (9300, 24, 1, 1, 7, 20),       # ring: several passes, ragged ends
     (13000, 72, 2, 1, 0, 21),
     (2049, 40, 2, 1, 0, 22),
+    (3000, 64, 1, 1, 0, 23),       # one LDS tile, the last tile in registers
+    (6100, 136, 3, 1, 5, 24),
 ])
 def test_jagged_colwise_ragged(rows, cols, G, mult, tail, seed):
     bits = adversarial((rows, cols), 200 + seed)

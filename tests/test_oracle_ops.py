@@ -349,3 +349,92 @@ def test_mx_rceil_never_saturates_and_top_code_in_upper_half():
     same = s == sf
     assert np.array_equal(same[nz], (mant <= 96)[nz])
     assert np.array_equal(q.reshape(64, 8, 32)[same], qf.reshape(64, 8, 32)[same])
+
+
+# ---------------------------------------------------------------- jagged MX
+
+def twin_jagged_mx_rowwise(x_bits, offs, mode="floor", canary=0xA5):
+    """Each group's columns, zero-padded on the right to a multiple of 32 (a
+    zero changes no block amax), go through the MX twin above; the padding
+    is dropped again and the groups' scale columns are concatenated."""
+    rows, cols = x_bits.shape
+    G = len(offs)
+    nb = (cols + 31) // 32 + G - 1
+    q = np.full((rows, cols), canary, dtype=np.uint8)
+    s = np.full((rows, nb), canary, dtype=np.uint8)
+    lo, b = 0, 0
+    for hi in [int(v) for v in offs]:
+        n = hi - lo
+        if n > 0:
+            pad = -n % 32
+            seg = np.concatenate([x_bits[:, lo:hi], np.zeros((rows, pad), np.uint16)], axis=1)
+            tq, ts = twin_mx_rowwise(seg, mode)
+            q[:, lo:hi] = tq[:, :n]
+            s[:, b:b + ts.shape[1]] = ts
+            b += ts.shape[1]
+        lo = hi
+    return q, s
+
+
+@pytest.mark.parametrize("mode", ["floor", "rceil"])
+@pytest.mark.parametrize("G", [1, 2, 3])
+def test_jagged_mx_rowwise_all_compositions(G, mode):
+    extent = 70 if G < 3 else 40
+    x = adversarial_bf16((3, extent), 61 + G)
+    n = 0
+    for sizes in compositions(extent, G):
+        offs = np.cumsum(sizes).astype(np.int32)
+        q, s = oracle.quantize_jagged_mx_rowwise(x, offs, mode=mode, canary=0xA5)
+        tq, ts = twin_jagged_mx_rowwise(x, offs, mode)
+        assert np.array_equal(q, tq), sizes
+        assert np.array_equal(s, ts), sizes
+        n += 1
+    assert n == math.comb(extent + G - 1, G - 1)
+
+
+def test_jagged_mx_short_tail_and_empty_groups_keep_canary():
+    x = adversarial_bf16((4, 200), 71)
+    offs = np.array([0, 33, 33, 97, 150], dtype=np.int32)       # tail 150..199 in no group
+    q, s = oracle.quantize_jagged_mx_rowwise(x, offs, canary=0xA5)
+    tq, ts = twin_jagged_mx_rowwise(x, offs)
+    assert np.array_equal(q, tq) and np.array_equal(s, ts)
+    assert np.all(q[:, 150:] == 0xA5)
+    # blocks: 0 + 2 + 0 + 2 + 2 = 6 of a capacity of 7 + 5 - 1 = 11
+    assert np.all(s[:, 6:] == 0xA5) and np.all(s[:, :6] != 0xA5)
+
+
+@pytest.mark.parametrize("mode", ["floor", "rceil"])
+def test_jagged_mx_aligned_groups_equal_plain_mx(mode):
+    """With every group a multiple of 32 long, the blocks are the plain MX
+    blocks and the scale columns are the plain ones in order."""
+    x = adversarial_bf16((8, 512), 72)
+    offs = np.array([64, 64, 224, 480, 512], dtype=np.int32)
+    q, s = oracle.quantize_jagged_mx_rowwise(x, offs, mode=mode, canary=0xA5)
+    pq, ps = oracle.quantize_mx_rowwise(x, mode=mode)
+    assert np.array_equal(q, pq)
+    assert np.array_equal(s[:, :16], ps) and np.all(s[:, 16:] == 0xA5)
+
+
+@pytest.mark.parametrize("mode", ["floor", "rceil"])
+def test_jagged_mx_colwise_is_rowwise_of_transpose(mode):
+    x = adversarial_bf16((150, 6), 73)
+    offs = np.array([17, 17, 80, 149], dtype=np.int32)
+    q, s = oracle.quantize_jagged_mx_colwise(x, offs, mode=mode, canary=0xA5)
+    tq, ts = twin_jagged_mx_rowwise(np.ascontiguousarray(x.T), offs, mode)
+    assert np.array_equal(q, tq.T) and np.array_equal(s, ts.T)
+
+
+def test_jagged_mx_group_locality():
+    """Scaling one group by 2^k shifts only that group's scale codes by k and
+    leaves every q byte unchanged."""
+    x = workloads.normal_bf16((4, 160), 74)
+    offs = np.array([45, 100, 160], dtype=np.int32)
+    q, s = oracle.quantize_jagged_mx_rowwise(x, offs)
+    y = x.copy()
+    f = workloads.bf16_bits_to_f32(y[:, 45:100]) * np.float32(2.0 ** 7)
+    y[:, 45:100] = workloads.to_bf16_bits(f)
+    q2, s2 = oracle.quantize_jagged_mx_rowwise(y, offs)
+    assert np.array_equal(q, q2)
+    d = s2.astype(int) - s.astype(int)
+    # group 0: blocks 0-1, group 1: blocks 2-3, group 2: blocks 4-5
+    assert np.all(d[:, 2:4] == 7) and np.all(d[:, [0, 1, 4, 5]] == 0)
