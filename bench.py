@@ -5,7 +5,8 @@ Default workload (``moe_bwd``): the MoE backward grad_weight operands — jagged
 rowwise quantization of grad_out^T (4096, 16384) plus jagged colwise
 quantization of x (16384, 4096), the same 8 token groups for both, bf16 in,
 e4m3 + fp32 per-group scales out.  One step = both launches.  Other
-workloads (``--workload``): ``mx3d`` (E=8 expert weights, 32x1 MXFP8),
+workloads (``--workload``): ``moe_bwd_mx`` (the same operands as jagged
+MXFP8 blocks), ``mx3d`` (E=8 expert weights, 32x1 MXFP8),
 ``mx3d_e{1,2,4,16,64}``, ``mx3d_rceil`` (E=8 with the rceil scale mode),
 ``blockwise`` (1x128 activations + 128x128 weights).
 
@@ -116,6 +117,55 @@ def build_moe_bwd(torch, mxq, workloads):
     return [l1, l2], keep, desc, cpu_sample
 
 
+def build_moe_bwd_mx(torch, mxq, workloads):
+    """The MX variant of the MoE backward grad_weight operands: jagged MXFP8
+    (32-element blocks restarting at each token-group start, e8m0 floor
+    scales) of grad_out^T rowwise and x colwise, the same 8 groups."""
+    import numpy as np
+
+    go_t = workloads.moe_grad_out_t()
+    x = workloads.moe_x()
+    offs = workloads.moe_offsets()
+    G = offs.size
+    d_go, d_x = bf16_dev(torch, go_t), bf16_dev(torch, x)
+    d_offs = torch.from_numpy(offs).cuda()
+    R1, C1 = go_t.shape
+    R2, C2 = x.shape
+    nb1 = mxq.jagged_mx_scale_capacity(C1, G)
+    nb2 = mxq.jagged_mx_scale_capacity(R2, G)
+    sizes = np.diff(np.concatenate([[0], offs]))
+    nb = int(sum((int(n) + 31) // 32 for n in sizes))          # blocks actually written
+    q1 = torch.empty(R1 * C1, dtype=torch.uint8, device="cuda")
+    s1 = torch.empty(R1 * nb1, dtype=torch.uint8, device="cuda")
+    q2 = torch.empty(R2 * C2, dtype=torch.uint8, device="cuda")
+    s2 = torch.empty(nb2 * C2, dtype=torch.uint8, device="cuda")
+    keep = [d_go, d_x, d_offs, q1, s1, q2, s2]
+    l1 = Launch("jagged_mx_rowwise grad_out^T (4096,16384)", "jagged_mx_rowwise_kernel",
+                mxq.mxq_quantize_jagged_mx_rowwise,
+                (d_go.data_ptr(), R1, C1, C1, 1, d_offs.data_ptr(), G, q1.data_ptr(), C1, 1,
+                 s1.data_ptr(), nb1, 1, 0), 3 * R1 * C1 + R1 * nb, R1 * C1)
+    l2 = Launch("jagged_mx_colwise x (16384,4096)", "jagged_mx_colwise_kernel",
+                mxq.mxq_quantize_jagged_mx_colwise,
+                (d_x.data_ptr(), R2, C2, C2, 1, d_offs.data_ptr(), G, q2.data_ptr(), 1, R2,
+                 s2.data_ptr(), C2, 1, 0), 3 * R2 * C2 + nb * C2, R2 * C2)
+    desc = {"workload": "moe_bwd_jagged_mx",
+            "tensors": "grad_out^T bf16 (4096,16384) 1x32 blocks per group -> row-major e4m3; "
+                       "x bf16 (16384,4096) 32x1 blocks per group -> column-major e4m3",
+            "groups": int(G), "group_sizes": [int(v) for v in sizes],
+            "scales": f"e8m0 floor, {nb} blocks per row / column"}
+
+    def cpu_sample(oracle, n):
+        t0 = time.perf_counter()
+        oracle.quantize_jagged_mx_rowwise(go_t[:n], offs)
+        oracle.quantize_jagged_mx_colwise(np.ascontiguousarray(x[:, :n]), offs)
+        dt = time.perf_counter() - t0
+        nbytes = 3 * n * C1 + n * nb + 3 * R2 * n + nb * n
+        return dt, nbytes, (f"jagged MX rowwise on {n} of 4096 rows of grad_out^T and jagged MX "
+                            f"colwise on {n} of 4096 columns of x")
+
+    return [l1, l2], keep, desc, cpu_sample
+
+
 def build_mx3d(torch, mxq, workloads, E, sweep, rceil=False):
     import numpy as np
 
@@ -203,6 +253,8 @@ def build(name, torch, mxq, workloads):
         return build_copy(torch)
     if name == "moe_bwd":
         return build_moe_bwd(torch, mxq, workloads)
+    if name == "moe_bwd_mx":
+        return build_moe_bwd_mx(torch, mxq, workloads)
     if name == "mx3d":
         return build_mx3d(torch, mxq, workloads, 8, sweep=False)
     if name == "mx3d_rceil":
@@ -299,7 +351,8 @@ def main():
     if not args.no_cpu_baseline and cpu_sample is not None:
         import oracle
 
-        n = args.cpu_sample_rows or {"moe_bwd": 4096, "blockwise": 2048}.get(args.workload, 256)
+        n = args.cpu_sample_rows or {"moe_bwd": 4096, "moe_bwd_mx": 2048,
+                                     "blockwise": 2048}.get(args.workload, 256)
         print(f"[bench] timing the CPU oracle on a sample (n={n})", file=sys.stderr, flush=True)
         dt, nbytes, what = cpu_sample(oracle, n)
         cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",

@@ -158,6 +158,44 @@ mxq_status mxq_quantize_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols
                                    int32_t scale_mode, void *stream);
 
 /*
+ * Jagged MXFP8: e8m0 block scales with 32-element blocks inside token
+ * groups, for MX grouped GEMMs whose groups run along K.  Source: "[mxfp8
+ * moe training] add CUDA kernel for per-group conversion of scale factors to
+ * blocked layout", stacked PR list (scales of token groups along K); the
+ * blocks and scale rules are those of mxq_quantize_mx_rowwise.  Reading (the
+ * pages do not pad groups): blocks restart at every group start, a group of
+ * n elements has ceil(n/32) blocks and its last block may be short; block k
+ * of group g has scale index B_g + k, B_g = sum over j < g of ceil(n_j/32).
+ *
+ * Groups as in mxq_quantize_jagged_rowwise (rowwise: along dim 1) and
+ * mxq_quantize_jagged_colwise (colwise: along dim 0).  Elements at or past
+ * offs[G-1] and scale entries past the last block are not written.
+ *
+ * rowwise: scales[r*ss_r + b*ss_b], b < ceil(cols/32) + G - 1 (the most any
+ *          offsets can need; the caller's buffer must hold that many).
+ *          Layouts with a kernel: sx_c == 1 && sq_c == 1 (row-major in and
+ *          out; sx_r % 8 == 0, sq_r % 16 == 0), or sx_r == 1 && sq_c == 1
+ *          (a transposed view; rows % 8 == 0, sx_c % 8 == 0, sq_r % 16 == 0).
+ * colwise: scales[b*ss_b + c*ss_c], b < ceil(rows/32) + G - 1.
+ *          Layouts with a kernel: sx_c == 1 && sq_r == 1 (row-major in,
+ *          column-major out; cols % 8 == 0, sx_r % 8 == 0, sq_c % 16 == 0),
+ *          or sx_r == 1 && sq_r == 1 (column-major in and out).
+ * The 16-byte fast paths need group starts on multiples of 8 (rowwise) or
+ * 16 (colwise); other offsets take element-wise loads or stores.
+ * scale_mode: MXQ_SCALE_FLOOR or MXQ_SCALE_RCEIL.
+ */
+mxq_status mxq_quantize_jagged_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols,
+                                          int64_t sx_r, int64_t sx_c, const int32_t *offs,
+                                          int32_t num_groups, uint8_t *q, int64_t sq_r,
+                                          int64_t sq_c, uint8_t *scales, int64_t ss_r,
+                                          int64_t ss_b, int32_t scale_mode, void *stream);
+mxq_status mxq_quantize_jagged_mx_colwise(const uint16_t *x, int64_t rows, int64_t cols,
+                                          int64_t sx_r, int64_t sx_c, const int32_t *offs,
+                                          int32_t num_groups, uint8_t *q, int64_t sq_r,
+                                          int64_t sq_c, uint8_t *scales, int64_t ss_b,
+                                          int64_t ss_c, int32_t scale_mode, void *stream);
+
+/*
  * Blockwise ("groupwise") fp8 quantization with one fp32 multiplier per
  * block_r x block_c block.  Source: "[fp8 blockwise] load 2d chunks for
  * groupwise quant to enable coalesced gmem accesses", body: 1 x blocksize

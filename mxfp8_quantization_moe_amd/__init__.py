@@ -18,14 +18,17 @@ from . import _capi
 from ._capi import (MXQ_ERR_INVALID_ARG, MXQ_ERR_LAUNCH, MXQ_ERR_UNSUPPORTED, MXQ_MAX_GROUPS,
                     MXQ_OK, MXQ_SCALE_FLOOR, MXQ_SCALE_RCEIL, LibraryMissing,
                     mxq_abi_version, mxq_debug_cast_e4m3, mxq_quantize_blockwise,
-                    mxq_quantize_jagged_colwise, mxq_quantize_jagged_rowwise,
+                    mxq_quantize_jagged_colwise, mxq_quantize_jagged_mx_colwise,
+                    mxq_quantize_jagged_mx_rowwise, mxq_quantize_jagged_rowwise,
                     mxq_quantize_mx_3d_colwise, mxq_quantize_mx_rowwise)
 
 __all__ = [
     "quantize_jagged_rowwise", "quantize_jagged_colwise", "quantize_mx_3d_colwise",
-    "quantize_mx_rowwise", "quantize_blockwise", "debug_cast_e4m3", "MXQError",
+    "quantize_mx_rowwise", "quantize_jagged_mx_rowwise", "quantize_jagged_mx_colwise",
+    "jagged_mx_scale_capacity", "quantize_blockwise", "debug_cast_e4m3", "MXQError",
     "mxq_quantize_jagged_rowwise", "mxq_quantize_jagged_colwise", "mxq_quantize_mx_3d_colwise",
-    "mxq_quantize_mx_rowwise", "mxq_quantize_blockwise", "mxq_debug_cast_e4m3",
+    "mxq_quantize_mx_rowwise", "mxq_quantize_jagged_mx_rowwise", "mxq_quantize_jagged_mx_colwise",
+    "mxq_quantize_blockwise", "mxq_debug_cast_e4m3",
     "mxq_abi_version", "LibraryMissing",
 ]
 
@@ -147,6 +150,50 @@ def quantize_mx_rowwise(x, *, scale_mode: int = MXQ_SCALE_FLOOR, stream=None):
         x.data_ptr(), rows, cols, x.stride(0), x.stride(1), q.data_ptr(), q.stride(0), q.stride(1),
         s.data_ptr(), s.stride(0), s.stride(1), scale_mode, _stream(x, stream))
     _check(code, "mxq_quantize_mx_rowwise")
+    return q, s
+
+
+def jagged_mx_scale_capacity(extent: int, num_groups: int) -> int:
+    """Scale entries a jagged MX call may write along the grouped dim:
+    ceil(extent/32) + num_groups - 1, the most that any offsets need."""
+    return (extent + 31) // 32 + num_groups - 1
+
+
+def quantize_jagged_mx_rowwise(x, offs, *, scale_mode: int = MXQ_SCALE_FLOOR, stream=None):
+    """MXFP8 with 1x32 blocks restarting at each group start, groups along
+    dim 1.  Returns ``(q, scales)``: q (rows, cols) row-major e4m3, scales
+    (rows, capacity) e8m0 uint8 where the first sum_g ceil(n_g/32) columns
+    are written."""
+    torch = _torch()
+    _require_bf16_cuda(x, 2, "x")
+    rows, cols = x.shape
+    G = offs.numel()
+    q = _empty_rowmajor_u8(torch, rows, cols, x.device)
+    s = torch.empty((rows, jagged_mx_scale_capacity(cols, G)), dtype=torch.uint8, device=x.device)
+    code = mxq_quantize_jagged_mx_rowwise(
+        x.data_ptr(), rows, cols, x.stride(0), x.stride(1), offs.data_ptr(), G, q.data_ptr(),
+        q.stride(0), q.stride(1), s.data_ptr(), s.stride(0), s.stride(1), scale_mode,
+        _stream(x, stream))
+    _check(code, "mxq_quantize_jagged_mx_rowwise")
+    return q, s
+
+
+def quantize_jagged_mx_colwise(x, offs, *, scale_mode: int = MXQ_SCALE_FLOOR, stream=None):
+    """MXFP8 with 32x1 blocks restarting at each group start, groups along
+    dim 0.  Returns ``(q, scales)``: q (rows, cols) column-major e4m3, scales
+    (capacity, cols) e8m0 uint8 where the first sum_g ceil(n_g/32) rows are
+    written."""
+    torch = _torch()
+    _require_bf16_cuda(x, 2, "x")
+    rows, cols = x.shape
+    G = offs.numel()
+    q = _empty_colmajor_u8(torch, rows, cols, x.device)
+    s = torch.empty((jagged_mx_scale_capacity(rows, G), cols), dtype=torch.uint8, device=x.device)
+    code = mxq_quantize_jagged_mx_colwise(
+        x.data_ptr(), rows, cols, x.stride(0), x.stride(1), offs.data_ptr(), G, q.data_ptr(),
+        q.stride(0), q.stride(1), s.data_ptr(), s.stride(0), s.stride(1), scale_mode,
+        _stream(x, stream))
+    _check(code, "mxq_quantize_jagged_mx_colwise")
     return q, s
 
 

@@ -39,6 +39,10 @@ SIGNATURES = {
                                    _vp, _i64, _i64, _i64, _i32, _vp],
     "mxq_quantize_mx_rowwise": [_vp, _i64, _i64, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64,
                                 _i32, _vp],
+    "mxq_quantize_jagged_mx_rowwise": [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _i64, _i64,
+                                       _vp, _i64, _i64, _i32, _vp],
+    "mxq_quantize_jagged_mx_colwise": [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _i64, _i64,
+                                       _vp, _i64, _i64, _i32, _vp],
     "mxq_quantize_blockwise": [_vp, _i64, _i64, _i64, _i64, _i32, _i32, _vp, _i64, _i64, _vp,
                                _i64, _i64, _vp],
     "mxq_debug_cast_e4m3": [_vp, _i64, _vp, _vp],
@@ -88,5 +92,7 @@ mxq_quantize_jagged_rowwise = _fwd("mxq_quantize_jagged_rowwise")
 mxq_quantize_jagged_colwise = _fwd("mxq_quantize_jagged_colwise")
 mxq_quantize_mx_3d_colwise = _fwd("mxq_quantize_mx_3d_colwise")
 mxq_quantize_mx_rowwise = _fwd("mxq_quantize_mx_rowwise")
+mxq_quantize_jagged_mx_rowwise = _fwd("mxq_quantize_jagged_mx_rowwise")
+mxq_quantize_jagged_mx_colwise = _fwd("mxq_quantize_jagged_mx_colwise")
 mxq_quantize_blockwise = _fwd("mxq_quantize_blockwise")
 mxq_debug_cast_e4m3 = _fwd("mxq_debug_cast_e4m3")

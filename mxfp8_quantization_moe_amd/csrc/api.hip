@@ -8,6 +8,7 @@
 #include "mxq.h"
 #include "block_kernels.hpp"
 #include "jagged_kernels.hpp"
+#include "jagged_mx_kernels.hpp"
 
 namespace {
 
@@ -117,6 +118,57 @@ mxq_status check_jagged_common(const uint16_t *x, int64_t rows, int64_t cols, co
     if ((reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
         return MXQ_ERR_INVALID_ARG;
     return MXQ_OK;
+}
+
+mxq_status check_jagged_mx(const uint16_t *x, int64_t rows, int64_t cols, const int32_t *offs,
+                           int32_t G, const uint8_t *q, const uint8_t *scales, int32_t scale_mode)
+{
+    if (rows < 0 || cols < 0 || G < 1 || G > MXQ_MAX_GROUPS)
+        return MXQ_ERR_INVALID_ARG;
+    if (rows > INT32_MAX || cols > INT32_MAX)
+        return MXQ_ERR_INVALID_ARG;
+    if (scale_mode != MXQ_SCALE_FLOOR && scale_mode != MXQ_SCALE_RCEIL)
+        return MXQ_ERR_INVALID_ARG;
+    if (!offs)
+        return MXQ_ERR_INVALID_ARG;
+    if ((rows > 0 && cols > 0) && (!x || !q || !scales))
+        return MXQ_ERR_INVALID_ARG;
+    if ((x && !aligned16(x)) || (q && !aligned16(q)))
+        return MXQ_ERR_INVALID_ARG;
+    return MXQ_OK;
+}
+
+// blocks along the unit-stride dim of a row-major (rows, cols) tensor
+mxq_status run_jagged_mx_rows(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
+                              const int32_t *offs, int G, uint8_t *q, int64_t ldq,
+                              uint8_t *scales, int64_t ss_r, int64_t ss_b, bool rceil,
+                              hipStream_t st)
+{
+    constexpr int RW = 16;
+    const int64_t nbmax = (cols + 31) / 32 + G - 1;
+    const int64_t nbt = (nbmax + 63) / 64;
+    const int64_t nrt = (rows + RW - 1) / RW;
+    if (nbt * nrt > INT32_MAX)
+        return MXQ_ERR_INVALID_ARG;
+    jagged_mx_rowwise_kernel<RW><<<dim3((unsigned)(nbt * nrt)), dim3(kJmxThreads), 0, st>>>(
+        x, ldx, (int)rows, (int)cols, offs, G, q, ldq, scales, ss_r, ss_b, (int)nbt, rceil ? 1 : 0);
+    return launch_status();
+}
+
+// blocks across the rows of a row-major (rows, cols) tensor, q column-major
+mxq_status run_jagged_mx_cols(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
+                              const int32_t *offs, int G, uint8_t *q, int64_t ldq,
+                              uint8_t *scales, int64_t ss_b, int64_t ss_c, bool rceil,
+                              hipStream_t st)
+{
+    const int64_t ntr = (rows + 127) / 128 + G - 1;
+    const int64_t tiles_c = (cols + 255) / 256;
+    if (ntr * tiles_c > INT32_MAX)
+        return MXQ_ERR_INVALID_ARG;
+    jagged_mx_colwise_kernel<<<dim3((unsigned)(ntr * tiles_c)), dim3(kJmxThreads), 0, st>>>(
+        x, ldx, (int)rows, (int)cols, offs, G, q, ldq, scales, ss_b, ss_c, (int)tiles_c,
+        rceil ? 1 : 0);
+    return launch_status();
 }
 
 }  // namespace
@@ -246,6 +298,65 @@ mxq_status mxq_quantize_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols
                                             reinterpret_cast<hipStream_t>(stream)>>>(
         x, sx_r, nbpr, nblocks, q, sq_r, scales, ss_r, ss_b, scale_mode == MXQ_SCALE_RCEIL);
     return launch_status();
+}
+
+mxq_status mxq_quantize_jagged_mx_rowwise(const uint16_t *x, int64_t rows, int64_t cols,
+                                          int64_t sx_r, int64_t sx_c, const int32_t *offs,
+                                          int32_t num_groups, uint8_t *q, int64_t sq_r,
+                                          int64_t sq_c, uint8_t *scales, int64_t ss_r,
+                                          int64_t ss_b, int32_t scale_mode, void *stream)
+{
+    mxq_status s = check_jagged_mx(x, rows, cols, offs, num_groups, q, scales, scale_mode);
+    if (s != MXQ_OK)
+        return s;
+    if (rows == 0 || cols == 0)
+        return MXQ_OK;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const bool rc = scale_mode == MXQ_SCALE_RCEIL;
+    if (sx_c == 1 && sq_c == 1) {
+        if (rows > 1 && (sx_r % 8 != 0 || sq_r % 16 != 0))
+            return MXQ_ERR_INVALID_ARG;
+        return run_jagged_mx_rows(x, rows, cols, sx_r, offs, num_groups, q, sq_r, scales, ss_r,
+                                  ss_b, rc, st);
+    }
+    if (sx_r == 1 && sq_c == 1) {
+        // a transposed view of a row-major (cols, rows) tensor: its blocks run
+        // across that tensor's rows, and its column-major q is this row-major q
+        if (rows % 8 != 0 || sx_c % 8 != 0 || sq_r % 16 != 0)
+            return MXQ_ERR_INVALID_ARG;
+        return run_jagged_mx_cols(x, cols, rows, sx_c, offs, num_groups, q, sq_r, scales, ss_b,
+                                  ss_r, rc, st);
+    }
+    return MXQ_ERR_UNSUPPORTED;
+}
+
+mxq_status mxq_quantize_jagged_mx_colwise(const uint16_t *x, int64_t rows, int64_t cols,
+                                          int64_t sx_r, int64_t sx_c, const int32_t *offs,
+                                          int32_t num_groups, uint8_t *q, int64_t sq_r,
+                                          int64_t sq_c, uint8_t *scales, int64_t ss_b,
+                                          int64_t ss_c, int32_t scale_mode, void *stream)
+{
+    mxq_status s = check_jagged_mx(x, rows, cols, offs, num_groups, q, scales, scale_mode);
+    if (s != MXQ_OK)
+        return s;
+    if (rows == 0 || cols == 0)
+        return MXQ_OK;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const bool rc = scale_mode == MXQ_SCALE_RCEIL;
+    if (sx_c == 1 && sq_r == 1) {
+        if (cols % 8 != 0 || sx_r % 8 != 0 || sq_c % 16 != 0)
+            return MXQ_ERR_INVALID_ARG;
+        return run_jagged_mx_cols(x, rows, cols, sx_r, offs, num_groups, q, sq_c, scales, ss_b,
+                                  ss_c, rc, st);
+    }
+    if (sx_r == 1 && sq_r == 1) {
+        // column-major in and out: the rowwise pattern on the transpose
+        if (cols > 1 && (sx_c % 8 != 0 || sq_c % 16 != 0))
+            return MXQ_ERR_INVALID_ARG;
+        return run_jagged_mx_rows(x, cols, rows, sx_c, offs, num_groups, q, sq_c, scales, ss_c,
+                                  ss_b, rc, st);
+    }
+    return MXQ_ERR_UNSUPPORTED;
 }
 
 mxq_status mxq_quantize_blockwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t sx_r,

@@ -8,6 +8,7 @@ import numpy as np
 import torch
 
 import mxfp8_quantization_moe_amd as mxq
+import workloads
 
 CANARY = 0xA5
 DEV = torch.device("cuda:0")
@@ -151,3 +152,65 @@ def assert_same_bytes(got: np.ndarray, want: np.ndarray, what: str) -> None:
     head = ", ".join(f"{tuple(int(i) for i in b)}: got {got[tuple(b)]:#x} want {want[tuple(b)]:#x}"
                      for b in bad[:10])
     raise AssertionError(f"{what}: {len(bad)} mismatches; first: {head}")
+
+
+def jagged_mx_rowwise(x: torch.Tensor, offs: torch.Tensor, mode="floor", stream=None, expect=0):
+    """Row-major q (row stride padded to 16 bytes), scales (rows, capacity)."""
+    rows, cols = x.shape
+    G = offs.numel()
+    nb = mxq.jagged_mx_scale_capacity(cols, G)
+    ldq = round16(max(cols, 1))
+    q = u8_canary(rows * ldq)
+    s = u8_canary(rows * nb)
+    code = mxq.mxq_quantize_jagged_mx_rowwise(x.data_ptr(), rows, cols, x.stride(0), x.stride(1),
+                                              offs.data_ptr(), G, q.data_ptr(), ldq, 1,
+                                              s.data_ptr(), nb, 1, SCALE_MODES[mode],
+                                              stream_handle(stream))
+    assert code == expect, code
+    torch.cuda.synchronize()
+    return _gather_u8(q, (rows, cols), (ldq, 1)), _gather_u8(s, (rows, nb), (nb, 1))
+
+
+def jagged_mx_colwise(x: torch.Tensor, offs: torch.Tensor, mode="floor", stream=None, expect=0):
+    """Column-major q (column stride padded), scales (capacity, cols)."""
+    rows, cols = x.shape
+    G = offs.numel()
+    nb = mxq.jagged_mx_scale_capacity(rows, G)
+    ldq = round16(max(rows, 1))
+    q = u8_canary(cols * ldq)
+    s = u8_canary(nb * cols)
+    code = mxq.mxq_quantize_jagged_mx_colwise(x.data_ptr(), rows, cols, x.stride(0), x.stride(1),
+                                              offs.data_ptr(), G, q.data_ptr(), 1, ldq,
+                                              s.data_ptr(), cols, 1, SCALE_MODES[mode],
+                                              stream_handle(stream))
+    assert code == expect, code
+    torch.cuda.synchronize()
+    return _gather_u8(q, (rows, cols), (1, ldq)), _gather_u8(s, (nb, cols), (cols, 1))
+
+
+def adversarial(shape, seed):
+    """N(0,1) bf16 with 1/16 of the entries replaced by signed zeros,
+    subnormals, the largest finite values, exact powers of two and values
+    that land on e4m3 rounding ties."""
+    g = np.random.default_rng(seed)
+    bits = workloads.normal_bf16(shape, seed)
+    flat = bits.reshape(-1)
+    pick = g.choice(flat.size, size=max(1, flat.size // 16), replace=False)
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x7F7F, 0xFF7F,
+                         0x3F80, 0xBF80, 0x43E0, 0x3C00], dtype=np.uint16)
+    flat[pick] = specials[g.integers(specials.size, size=pick.size)]
+    return bits
+
+
+def random_offsets(extent, G, seed, multiple=1, empties=1, short_tail=0):
+    """Sorted random group ends on multiples of ``multiple``, with ``empties``
+    forced empty groups and the last ``short_tail`` elements in no group."""
+    g = np.random.default_rng(seed)
+    cuts = np.sort(g.integers(0, (extent - short_tail) // multiple + 1, size=G - 1)) * multiple
+    offs = np.concatenate([cuts, [extent - short_tail]]).astype(np.int64)
+    for _ in range(empties):
+        j = int(g.integers(1, G)) if G > 1 else 0
+        if j > 0:
+            offs[j] = offs[j - 1]
+    offs = np.maximum.accumulate(offs)
+    return offs.astype(np.int32)

@@ -110,3 +110,30 @@ def test_mx_and_blockwise_reject_bad_arguments(lib):
     assert bw(A, 128, 256, 256, 1, 1, 128, A, 1, 128, A, 2, 1, None) == 2               # 1x128 col-major
     assert bw(A, 128, 256, 256, 1, 128, 128, A, 256, 1, A, 2, 1, None) == 2             # 128x128 row-major
     assert bw(A, 0, 256, 256, 1, 128, 128, A, 1, 16, A, 2, 1, None) == 0                # empty
+
+
+def test_jagged_mx_rejects_bad_arguments(lib):
+    rw = lib.mxq_quantize_jagged_mx_rowwise
+    cw = lib.mxq_quantize_jagged_mx_colwise
+    ok_args = dict(x=A, rows=4, cols=64, sx_r=64, sx_c=1, offs=A, G=2, q=A, sq_r=64, sq_c=1, s=A,
+                   ss0=3, ss1=1, mode=0)
+
+    def call(fn, **kw):
+        a = dict(ok_args, **kw)
+        return fn(a["x"], a["rows"], a["cols"], a["sx_r"], a["sx_c"], a["offs"], a["G"], a["q"],
+                  a["sq_r"], a["sq_c"], a["s"], a["ss0"], a["ss1"], a["mode"], None)
+
+    assert call(rw, G=0) == 1
+    assert call(rw, G=4097) == 1
+    assert call(rw, mode=2) == 1
+    assert call(rw, offs=0) == 1
+    assert call(rw, s=0) == 1
+    assert call(rw, q=MIS) == 1
+    assert call(rw, sx_r=60) == 1                  # row pitch not a multiple of 8
+    assert call(rw, sx_r=1, sx_c=3) == 1           # transposed view, misaligned pitch
+    assert call(rw, sx_r=1, sx_c=64, rows=6) == 1  # transposed view needs rows % 8 == 0
+    assert call(rw, sq_r=1, sq_c=4) == 2           # column-major out: no kernel
+    assert call(rw, cols=0) == 0 and call(rw, rows=0, mode=1) == 0
+    assert call(cw, sq_r=1, sq_c=16, cols=12, sx_r=16) == 1   # cols % 8
+    assert call(cw, sq_r=64, sq_c=1) == 2          # row-major out from row-major in: no kernel
+    assert call(cw, rows=0, sq_r=1, sq_c=16) == 0

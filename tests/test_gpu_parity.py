@@ -10,33 +10,10 @@ import torch
 
 import oracle
 import workloads
-from gpu_helpers import (CANARY, assert_same_bytes, bf16_dev, blockwise, i32_dev, jagged_colwise,
-                         jagged_rowwise, mx_3d_colwise, mx_rowwise)
+from gpu_helpers import (CANARY, adversarial, assert_same_bytes, bf16_dev, blockwise, i32_dev,
+                         jagged_colwise, jagged_rowwise, mx_3d_colwise, mx_rowwise, random_offsets)
 
 pytestmark = pytest.mark.gpu
-
-
-def adversarial(shape, seed):
-    g = np.random.default_rng(seed)
-    bits = workloads.normal_bf16(shape, seed)
-    flat = bits.reshape(-1)
-    pick = g.choice(flat.size, size=max(1, flat.size // 16), replace=False)
-    specials = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x7F7F, 0xFF7F,
-                         0x3F80, 0xBF80, 0x43E0, 0x3C00], dtype=np.uint16)
-    flat[pick] = specials[g.integers(specials.size, size=pick.size)]
-    return bits
-
-
-def random_offsets(extent, G, seed, multiple=1, empties=1, short_tail=0):
-    g = np.random.default_rng(seed)
-    cuts = np.sort(g.integers(0, (extent - short_tail) // multiple + 1, size=G - 1)) * multiple
-    offs = np.concatenate([cuts, [extent - short_tail]]).astype(np.int64)
-    for _ in range(empties):                   # force some empty groups
-        j = int(g.integers(1, G)) if G > 1 else 0
-        if j > 0:
-            offs[j] = offs[j - 1]
-    offs = np.maximum.accumulate(offs)
-    return offs.astype(np.int32)
 
 
 def check_rowwise(bits, offs, canary_tail=True):
