@@ -39,6 +39,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="moe_bwd")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--flush-iters", type=int, default=0,
+                   help="after the timed steps, time each kernel this many more times with a "
+                        "1 GiB buffer written before every launch (cold L2 and MALL) and report "
+                        "median/min/max; 0 = skip")
     p.add_argument("--cpu-sample-rows", type=int, default=0,
                    help="rows/columns per tensor for the CPU-oracle sample (0 = auto)")
     return p.parse_args()
@@ -341,11 +345,35 @@ def main():
     dl = launches[dom]
     achieved = dl.nbytes / (per_kernel_ms[dom] * 1e-3) / 1e9
     traffic = traffic_for(dl.kernel, args.workload)
+    warm_ms = [[ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(K)] for i in range(len(launches))]
     kernels = {l.name: {"avg_us": round(per_kernel_ms[i] * 1e3, 2),
+                        "median_us": round(float(np.median(warm_ms[i])) * 1e3, 2),
+                        "min_us": round(float(np.min(warm_ms[i])) * 1e3, 2),
+                        "max_us": round(float(np.max(warm_ms[i])) * 1e3, 2),
                         "algorithmic_bytes": l.nbytes,
                         "GBps": round(l.nbytes / (per_kernel_ms[i] * 1e-3) / 1e9, 1),
                         "frac_of_peak": round(l.nbytes / (per_kernel_ms[i] * 1e-3) / 1e9 / PEAK_GBPS, 4)}
                for i, l in enumerate(launches)}
+
+    if args.flush_iters > 0:
+        # cold-cache timing: a 1 GiB write (more than the L2s and the 256 MB
+        # MALL) on the same stream before every launch
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        for i, l in enumerate(launches):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.flush_iters)]
+            for k, (a, b) in enumerate(evs):
+                flush.fill_(k & 0xFF)
+                a.record(stream)
+                l(sh)
+                b.record(stream)
+            torch.cuda.synchronize()
+            ms = [a.elapsed_time(b) for a, b in evs]
+            kernels[l.name]["flushed_us"] = {"median": round(float(np.median(ms)) * 1e3, 2),
+                                             "min": round(float(np.min(ms)) * 1e3, 2),
+                                             "max": round(float(np.max(ms)) * 1e3, 2),
+                                             "iters": args.flush_iters}
+        del flush
 
     cpu = None
     if not args.no_cpu_baseline and cpu_sample is not None:
