@@ -25,105 +25,13 @@
 
 #include <stdint.h>
 
+#include "group_tables.hpp"
 #include "mxq_device.hpp"
 #include "wave_ops.hpp"
 
 namespace mxq {
 
 constexpr int kJmxThreads = 256;
-constexpr int kJmxMaxGroups = 4096;
-
-// units of 2^SH elements in a group of n (n <= 0: none)
-template <int SH>
-__device__ __forceinline__ int units_of(int n)
-{
-    return n > 0 ? (n + (1 << SH) - 1) >> SH : 0;
-}
-
-// Fills s_end[g] = offs[g] clamped to [0, extent] and, for SH = SHA and SHB,
-// the exclusive prefix counts s_pa / s_pb (entry G = total) of the groups'
-// units, n_g = s_end[g] - s_end[g-1] (non-positive counts as empty).  Each
-// thread owns a contiguous chunk of groups; chunk totals are scanned across
-// the workgroup.  Ends with a barrier.
-template <int SHA, int SHB>
-__device__ void group_tables(const int32_t *__restrict__ offs, int G, int extent, int *s_end,
-                             int *s_pa, int *s_pb)
-{
-    __shared__ int s_wa[kJmxThreads / 64], s_wb[kJmxThreads / 64];
-    const int t = threadIdx.x;
-    const int lane = t & 63;
-    const int w = t >> 6;
-    const int ch = (G + kJmxThreads - 1) / kJmxThreads;
-    const int g0 = t * ch;
-    for (int k = 0; k < ch; ++k) {
-        const int g = g0 + k;
-        if (g < G) {
-            int e = offs[g];
-            s_end[g] = e < 0 ? 0 : (e > extent ? extent : e);
-        }
-    }
-    __syncthreads();
-    int sa = 0, sb = 0;
-    for (int k = 0; k < ch; ++k) {
-        const int g = g0 + k;
-        if (g < G) {
-            const int n = s_end[g] - (g ? s_end[g - 1] : 0);
-            sa += units_of<SHA>(n);
-            sb += units_of<SHB>(n);
-        }
-    }
-    // inclusive scan within the wave, then across the waves
-    int ia = sa, ib = sb;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int ya = __shfl_up(ia, d, 64);
-        const int yb = __shfl_up(ib, d, 64);
-        if (lane >= d) {
-            ia += ya;
-            ib += yb;
-        }
-    }
-    if (lane == 63) {
-        s_wa[w] = ia;
-        s_wb[w] = ib;
-    }
-    __syncthreads();
-    int ea = ia - sa, eb = ib - sb;
-    for (int ww = 0; ww < w; ++ww) {
-        ea += s_wa[ww];
-        eb += s_wb[ww];
-    }
-    for (int k = 0; k < ch; ++k) {
-        const int g = g0 + k;
-        if (g < G) {
-            const int n = s_end[g] - (g ? s_end[g - 1] : 0);
-            s_pa[g] = ea;
-            s_pb[g] = eb;
-            ea += units_of<SHA>(n);
-            eb += units_of<SHB>(n);
-        }
-    }
-    if (t == kJmxThreads - 1) {
-        s_pa[G] = ea;
-        s_pb[G] = eb;
-    }
-    __syncthreads();
-}
-
-// the group whose units cover unit j: s_pre[g] <= j < s_pre[g+1], given
-// 0 <= j < s_pre[G]
-__device__ __forceinline__ int find_group(const int *s_pre, int G, int j)
-{
-    int a = 0, b = G;
-    while (b - a > 1) {
-        const int m = (a + b) >> 1;
-        if (s_pre[m] <= j)
-            a = m;
-        else
-            b = m;
-    }
-    return a;
-}
 
 // x: (rows, cols), row r at x + r*ldx (ldx % 8 == 0), unit column stride;
 // groups along the columns.  q: row-major, ldq % 16 == 0.
@@ -135,23 +43,26 @@ __global__ __launch_bounds__(kJmxThreads) void jagged_mx_rowwise_kernel(
     const int32_t *__restrict__ offs, int G, uint8_t *__restrict__ q, int64_t ldq,
     uint8_t *__restrict__ scales, int64_t ss_r, int64_t ss_b, int nbt, int rceil)
 {
-    __shared__ int s_end[kJmxMaxGroups];
-    __shared__ int s_pre[kJmxMaxGroups + 1];
+    // group table, sized for the largest G: the LDS it takes keeps the
+    // occupancy at a level measured to stream faster than a table sized by G
+    __shared__ int s_end[kMaxTableGroups];
+    __shared__ int s_pre[kMaxTableGroups + 1];
 
     const int t = threadIdx.x;
     const int bj = (int)(blockIdx.x % (unsigned)nbt);
     const int br = (int)(blockIdx.x / (unsigned)nbt);
     const int r0 = br * RW;
 
-    // block table (units of 32), filled once (both tables are the same one)
-    group_tables<5, 5>(offs, G, cols, s_end, s_pre, s_pre);
+    // block table: prefix counts of 32-element blocks per group
+    load_group_ends<kJmxThreads>(offs, G, cols, s_end);
+    slot_prefix<kJmxThreads>(G, s_pre, [&](int g) { return units_of<5>(group_len(s_end, g)); });
     const int total = s_pre[G];
 
     const int j = bj * 64 + (t >> 2);
     const int l = t & 3;
     int p0 = 0, pn = 0;
     if (j < total) {
-        const int g = find_group(s_pre, G, j);
+        const int g = find_slot(s_pre, G, j);
         const int lo = g ? s_end[g - 1] : 0;
         const int hi = s_end[g];
         const int start = lo + 32 * (j - s_pre[g]);
@@ -218,9 +129,10 @@ __global__ __launch_bounds__(kJmxThreads) void jagged_mx_colwise_kernel(
     const int32_t *__restrict__ offs, int G, uint8_t *__restrict__ q, int64_t ldq,
     uint8_t *__restrict__ scales, int64_t ss_b, int64_t ss_c, int tiles_c, int rceil)
 {
-    __shared__ int s_end[kJmxMaxGroups];
-    __shared__ int s_pt[kJmxMaxGroups + 1];   // 128-row tiles
-    __shared__ int s_pb[kJmxMaxGroups + 1];   // 32-row blocks
+    // group table, sized for the largest G (see the rowwise kernel)
+    __shared__ int s_end[kMaxTableGroups];
+    __shared__ int s_pt[kMaxTableGroups + 1];   // 128-row tiles
+    __shared__ int s_pb[kMaxTableGroups + 1];   // 32-row blocks
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -230,10 +142,13 @@ __global__ __launch_bounds__(kJmxThreads) void jagged_mx_colwise_kernel(
     const int tc = (int)(blockIdx.x % (unsigned)tiles_c);
     const int tid = (int)(blockIdx.x / (unsigned)tiles_c);
 
-    group_tables<7, 5>(offs, G, rows, s_end, s_pt, s_pb);
+    load_group_ends<kJmxThreads>(offs, G, rows, s_end);
+    slot_prefix2<kJmxThreads>(G, s_pt, s_pb,
+                              [&](int gg) { return units_of<7>(group_len(s_end, gg)); },
+                              [&](int gg) { return units_of<5>(group_len(s_end, gg)); });
     if (tid >= s_pt[G])
         return;
-    const int g = find_group(s_pt, G, tid);
+    const int g = find_slot(s_pt, G, tid);
     const int lo = g ? s_end[g - 1] : 0;
     const int hi = s_end[g];
     const int k = tid - s_pt[g];
