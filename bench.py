@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="moe_bwd")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-copy-ceiling", action="store_true",
+                   help="skip timing the 4 GiB device-to-device copy used as the practical ceiling")
     p.add_argument("--flush-iters", type=int, default=0,
                    help="after the timed steps, time each kernel this many more times with a "
                         "1 GiB buffer written before every launch (cold L2 and MALL) and report "
@@ -178,6 +180,8 @@ def build_mx3d(torch, mxq, workloads, E, sweep, rceil=False):
     for e in range(E):
         bits = workloads.mx3d_sweep_expert(e) if sweep else workloads.mx3d_expert(e)
         w[e].copy_(bf16_dev(torch, bits))
+        if E > 8 and (e + 1) % 8 == 0:
+            print(f"[bench] generated {e + 1} of {E} experts", file=sys.stderr, flush=True)
     q = torch.empty(E * N * K, dtype=torch.uint8, device="cuda")
     s = torch.empty(E * (N // 32) * K, dtype=torch.uint8, device="cuda")
     l = Launch(f"mx_3d_colwise ({E},{N},{K})", "block_strided_kernel<32, 1, true>",
@@ -375,6 +379,28 @@ def main():
                                              "iters": args.flush_iters}
         del flush
 
+    ceiling = None
+    if not args.no_copy_ceiling:
+        # practical ceiling: a 4 GiB device-to-device copy (the runtime's copy
+        # kernel), counted as bytes read plus bytes written
+        n = 4 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for a, b in evs:
+            a.record(stream)
+            dst.copy_(src)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        copy_gbps = 2 * n / (ms * 1e-3) / 1e9
+        ceiling = {"d2d_copy_GBps": round(copy_gbps, 1), "copy_bytes": 2 * n,
+                   "frac_of_copy": round(achieved / copy_gbps, 4)}
+        del src, dst
+
     cpu = None
     if not args.no_cpu_baseline and cpu_sample is not None:
         import oracle
@@ -405,6 +431,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": dl.kernel, "algorithmic_bytes_per_launch": dl.nbytes,
                      "avg_launch_us": round(per_kernel_ms[dom] * 1e3, 2)},
+        "copy_ceiling": ceiling,
         "kernels": kernels,
         "cpu_baseline": cpu,
         "csrc_digest": csrc_digest(),

@@ -1,0 +1,25 @@
+"""Host-side checks of bench.py's command line (no GPU needed)."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    out = json.loads(r.stdout.strip().splitlines()[-1])
+    assert out["n_gpus"] == 2 and "one GPU" in out["error"]
+
+
+def test_workload_table_names_every_configuration():
+    sys.path.insert(0, ROOT)
+    import bench
+
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    for name in ("moe_bwd", "moe_bwd_mx", "mx3d", "mx3d_rceil", "blockwise", "copy"):
+        assert f'"{name}"' in src, name
+    assert callable(bench.build)
