@@ -94,8 +94,9 @@ mxq_status run_jagged_strided(const uint16_t *x, int64_t ext, int64_t ncols, int
     const int64_t nblocks = 8 * SPS * ((G * nsuper + 7) / 8);
     if (nblocks > INT32_MAX)
         return MXQ_ERR_INVALID_ARG;
+    const size_t lds = G > 64 ? (3 * (size_t)G + 2) * sizeof(int) + (size_t)G : 0;
     jagged_strided_kernel<CG, kJaggedStridedTiles, NW>
-        <<<dim3((unsigned)nblocks), dim3(64 * NW), 0, st>>>(x, ldx, (int)ext, (int)ncols, offs, G, q,
+        <<<dim3((unsigned)nblocks), dim3(64 * NW), lds, st>>>(x, ldx, (int)ext, (int)ncols, offs, G, q,
                                                            ldq, scales, ss_g, ss_col, (int)nsuper);
     return launch_status();
 }

@@ -26,6 +26,7 @@
 //    largest group first (computed on the device from the offsets).
 #pragma once
 
+#include "group_tables.hpp"
 #include "mxq_device.hpp"
 #include "wave_ops.hpp"
 
@@ -375,15 +376,27 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_long_kernel(
 
 // --------------------------------------------------------------- strided
 
-// Mapping of workgroups to (group rank, column strip).  SPS = 8 / CG strips
-// of 8*CG columns (16*CG bytes of a row) make one 128-byte "superstrip"; the
-// SPS workgroups of a superstrip get block ids that differ by 8, so with the
-// round-robin placement of workgroups on the 8 XCDs they share one XCD (and
-// its L2) and are dispatched back to back: their row pieces complete each
-// other's cache lines.  Superstrips are numbered rank-major, ranks ordered
-// largest group first.
+// Colwise work items, per column strip.  A long group (16-row-aligned span
+// over TROWS rows) is one item; its workgroup reads up to T tiles into
+// registers and streams the rest.  Short groups (empty ones included) are
+// packed: the consecutive short groups whose starts fall in one TROWS-row
+// block, at most kPackMax of them, make one item.  A pack spans fewer than
+// 2*TROWS rows, so it is read once into registers; each wave reduces its
+// rows with shuffles when they all belong to one group and with per-lane
+// segments otherwise, merging into per-group column maxima in LDS.  Every
+// item owns at least one group, so a strip has at most G items.  Long
+// groups come first, largest first when G <= 64 (ranked on the device by
+// one wave, lane g holding group g), then the packs in group order.
+constexpr int kPackMax = 16;
+
+// Workgroup -> (item, column strip).  SPS = 8 / CG strips of 8*CG columns
+// (16*CG bytes of a row) make one 128-byte "superstrip"; the SPS workgroups
+// of a superstrip get block ids that differ by 8, so with the round-robin
+// placement of workgroups on the 8 XCDs they share one XCD (and its L2) and
+// are dispatched back to back: their row pieces complete each other's cache
+// lines.  Superstrips are numbered item-major.
 struct StripMap {
-    int rank, strip;
+    int item, strip;
     bool valid;
 };
 
@@ -395,22 +408,80 @@ __device__ __forceinline__ StripMap map_strip(int b, int nsuper, int G)
     const int sub = k % SPS;           // strip within the superstrip
     const int S = (k / SPS) * 8 + x;   // logical superstrip index
     StripMap m;
-    m.rank = S / nsuper;
+    m.item = S / nsuper;
     m.strip = (S % nsuper) * SPS + sub;
-    m.valid = m.rank < G;
+    m.valid = m.item < G;
     return m;
+}
+
+// Per-workgroup item table for G > 64 (NTH threads), all in LDS: s_end
+// (clamped group ends), s_lead (1 for a group that starts a pack), s_lpre /
+// s_ppre (exclusive prefix counts of long groups / pack leaders by group
+// index; long groups then go in index order).  TR = rows per tile.
+template <int NTH, int TR>
+__device__ void strided_table(const int32_t *__restrict__ offs, int G, int rows, int *s_end,
+                              uint8_t *s_lead, int *s_lpre, int *s_ppre)
+{
+    load_group_ends<NTH>(offs, G, rows, s_end);
+    auto lo_of = [&](int g) { return g ? s_end[g - 1] : 0; };
+    auto is_long = [&](int g) {
+        const int lo = lo_of(g), hi = s_end[g];
+        return hi > lo && hi - (lo & ~15) > TR;
+    };
+    // run starts: a run of short groups breaks at a long group and where the
+    // start moves to another TR-row block; inclusive max-scan of the breaks
+    {
+        __shared__ int s_wmax[NTH / 64];
+        const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+        const int ch = (G + NTH - 1) / NTH;
+        const int s0 = t * ch;
+        auto brk = [&](int g) {
+            return (g == 0 || is_long(g) || is_long(g - 1) || lo_of(g) / TR != lo_of(g - 1) / TR)
+                       ? g : -1;
+        };
+        int m = -1;
+        for (int k = 0; k < ch; ++k)
+            if (s0 + k < G)
+                m = max(m, brk(s0 + k));
+        int inc = m;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(inc, d, 64);
+            if (lane >= d)
+                inc = max(inc, y);
+        }
+        if (lane == 63)
+            s_wmax[w] = inc;
+        __syncthreads();
+        int run = __shfl_up(inc, 1, 64);
+        if (lane == 0)
+            run = -1;
+        for (int ww = 0; ww < w; ++ww)
+            run = max(run, s_wmax[ww]);
+        for (int k = 0; k < ch; ++k) {
+            const int g = s0 + k;
+            if (g < G) {
+                run = max(run, brk(g));
+                s_lead[g] = (!is_long(g) && ((g - run) % kPackMax) == 0) ? 1 : 0;
+            }
+        }
+        __syncthreads();
+    }
+    slot_prefix2<NTH>(G, s_lpre, s_ppre, [&](int g) { return is_long(g) ? 1 : 0; },
+                      [&](int g) { return (int)s_lead[g]; });
 }
 
 // x: (rows, cols), row r at x + r*ldx, unit column stride, cols % 8 == 0.
 // q: column-major, element (r, c) at q[c*ldq + r].
 // scales[g*ss_g + c*ss_c].
 // Each lane holds a 16-row x 8-column piece; a wave stacks 64/CG pieces
-// down the rows and CG across; four waves stack down the rows, so one
-// register tile covers TROWS = 4*16*64/CG rows x 8*CG columns.  Up to T
-// tiles stay resident: a group of at most T*TROWS rows is read from HBM
-// once.  Longer groups stream their tiles beyond the first T-1 through the
-// last buffer and re-read them in the scaling pass.
-// Grid: 8 * (8/CG) * ceil(G * nsuper / 8) workgroups (see map_strip).
+// down the rows and CG across; NW waves stack down the rows, so one
+// register tile covers TROWS = NW*16*64/CG rows x 8*CG columns.  Up to T
+// tiles stay resident: a long group of at most T*TROWS rows is read from
+// HBM once; longer groups stream their tiles beyond the first T-1 through
+// the last buffer and re-read them in the scaling pass.
+// Grid: 8 * (8/CG) * ceil(G * nsuper / 8) workgroups (see map_strip);
+// dynamic LDS (3G + 2) * 4 + G bytes when G > 64, none otherwise.
 template <int CG, int T, int NW>
 __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int rows, int cols,
@@ -421,10 +492,21 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
     constexpr int WROWS = 16 * QD;    // rows per wave
     constexpr int TROWS = NW * WROWS; // rows per register tile
     constexpr int SW = 8 * CG;        // strip width in columns
+    constexpr int NTH = 64 * NW;
+    static_assert(T >= 2, "a pack spans up to two tiles");
 
-    __shared__ int s_group;
+    // group tables: 64 ends in static LDS; for G > 64 the launch passes
+    // (3G + 2) ints and G bytes of dynamic LDS.  Little LDS lets the next
+    // workgroup on a CU start while this one's last waves drain.
+    __shared__ int s_end64[64];
+    extern __shared__ int s_dyn[];
+    int *const s_end = G <= 64 ? s_end64 : s_dyn;
+    int *const s_lpre = s_dyn + G;
+    int *const s_ppre = s_dyn + 2 * G + 1;
+    uint8_t *const s_lead = reinterpret_cast<uint8_t *>(s_dyn + 3 * G + 2);
     __shared__ uint32_t s_red[NW][SW];
     __shared__ float s_scale[SW];
+    __shared__ uint32_t s_pk[kPackMax][SW];   // pack: column maxima, then multipliers
 
     const StripMap sm = map_strip<8 / CG>(blockIdx.x, nsuper, G);
     if (!sm.valid)
@@ -436,45 +518,284 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
     const int cg = lane % CG;
     const int qd = lane / CG;
 
-    // group of this rank: largest first (ties by index) when G is small
-    // enough to rank here, identity otherwise.  The offsets are read from
-    // global memory once (one load per thread) and ranked from LDS.
-    __shared__ int s_lo[64], s_hi[64];
+    // this workgroup's item: a long group g, or a pack of short groups [g0, g1)
+    __shared__ int s_sel[3];
     if (G <= 64) {
-        if (t < G) {
-            int lo_t = t == 0 ? 0 : offs[t - 1];
-            int hi_t = offs[t];
-            lo_t = lo_t < 0 ? 0 : (lo_t > rows ? rows : lo_t);
-            hi_t = hi_t < lo_t ? lo_t : (hi_t > rows ? rows : hi_t);
-            s_lo[t] = lo_t;
-            s_hi[t] = hi_t;
+        // one wave builds the table with lane g holding group g
+        if (w == 0) {
+            const bool valid = lane < G;
+            int hi = valid ? offs[lane] : rows;
+            hi = hi < 0 ? 0 : (hi > rows ? rows : hi);
+            int lo = __shfl_up(hi, 1, 64);
+            lo = lane == 0 ? 0 : lo;
+            if (valid)
+                s_end[lane] = hi;
+            const int len = hi > lo ? hi - lo : 0;
+            const bool lng = valid && hi > lo && hi - (lo & ~15) > TROWS;
+            const int blk = lo / TROWS;
+            const int pblk = __shfl_up(blk, 1, 64);
+            const int plng = __shfl_up(lng ? 1 : 0, 1, 64);
+            int run = (valid && (lane == 0 || lng || plng || blk != pblk)) ? lane : -1;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int y = __shfl_up(run, d, 64);
+                if (lane >= d)
+                    run = max(run, y);
+            }
+            const bool lead = valid && !lng && ((lane - run) % kPackMax) == 0;
+            const uint64_t mlong = __ballot(lng);
+            const uint64_t mlead = __ballot(lead);
+            const int nl = __popcll(mlong);
+            const int item = sm.item;
+            if (item < nl) {
+                // rank of a long group: longer first, ties by index
+                int r = 0;
+                for (int h = 0; h < G; ++h) {
+                    const int lh = __builtin_amdgcn_readlane(len, h);
+                    const bool hl = (mlong >> h) & 1ull;
+                    r += hl && ((lh > len) || (lh == len && h < lane));
+                }
+                if (lng && r == item) {
+                    s_sel[0] = 0;
+                    s_sel[1] = lane;
+                }
+            } else if (lane == 0) {
+                int k = item - nl;
+                uint64_t m = mlead;
+                while (k > 0 && m) {
+                    m &= m - 1;
+                    --k;
+                }
+                if (!m) {
+                    s_sel[0] = 2;   // no such item
+                } else {
+                    const int g0 = __ffsll((unsigned long long)m) - 1;
+                    const uint64_t after = g0 + 1 < 64 ? ~0ull << (g0 + 1) : 0ull;
+                    const uint64_t stop = (mlead | mlong) & after;
+                    s_sel[0] = 1;
+                    s_sel[1] = g0;
+                    s_sel[2] = stop ? __ffsll((unsigned long long)stop) - 1 : G;
+                }
+            }
         }
         __syncthreads();
-        if (t < G) {
-            const int mine = s_hi[t] - s_lo[t];
-            int r = 0;
-            for (int h = 0; h < G; ++h) {
-                const int lh = s_hi[h] - s_lo[h];
-                r += (lh > mine) || (lh == mine && h < t);
+    } else {
+        strided_table<NTH, TROWS>(offs, G, rows, s_end, s_lead, s_lpre, s_ppre);
+        if (t == 0) {
+            const int nlong = s_lpre[G], npack = s_ppre[G];
+            if (sm.item < nlong) {
+                s_sel[0] = 0;
+                s_sel[1] = find_slot(s_lpre, G, sm.item);
+            } else if (sm.item < nlong + npack) {
+                const int pk = sm.item - nlong;
+                const int g0 = find_slot(s_ppre, G, pk);
+                int g1 = pk + 1 < npack ? find_slot(s_ppre, G, pk + 1) : G;
+                if (s_lpre[g0] < nlong) {
+                    const int gl = find_slot(s_lpre, G, s_lpre[g0]);   // first long group after g0
+                    g1 = gl < g1 ? gl : g1;
+                }
+                s_sel[0] = 1;
+                s_sel[1] = g0;
+                s_sel[2] = g1;
+            } else {
+                s_sel[0] = 2;
             }
-            if (r == sm.rank)
-                s_group = t;
         }
-    } else if (t == 0) {
-        const int gg = sm.rank;
-        int lo_t = gg == 0 ? 0 : offs[gg - 1];
-        int hi_t = offs[gg];
-        lo_t = lo_t < 0 ? 0 : (lo_t > rows ? rows : lo_t);
-        hi_t = hi_t < lo_t ? lo_t : (hi_t > rows ? rows : hi_t);
-        s_group = 0;
-        s_lo[0] = lo_t;
-        s_hi[0] = hi_t;
+        __syncthreads();
     }
-    __syncthreads();
-    const int g = G <= 64 ? s_group : sm.rank;
-    const int slot = G <= 64 ? g : 0;
-    const int lo = s_lo[slot];
-    const int hi = s_hi[slot];
+    const int kind = s_sel[0];
+    if (kind == 2)
+        return;
+
+    if (kind == 1) {
+        // ---- a pack of short groups [g0, g1)
+        const int g0 = s_sel[1];
+        const int g1 = s_sel[2];
+        const int npk = g1 - g0;
+        const int plo = g0 ? s_end[g0 - 1] : 0;
+        int phi = s_end[g1 - 1];
+        phi = phi < plo ? plo : phi;
+        const int prb = plo & ~15;
+        int nit = phi > plo ? (phi - prb + TROWS - 1) / TROWS : 0;
+        nit = nit < T ? nit : T;
+        const int cbase = sm.strip * SW + 8 * cg;
+        const bool col_ok = cbase < cols;
+
+        // group of row r inside the pack (rows before plo / at phi and after
+        // have none): first g in [g0, g1) whose end is past r
+        auto group_of = [&](int r) {
+            int a = g0, b = g1;
+            while (a < b) {
+                const int m = (a + b) >> 1;
+                if (s_end[m] <= r)
+                    a = m + 1;
+                else
+                    b = m;
+            }
+            return a;
+        };
+
+        for (int e = t; e < npk * SW; e += NTH)
+            s_pk[e / SW][e % SW] = 0u;
+
+        uint4 v[T][16];
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+            if (tt < nit) {
+                const int rb = prb + tt * TROWS + w * WROWS + 16 * qd;
+                const uint16_t *p = x + (int64_t)rb * ldx + cbase;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = rb + i;
+                    v[tt][i] = (col_ok && r >= plo && r < phi) ? ld16_nt(p + (int64_t)i * ldx)
+                                                                : make_uint4(0u, 0u, 0u, 0u);
+                }
+            }
+        }
+        __syncthreads();   // s_pk cleared
+
+        // reduce: per tile, a wave whose rows all lie in one group uses
+        // shuffles; otherwise each lane merges its own row segments
+        int ga[T], gb[T];   // group of the lane's first / last row in the pack (g1: none)
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+            ga[tt] = gb[tt] = g1;
+            if (tt >= nit)
+                continue;
+            const int rb = prb + tt * TROWS + w * WROWS + 16 * qd;
+            const int r0 = rb < plo ? plo : rb;
+            const int r1 = (rb + 16 < phi ? rb + 16 : phi) - 1;
+            if (r0 <= r1) {
+                ga[tt] = group_of(r0);
+                gb[tt] = group_of(r1);
+            }
+            const uint64_t has = __ballot(ga[tt] < g1);
+            if (has == 0)
+                continue;
+            const int gw = __shfl(ga[tt], __ffsll((unsigned long long)has) - 1, 64);
+            const bool uniform = __all(ga[tt] == g1 || (ga[tt] == gb[tt] && ga[tt] == gw));
+            if (uniform) {
+                uint32_t mx[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    mx[0] = absmax2(mx[0], v[tt][i].x);
+                    mx[1] = absmax2(mx[1], v[tt][i].y);
+                    mx[2] = absmax2(mx[2], v[tt][i].z);
+                    mx[3] = absmax2(mx[3], v[tt][i].w);
+                }
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    mx[d] = strided_pkmax<CG>(mx[d]);
+                if (qd == 0 && col_ok) {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        atomicMax(&s_pk[gw - g0][8 * cg + 2 * d], mx[d] & 0xffffu);
+                        atomicMax(&s_pk[gw - g0][8 * cg + 2 * d + 1], mx[d] >> 16);
+                    }
+                }
+            } else if (ga[tt] < g1 && col_ok) {
+                int gc = ga[tt];
+                int next = s_end[gc];
+                uint32_t acc[4] = {0u, 0u, 0u, 0u};
+                auto flush = [&]() {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        atomicMax(&s_pk[gc - g0][8 * cg + 2 * d], acc[d] & 0xffffu);
+                        atomicMax(&s_pk[gc - g0][8 * cg + 2 * d + 1], acc[d] >> 16);
+                        acc[d] = 0u;
+                    }
+                };
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = rb + i;
+                    if (r >= plo && r < phi) {
+                        if (r >= next) {
+                            flush();
+                            while (gc < g1 - 1 && s_end[gc] <= r)
+                                ++gc;
+                            next = s_end[gc];
+                        }
+                        acc[0] = absmax2(acc[0], v[tt][i].x);
+                        acc[1] = absmax2(acc[1], v[tt][i].y);
+                        acc[2] = absmax2(acc[2], v[tt][i].z);
+                        acc[3] = absmax2(acc[3], v[tt][i].w);
+                    }
+                }
+                flush();
+            }
+        }
+        __syncthreads();
+        for (int e = t; e < npk * SW; e += NTH) {
+            const int k = e / SW, c = e % SW;
+            const float s = fp32_scale(s_pk[k][c]);
+            s_pk[k][c] = __float_as_uint(s);
+            const int col = sm.strip * SW + c;
+            if (col < cols)
+                scales[(int64_t)(g0 + k) * ss_g + (int64_t)col * ss_c] = s;
+        }
+        __syncthreads();
+        if (!col_ok)
+            return;
+
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+            if (tt >= nit || ga[tt] >= g1)
+                continue;
+            const int rb = prb + tt * TROWS + w * WROWS + 16 * qd;
+            if (ga[tt] == gb[tt]) {
+                float sc[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    sc[j] = __uint_as_float(s_pk[ga[tt] - g0][8 * cg + j]);
+                const bool full = rb >= plo && rb + 16 <= phi;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    uint4 o;
+                    o.x = cvt4_nosat(elem8(v[tt][0], j) * sc[j], elem8(v[tt][1], j) * sc[j],
+                                     elem8(v[tt][2], j) * sc[j], elem8(v[tt][3], j) * sc[j]);
+                    o.y = cvt4_nosat(elem8(v[tt][4], j) * sc[j], elem8(v[tt][5], j) * sc[j],
+                                     elem8(v[tt][6], j) * sc[j], elem8(v[tt][7], j) * sc[j]);
+                    o.z = cvt4_nosat(elem8(v[tt][8], j) * sc[j], elem8(v[tt][9], j) * sc[j],
+                                     elem8(v[tt][10], j) * sc[j], elem8(v[tt][11], j) * sc[j]);
+                    o.w = cvt4_nosat(elem8(v[tt][12], j) * sc[j], elem8(v[tt][13], j) * sc[j],
+                                     elem8(v[tt][14], j) * sc[j], elem8(v[tt][15], j) * sc[j]);
+                    uint8_t *pq = q + (int64_t)(cbase + j) * ldq + rb;
+                    if (full) {
+                        st16_nt(pq, o);
+                    } else {
+                        const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            if (rb + i >= plo && rb + i < phi)
+                                pq[i] = (uint8_t)(ow[i >> 2] >> (8 * (i & 3)));
+                    }
+                }
+            } else {
+                // rows of several groups: per-row multipliers, byte stores
+                int gc = ga[tt];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = rb + i;
+                    if (r < plo || r >= phi)
+                        continue;
+                    while (gc < g1 - 1 && s_end[gc] <= r)
+                        ++gc;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float sj = __uint_as_float(s_pk[gc - g0][8 * cg + j]);
+                        q[(int64_t)(cbase + j) * ldq + r] = (uint8_t)cvt1(elem8(v[tt][i], j) * sj);
+                    }
+                }
+            }
+        }
+        return;
+    }
+
+    // ---- a long group
+    const int g = s_sel[1];
+    const int lo = g ? s_end[g - 1] : 0;
+    int hi = s_end[g];
+    hi = hi < lo ? lo : hi;
 
     const int cbase = sm.strip * SW + 8 * cg;
     const bool col_ok = cbase < cols;

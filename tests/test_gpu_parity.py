@@ -78,8 +78,13 @@ def test_jagged_rowwise_empty_extent_writes_empty_group_scales():
     (9300, 24, 1, 1, 7, 20),       # ring: several passes, ragged ends
     (13000, 72, 2, 1, 0, 21),
     (2049, 40, 2, 1, 0, 22),
-    (3000, 64, 1, 1, 0, 23),       # one LDS tile, the last tile in registers
+    (3000, 64, 1, 1, 0, 23),
     (6100, 136, 3, 1, 5, 24),
+    (16384, 64, 64, 256, 0, 25),   # short groups packed, waves inside one group
+    (5000, 40, 200, 1, 0, 26),     # packs of up to 64 groups, waves across groups
+    (3000, 16, 1000, 1, 3, 27),    # groups of a few rows, many per lane
+    (20000, 24, 30, 16, 0, 28),    # long and short groups interleaved
+    (4096, 8, 4096, 1, 0, 29),     # the most groups, most of them empty
 ])
 def test_jagged_colwise_ragged(rows, cols, G, mult, tail, seed):
     bits = adversarial((rows, cols), 200 + seed)
@@ -206,3 +211,11 @@ def test_mx_every_bf16_amax(mode):
     oq, os_ = oracle.quantize_mx_rowwise(x, mode=mode)
     assert_same_bytes(q, oq, f"mx rowwise {mode} q (every amax)")
     assert_same_bytes(s, os_, f"mx rowwise {mode} scales (every amax)")
+
+
+def test_jagged_colwise_many_equal_groups():
+    """64 groups of 256 rows (many experts, few tokens each): whole waves
+    inside one group, four groups per 1024-row block."""
+    bits = adversarial((16384, 72), 230)
+    offs = np.arange(256, 16385, 256, dtype=np.int32)
+    check_colwise(bits, offs)
