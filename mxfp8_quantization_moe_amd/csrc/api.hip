@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "mxq.h"
 #include "block_kernels.hpp"
@@ -26,20 +27,30 @@ mxq_status launch_status()
     return e == hipSuccess ? MXQ_OK : MXQ_ERR_LAUNCH;
 }
 
-// number of compute units of the current device (queried once per device)
-int device_cu_count()
+// number of compute units of the device that runs `st` (the calling
+// thread's current device for the null stream), queried once per device;
+// the cache is atomic so concurrent callers are safe
+int device_cu_count(hipStream_t st)
 {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    if (st) {
+        hipDevice_t d = 0;
+        if (hipStreamGetDevice(st, &d) != hipSuccess)
+            return 256;
+        dev = (int)d;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
         return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    }
+    if (dev < 0 || dev >= 64)
+        return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 // jagged, reduction along the unit-stride dim of a (nrows, ext) view
@@ -54,7 +65,7 @@ mxq_status run_jagged_contig(const uint16_t *x, int64_t nrows, int64_t ext, int6
     const size_t lds = (size_t)3 * G * sizeof(uint32_t);
     // persistent grid: a few workgroups per compute unit, each walking rows
     const int64_t per_cu = 4;
-    const int64_t nwg = std::min<int64_t>(nrows, per_cu * device_cu_count());
+    const int64_t nwg = std::min<int64_t>(nrows, per_cu * device_cu_count(st));
     const dim3 grid((unsigned)nwg), block(kThreads);
     const int rows = (int)nrows, cols = (int)ext;
     if (ext > 8 * kThreads * 8) {
