@@ -16,7 +16,7 @@ namespace {
 using namespace mxq;
 
 constexpr int kJaggedStridedCG = 8;     // 64-column strips (full 128-byte row pieces)
-constexpr int kJaggedStridedTiles = 2;  // register tiles per lane
+constexpr int kJaggedStridedTiles = 3;  // register tiles per lane (233 VGPRs, 2 waves per SIMD)
 constexpr int kJaggedStridedWaves = 8;  // waves per workgroup: tile = 8*16*64/CG = 1024 rows
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
