@@ -19,6 +19,11 @@ page, and the token-grouped operands of the jagged scaling pages):
 * ``mx3d_sweep`` the same with 1% of 32x1 blocks zeroed and 1% scaled 2^20.
 * ``blockwise`` act (8192, 4096) and W (4096, 4096), N(0,1) with 1/8 of the
               columns Student-t(3).
+* ``large``   tensors of more than 2^31 elements (64-bit indexing checks),
+              N(0,1) drawn directly on the GPU by torch's seeded Philox
+              generator (too large to draw on the host in a test); the
+              tests copy the bit patterns of sampled rows or columns back
+              for the oracle.
 """
 from __future__ import annotations
 
@@ -190,3 +195,12 @@ def blockwise_weight() -> np.ndarray:
 def algorithmic_bytes(numel: int, scale_bytes: int) -> int:
     """bf16 read + e4m3 write + scale write (offsets excluded)."""
     return 2 * numel + numel + scale_bytes
+
+
+def device_normal_bf16(shape, seed: int, device="cuda"):
+    """N(0,1) bf16 tensor drawn on the GPU with torch's seeded generator.
+    For inputs too large to draw on the host; callers hand the oracle the
+    bit patterns of whatever part they check, read back from the device."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
