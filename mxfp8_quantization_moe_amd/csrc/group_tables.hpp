@@ -129,6 +129,43 @@ __device__ void slot_prefix2(int G, int *s_pa, int *s_pb, CountA count_a, CountB
     __syncthreads();
 }
 
+// The same tables for G <= 64 built by the calling wave alone (lane g holds
+// group g): s_end, and the exclusive prefix counts of units of 2^SHA and
+// 2^SHB elements per group into s_pa / s_pb (entry G = total).  One global
+// load per lane and shuffle scans; the caller follows with a barrier.
+template <int SHA, int SHB>
+__device__ __forceinline__ void wave_group_tables(const int32_t *__restrict__ offs, int G,
+                                                  int extent, int *s_end, int *s_pa, int *s_pb)
+{
+    const int lane = threadIdx.x & 63;
+    const bool valid = lane < G;
+    int hi = valid ? offs[lane] : extent;
+    hi = hi < 0 ? 0 : (hi > extent ? extent : hi);
+    int lo = __shfl_up(hi, 1, 64);
+    lo = lane == 0 ? 0 : lo;
+    const int n = valid && hi > lo ? hi - lo : 0;
+    const int ua = units_of<SHA>(n), ub = units_of<SHB>(n);
+    int ia = ua, ib = ub;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int ya = __shfl_up(ia, d, 64);
+        const int yb = __shfl_up(ib, d, 64);
+        if (lane >= d) {
+            ia += ya;
+            ib += yb;
+        }
+    }
+    if (valid) {
+        s_end[lane] = hi;
+        s_pa[lane] = ia - ua;
+        s_pb[lane] = ib - ub;
+    }
+    if (lane == G - 1) {
+        s_pa[G] = ia;
+        s_pb[G] = ib;
+    }
+}
+
 // the slot whose work covers index j: s_pre[s] <= j < s_pre[s+1], given
 // 0 <= j < s_pre[G] (slots with no work are skipped)
 __device__ __forceinline__ int find_slot(const int *s_pre, int G, int j)

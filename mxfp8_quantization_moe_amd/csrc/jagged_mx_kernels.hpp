@@ -54,8 +54,14 @@ __global__ __launch_bounds__(kJmxThreads) void jagged_mx_rowwise_kernel(
     const int r0 = br * RW;
 
     // block table: prefix counts of 32-element blocks per group
-    load_group_ends<kJmxThreads>(offs, G, cols, s_end);
-    slot_prefix<kJmxThreads>(G, s_pre, [&](int g) { return units_of<5>(group_len(s_end, g)); });
+    if (G <= 64) {
+        if (t < 64)
+            wave_group_tables<5, 5>(offs, G, cols, s_end, s_pre, s_pre);
+        __syncthreads();
+    } else {
+        load_group_ends<kJmxThreads>(offs, G, cols, s_end);
+        slot_prefix<kJmxThreads>(G, s_pre, [&](int g) { return units_of<5>(group_len(s_end, g)); });
+    }
     const int total = s_pre[G];
 
     const int j = bj * 64 + (t >> 2);
@@ -142,10 +148,16 @@ __global__ __launch_bounds__(kJmxThreads) void jagged_mx_colwise_kernel(
     const int tc = (int)(blockIdx.x % (unsigned)tiles_c);
     const int tid = (int)(blockIdx.x / (unsigned)tiles_c);
 
-    load_group_ends<kJmxThreads>(offs, G, rows, s_end);
-    slot_prefix2<kJmxThreads>(G, s_pt, s_pb,
-                              [&](int gg) { return units_of<7>(group_len(s_end, gg)); },
-                              [&](int gg) { return units_of<5>(group_len(s_end, gg)); });
+    if (G <= 64) {
+        if (t < 64)
+            wave_group_tables<7, 5>(offs, G, rows, s_end, s_pt, s_pb);
+        __syncthreads();
+    } else {
+        load_group_ends<kJmxThreads>(offs, G, rows, s_end);
+        slot_prefix2<kJmxThreads>(G, s_pt, s_pb,
+                                  [&](int gg) { return units_of<7>(group_len(s_end, gg)); },
+                                  [&](int gg) { return units_of<5>(group_len(s_end, gg)); });
+    }
     if (tid >= s_pt[G])
         return;
     const int g = find_slot(s_pt, G, tid);
