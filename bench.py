@@ -51,12 +51,20 @@ def parse():
 
 
 def csrc_digest() -> str:
+    """Digest of the kernel sources with comments and blank space removed, so
+    the counter summary stays valid across comment-only edits."""
+    import re
+
     d = os.path.join(ROOT, "mxfp8_quantization_moe_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(d)):
-        with open(os.path.join(d, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
+        with open(os.path.join(d, name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = "\n".join(line.strip() for line in text.splitlines() if line.strip())
+        h.update(name.encode())
+        h.update(text.encode())
     return h.hexdigest()[:16]
 
 

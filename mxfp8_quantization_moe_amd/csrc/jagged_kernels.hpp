@@ -17,13 +17,14 @@
 //
 //  * jagged_strided_kernel — the reduction runs across rows (colwise on a
 //    row-major tensor), the output is column-major.  A workgroup owns one
-//    (column strip, group).  Each lane holds a 16-row x 8-column sub-tile
+//    (column strip, item), an item being one long group or a pack of
+//    consecutive short groups.  Each lane holds a 16-row x 8-column sub-tile
 //    loaded as sixteen 16-byte row pieces, so a load instruction reads whole
 //    row segments and, after the scale is applied per column, the lane owns
 //    16 consecutive bytes of each of its 8 output columns: the transpose to
 //    column-major happens inside the lane's registers and every store is a
-//    16-byte piece of a contiguous column run.  Workgroups are ordered
-//    largest group first (computed on the device from the offsets).
+//    16-byte piece of a contiguous column run.  Long groups come first,
+//    largest first (ranked on the device from the offsets).
 #pragma once
 
 #include "group_tables.hpp"
