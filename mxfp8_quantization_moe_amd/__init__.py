@@ -63,6 +63,16 @@ def _require_bf16_cuda(x, ndim: int, name: str):
                         f"{tuple(x.shape)} on {x.device}")
 
 
+def _require_offs(offs, x):
+    """Group ends: a contiguous 1-D int32 tensor on x's device (read only by
+    the kernels, never on the host)."""
+    torch = _torch()
+    if (offs.dtype != torch.int32 or offs.dim() != 1 or not offs.is_contiguous()
+            or offs.device != x.device):
+        raise TypeError(f"offs must be a contiguous 1-D int32 tensor on {x.device}, got "
+                        f"{offs.dtype} {tuple(offs.shape)} on {offs.device}")
+
+
 def _round_up(n: int, m: int) -> int:
     return (n + m - 1) // m * m
 
@@ -91,6 +101,7 @@ def quantize_jagged_rowwise(x, offs, *, stream=None):
     tensor (e.g. ``grad_out.t()``)."""
     torch = _torch()
     _require_bf16_cuda(x, 2, "x")
+    _require_offs(offs, x)
     rows, cols = x.shape
     G = offs.numel()
     q = _empty_rowmajor_u8(torch, rows, cols, x.device)
@@ -108,6 +119,7 @@ def quantize_jagged_colwise(x, offs, *, stream=None):
     (G, cols) fp32."""
     torch = _torch()
     _require_bf16_cuda(x, 2, "x")
+    _require_offs(offs, x)
     rows, cols = x.shape
     G = offs.numel()
     q = _empty_colmajor_u8(torch, rows, cols, x.device)
@@ -166,6 +178,7 @@ def quantize_jagged_mx_rowwise(x, offs, *, scale_mode: int = MXQ_SCALE_FLOOR, st
     are written."""
     torch = _torch()
     _require_bf16_cuda(x, 2, "x")
+    _require_offs(offs, x)
     rows, cols = x.shape
     G = offs.numel()
     q = _empty_rowmajor_u8(torch, rows, cols, x.device)
@@ -185,6 +198,7 @@ def quantize_jagged_mx_colwise(x, offs, *, scale_mode: int = MXQ_SCALE_FLOOR, st
     written."""
     torch = _torch()
     _require_bf16_cuda(x, 2, "x")
+    _require_offs(offs, x)
     rows, cols = x.shape
     G = offs.numel()
     q = _empty_colmajor_u8(torch, rows, cols, x.device)
