@@ -74,7 +74,8 @@ def _load():
     lib.oracle_quantize_jagged_mx_colwise.argtypes = jmx
     lib.oracle_quantize_blockwise.argtypes = [_vp, _i64, _i64, _i64, _i64, _i32, _i32, _vp,
                                               _i64, _i64, _vp, _i64, _i64]
-    for name in ("oracle_quantize_jagged_rowwise", "oracle_quantize_jagged_colwise",
+    lib.oracle_relayout_mx_scales_grouped.argtypes = [_vp, _i64, _i64, _i64, _vp, _i32, _vp, _vp]
+    for name in ("oracle_relayout_mx_scales_grouped", "oracle_quantize_jagged_rowwise", "oracle_quantize_jagged_colwise",
                  "oracle_quantize_mx_3d_colwise", "oracle_quantize_mx_rowwise",
                  "oracle_quantize_blockwise", "oracle_quantize_jagged_mx_rowwise",
                  "oracle_quantize_jagged_mx_colwise"):
@@ -249,6 +250,34 @@ def quantize_jagged_mx_colwise(x: np.ndarray, offs, mode: str = "floor", canary:
                                                     SCALE_MODES[mode]),
           "jagged_mx_colwise")
     return q, s
+
+
+def mx_tile_capacity(rows: int, extent: int, G: int) -> int:
+    """Upper bound, in bytes, of the re-laid-out scales of ``rows`` rows and
+    G groups covering at most ``extent`` tokens: 256 bytes per tile,
+    ceil(rows/16) row blocks, at most ceil(extent/512) + G - 1 K tiles."""
+    return 256 * ((rows + 15) // 16) * ((extent + 511) // 512 + G - 1) if G > 0 else 0
+
+
+def relayout_mx_scales_grouped(scales: np.ndarray, offs, extent: int, canary: int = 0):
+    """scales: (rows, blocks) uint8 e8m0 array (any strides) whose block b of
+    row r is the jagged MX scale of that row and block, offs: the token
+    groups of the jagged MX quantization that wrote them (covering at most
+    ``extent`` tokens).  For the colwise operand pass the transposed (cols,
+    blocks) view.  Returns the tile bytes (capacity bytes; bytes past the last
+    tile keep ``canary``) and tile_starts (G + 1 int32)."""
+    if scales.dtype != np.uint8 or scales.ndim != 2:
+        raise TypeError("expected a 2-D uint8 array of e8m0 scales")
+    offs = np.ascontiguousarray(np.asarray(offs, dtype=np.int32))
+    rows = scales.shape[0]
+    G = offs.size
+    out = np.full(mx_tile_capacity(rows, extent, G), canary, dtype=np.uint8)
+    starts = np.zeros(G + 1, dtype=np.int32)
+    ss = scales.strides
+    _call(_load().oracle_relayout_mx_scales_grouped(_ptr(scales), rows, ss[0], ss[1], _ptr(offs), G,
+                                                    _ptr(out), _ptr(starts)),
+          "relayout_mx_scales_grouped")
+    return out, starts
 
 
 def quantize_blockwise(x: np.ndarray, block_r: int, block_c: int):

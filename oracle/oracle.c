@@ -30,6 +30,15 @@
  *     spans two groups, a group's last block may be short, and scale entries
  *     are numbered group after group).
  *
+ *   - "[mxfp8 moe training] add CUDA kernel for per-group conversion of scale
+ *     factors to blocked layout", title and stacked PR list: after jagged MX
+ *     quantization with groups along K, each group's e8m0 scales are re-laid
+ *     out for the consumer grouped GEMM.  The page does not print the target
+ *     layout (it is another vendor's MMA layout); the layout written here is
+ *     the scale operand order of the gfx950 scaled MFMA with 16 rows and 128
+ *     K values per instruction (AMD CDNA4 ISA, V_MFMA_SCALE_F32_16X16X128_
+ *     F8F6F4), as stated at oracle_relayout_mx_scales_grouped.
+ *
  * Numeric readings (the pages name the formats but print no formula):
  *   - fp8 is OCP E4M3FN: bias 7, 3 mantissa bits, no infinities, max 448,
  *     codes 0x7F/0xFF are NaN.  Encoding is round-to-nearest-even with
@@ -408,6 +417,65 @@ int oracle_quantize_jagged_mx_colwise(const uint16_t *x, int64_t rows, int64_t c
             }
         }
     }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------ MX scales -> scaled-MFMA scale tiles */
+
+/* Per-group re-layout of jagged MX scales (groups along K) into tiles that a
+ * gfx950 scaled-MFMA grouped GEMM loads as its scale operand.
+ *
+ * The consumer instruction multiplies a 16-row x 128-K operand tile; lane
+ * 16j + i of the wave supplies, in one 32-bit register, the e8m0 scale of row
+ * i and K block j (32 K values) of that tile, and the instruction's op_sel
+ * picks one byte of the register.  Four consecutive K steps therefore share
+ * one register per lane, byte u for step u: a tile here is 16 rows x 16
+ * blocks (512 K values) stored as 64 lane words of 4 bytes, 256 bytes:
+ *
+ *   byte 4 * lane + u of a tile = scale of row i = lane % 16 and block
+ *   4 * u + lane / 16 of the tile (u = 0..3).
+ *
+ * Group g (token range from offs, n_g tokens, nb_g = ceil(n_g / 32) blocks
+ * numbered from B_g as the jagged MX functions number them) gets
+ * RB = ceil(rows / 16) x KT_g = ceil(nb_g / 16) tiles, row-block-major:
+ * tile (rb, kt) is tile number T_g + rb * KT_g + kt, T_g = RB * sum over h < g
+ * of KT_h.  Entries past the last row or past the group's last block are 0.
+ * tile_starts[g] = T_g for g = 0..G (tile_starts[G] = total tiles).
+ *
+ * scales[r * ss_r + b * ss_b] is the scale of row r and block b; for the
+ * colwise operand the "rows" are its columns. */
+int oracle_relayout_mx_scales_grouped(const uint8_t *scales, int64_t rows, int64_t ss_r,
+                                      int64_t ss_b, const int32_t *offs, int32_t G,
+                                      uint8_t *out, int32_t *tile_starts)
+{
+    if (rows < 0 || check_offs_args(G) != ORACLE_OK)
+        return ORACLE_BAD_ARG;
+    const int64_t RB = (rows + 15) / 16;
+    int64_t b0 = 0; /* B_g */
+    int64_t t0 = 0; /* T_g */
+    for (int32_t g = 0; g < G; ++g) {
+        int64_t lo = g == 0 ? 0 : offs[g - 1];
+        int64_t n = offs[g] - lo;
+        if (n < 0)
+            n = 0;
+        const int64_t nb = (n + 31) / 32;
+        const int64_t KT = (nb + 15) / 16;
+        tile_starts[g] = (int32_t)t0;
+        for (int64_t rb = 0; rb < RB; ++rb)
+            for (int64_t kt = 0; kt < KT; ++kt) {
+                uint8_t *tile = out + (t0 + rb * KT + kt) * 256;
+                for (int lane = 0; lane < 64; ++lane)
+                    for (int u = 0; u < 4; ++u) {
+                        const int64_t r = rb * 16 + lane % 16;
+                        const int64_t blk = kt * 16 + 4 * u + lane / 16;
+                        tile[4 * lane + u] =
+                            (r < rows && blk < nb) ? scales[r * ss_r + (b0 + blk) * ss_b] : 0;
+                    }
+            }
+        b0 += nb;
+        t0 += RB * KT;
+    }
+    tile_starts[G] = (int32_t)t0;
     return ORACLE_OK;
 }
 
