@@ -8,7 +8,9 @@ e4m3 + fp32 per-group scales out.  One step = both launches.  Other
 workloads (``--workload``): ``moe_bwd_mx`` (the same operands as jagged
 MXFP8 blocks), ``mx3d`` (E=8 expert weights, 32x1 MXFP8),
 ``mx3d_e{1,2,4,16,64}``, ``mx3d_rceil`` (E=8 with the rceil scale mode),
-``blockwise`` (1x128 activations + 128x128 weights).
+``blockwise`` (1x128 activations + 128x128 weights), ``relayout`` (the
+per-group re-layout of (8192, 32768) e8m0 scales into scaled-MFMA tiles; its
+bytes are scale bytes read plus tile bytes written).
 
 Metric: algorithmic HBM bytes (2 B bf16 read + 1 B e4m3 write + scale bytes
 per launch) divided by time.  Inputs are resident in HBM before the timed
@@ -246,6 +248,44 @@ def build_blockwise(torch, mxq, workloads):
     return [l1, l2], [da, dw, qa, sa, qw, sw], desc, cpu_sample
 
 
+def build_relayout(torch, mxq, workloads):
+    """Per-group re-layout of jagged MX scales into scaled-MFMA scale tiles on
+    the largest scale shape of the per-group conversion benchmarks:
+    (8192, 32768) e8m0 scale columns of 8 MoE-like token groups over 2^20
+    tokens, stored row-major (blocks contiguous)."""
+    import numpy as np
+
+    scales, offs = workloads.relayout_case()
+    rows, cap = scales.shape
+    extent = 1 << 20
+    G = offs.size
+    sizes = np.diff(np.concatenate([[0], offs]))
+    nb = int(sum((int(n) + 31) // 32 for n in sizes))
+    ntiles = ((rows + 15) // 16) * int(sum((int(n) + 511) // 512 for n in sizes))
+    d_s = torch.from_numpy(scales).cuda()
+    d_offs = torch.from_numpy(offs).cuda()
+    tiles = torch.empty(mxq.mx_tile_capacity(rows, extent, G), dtype=torch.uint8, device="cuda")
+    starts = torch.empty(G + 1, dtype=torch.int32, device="cuda")
+    l = Launch(f"relayout_mx_scales ({rows},{nb}) e8m0, {G} groups", "relayout_mx_scales_kernel<0, 4, false>",
+               mxq.mxq_relayout_mx_scales_grouped,
+               (d_s.data_ptr(), rows, cap, 1, d_offs.data_ptr(), G, extent, tiles.data_ptr(),
+                starts.data_ptr()), rows * nb + 256 * ntiles, rows * nb)
+    desc = {"workload": "relayout_scales",
+            "tensors": f"e8m0 scales ({rows},{nb}) row-major -> 16x16-block scaled-MFMA tiles "
+                       f"({ntiles} tiles of 256 B)",
+            "groups": int(G), "group_sizes": [int(v) for v in sizes],
+            "bytes": "scale bytes read + tile bytes written (zero padding included)"}
+
+    def cpu_sample(oracle, n):
+        t0 = time.perf_counter()
+        oracle.relayout_mx_scales_grouped(scales[:n], offs, extent)
+        dt = time.perf_counter() - t0
+        nt = ((n + 15) // 16) * int(sum((int(v) + 511) // 512 for v in sizes))
+        return dt, n * nb + 256 * nt, f"{n} of {rows} rows, all {G} groups"
+
+    return [l], [d_s, d_offs, tiles, starts], desc, cpu_sample
+
+
 def build_copy(torch):
     """Calibration: a plain device-to-device copy of 256 MiB (torch's copy,
     i.e. the runtime's copy kernel).  Its FETCH_SIZE / WRITE_SIZE counters
@@ -279,6 +319,8 @@ def build(name, torch, mxq, workloads):
         return build_mx3d(torch, mxq, workloads, int(name[len("mx3d_e"):]), sweep=True)
     if name == "blockwise":
         return build_blockwise(torch, mxq, workloads)
+    if name == "relayout":
+        return build_relayout(torch, mxq, workloads)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -426,7 +468,7 @@ def main():
         import oracle
 
         n = args.cpu_sample_rows or {"moe_bwd": 4096, "moe_bwd_mx": 2048,
-                                     "blockwise": 2048}.get(args.workload, 256)
+                                     "blockwise": 2048, "relayout": 8192}.get(args.workload, 256)
         print(f"[bench] timing the CPU oracle on a sample (n={n})", file=sys.stderr, flush=True)
         dt, nbytes, what = cpu_sample(oracle, n)
         cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",

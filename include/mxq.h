@@ -196,6 +196,50 @@ mxq_status mxq_quantize_jagged_mx_colwise(const uint16_t *x, int64_t rows, int64
                                           int64_t ss_c, int32_t scale_mode, void *stream);
 
 /*
+ * Per-group re-layout of jagged MX e8m0 scales into the scale-operand tiles
+ * of a gfx950 scaled-MFMA grouped GEMM.  Source: "[mxfp8 moe training] add
+ * CUDA kernel for per-group conversion of scale factors to blocked layout",
+ * title, benchmarks and stacked PR list: after jagged MX quantization with
+ * token groups along K, each group's scales are converted, on the device, to
+ * the layout the grouped GEMM reads.  The page's target is another vendor's
+ * MMA layout and is not printed; the layout here (reading) is the scale
+ * operand order of the gfx950 scaled MFMA with 16 rows x 128 K values of
+ * e4m3 (CDNA4 ISA, V_MFMA_SCALE_F32_16X16X128_F8F6F4): lane 16j + i of a
+ * wave supplies the scale of row i and 32-value K block j in one 32-bit
+ * register whose byte op_sel selects, so one register serves four 128-value
+ * K steps.
+ *
+ * scales  e8m0 bytes of `rows` rows, block b of row r at
+ *         scales[r*ss_r + b*ss_b], blocks numbered as the jagged MX calls
+ *         number them (group g's nb_g = ceil(n_g/32) blocks from B_g).  For
+ *         the rowwise operand pass its (rows, blocks) scales; for the
+ *         colwise operand pass its scales with the columns as rows
+ *         (ss_r = ss_c, ss_b = ss_b of mxq_quantize_jagged_mx_colwise).
+ * offs, num_groups, extent
+ *         the token groups and the token extent given to the jagged MX
+ *         call (offsets are clamped to [0, extent] the same way).
+ * tiles   output, 16-byte aligned, capacity 256 * ceil(rows/16) *
+ *         (ceil(extent/512) + G - 1) bytes.  A tile is 16 rows x 16 blocks
+ *         stored as 64 lane words of 4 bytes:
+ *           byte 4*lane + u = scale of row lane % 16, block 4u + lane / 16
+ *         (tile-local row and block).  Group g owns ceil(rows/16) x
+ *         KT_g = ceil(n_g/512) tiles, tile (rb, kt) at index
+ *         T_g + rb*KT_g + kt, T_g = ceil(rows/16) * sum of KT_h over h < g.
+ *         Entries past the last row or past the group's last block are 0;
+ *         bytes past the last tile are not written.
+ * tile_starts
+ *         output, G + 1 int32 (T_g, and the total at index G), or NULL.
+ * Layouts with a kernel: any strides; ss_b == 1 and ss_r == 1 read whole
+ * 256-byte pieces, others read bytes.
+ * Errors: MXQ_ERR_INVALID_ARG also for negative strides and for a tile
+ * count past INT32_MAX.
+ */
+mxq_status mxq_relayout_mx_scales_grouped(const uint8_t *scales, int64_t rows, int64_t ss_r,
+                                          int64_t ss_b, const int32_t *offs, int32_t num_groups,
+                                          int64_t extent, uint8_t *tiles, int32_t *tile_starts,
+                                          void *stream);
+
+/*
  * Blockwise ("groupwise") fp8 quantization with one fp32 multiplier per
  * block_r x block_c block.  Source: "[fp8 blockwise] load 2d chunks for
  * groupwise quant to enable coalesced gmem accesses", body: 1 x blocksize

@@ -20,15 +20,17 @@ from ._capi import (MXQ_ERR_INVALID_ARG, MXQ_ERR_LAUNCH, MXQ_ERR_UNSUPPORTED, MX
                     mxq_abi_version, mxq_debug_cast_e4m3, mxq_quantize_blockwise,
                     mxq_quantize_jagged_colwise, mxq_quantize_jagged_mx_colwise,
                     mxq_quantize_jagged_mx_rowwise, mxq_quantize_jagged_rowwise,
-                    mxq_quantize_mx_3d_colwise, mxq_quantize_mx_rowwise)
+                    mxq_quantize_mx_3d_colwise, mxq_quantize_mx_rowwise,
+                    mxq_relayout_mx_scales_grouped)
 
 __all__ = [
     "quantize_jagged_rowwise", "quantize_jagged_colwise", "quantize_mx_3d_colwise",
     "quantize_mx_rowwise", "quantize_jagged_mx_rowwise", "quantize_jagged_mx_colwise",
-    "jagged_mx_scale_capacity", "quantize_blockwise", "debug_cast_e4m3", "MXQError",
+    "jagged_mx_scale_capacity", "relayout_mx_scales_grouped", "mx_tile_capacity",
+    "quantize_blockwise", "debug_cast_e4m3", "MXQError",
     "mxq_quantize_jagged_rowwise", "mxq_quantize_jagged_colwise", "mxq_quantize_mx_3d_colwise",
     "mxq_quantize_mx_rowwise", "mxq_quantize_jagged_mx_rowwise", "mxq_quantize_jagged_mx_colwise",
-    "mxq_quantize_blockwise", "mxq_debug_cast_e4m3",
+    "mxq_relayout_mx_scales_grouped", "mxq_quantize_blockwise", "mxq_debug_cast_e4m3",
     "mxq_abi_version", "LibraryMissing",
 ]
 
@@ -209,6 +211,38 @@ def quantize_jagged_mx_colwise(x, offs, *, scale_mode: int = MXQ_SCALE_FLOOR, st
         _stream(x, stream))
     _check(code, "mxq_quantize_jagged_mx_colwise")
     return q, s
+
+
+def mx_tile_capacity(rows: int, extent: int, num_groups: int) -> int:
+    """Bytes of scaled-MFMA scale tiles that a re-layout of ``rows`` rows and
+    ``num_groups`` groups over ``extent`` tokens may write:
+    256 * ceil(rows/16) * (ceil(extent/512) + num_groups - 1)."""
+    return 256 * ((rows + 15) // 16) * ((extent + 511) // 512 + num_groups - 1)
+
+
+def relayout_mx_scales_grouped(scales, offs, extent: int, *, stream=None):
+    """Per-group re-layout of jagged MX scales into scaled-MFMA scale tiles.
+    ``scales``: (rows, blocks) uint8 e8m0 tensor, any strides (for the colwise
+    operand pass the (cols, blocks) transposed view of its scales), ``offs``
+    and ``extent``: the groups and the token extent of the jagged MX call.
+    Returns ``(tiles, tile_starts)``: tiles a uint8 tensor of
+    mx_tile_capacity bytes (tile_starts[G] * 256 of them written),
+    tile_starts (G + 1,) int32."""
+    torch = _torch()
+    if scales.dtype != torch.uint8 or scales.dim() != 2 or not scales.is_cuda:
+        raise TypeError(f"scales must be a 2-D uint8 CUDA tensor, got {scales.dtype} "
+                        f"{tuple(scales.shape)} on {scales.device}")
+    _require_offs(offs, scales)
+    rows = scales.shape[0]
+    G = offs.numel()
+    tiles = torch.empty(max(mx_tile_capacity(rows, extent, G), 16), dtype=torch.uint8,
+                        device=scales.device)
+    starts = torch.empty(G + 1, dtype=torch.int32, device=scales.device)
+    code = mxq_relayout_mx_scales_grouped(
+        scales.data_ptr(), rows, scales.stride(0), scales.stride(1), offs.data_ptr(), G, extent,
+        tiles.data_ptr(), starts.data_ptr(), _stream(scales, stream))
+    _check(code, "mxq_relayout_mx_scales_grouped")
+    return tiles, starts
 
 
 def quantize_blockwise(x, block_r: int, block_c: int, *, stream=None):

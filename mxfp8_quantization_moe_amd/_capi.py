@@ -43,6 +43,7 @@ SIGNATURES = {
                                        _vp, _i64, _i64, _i32, _vp],
     "mxq_quantize_jagged_mx_colwise": [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _i64, _i64,
                                        _vp, _i64, _i64, _i32, _vp],
+    "mxq_relayout_mx_scales_grouped": [_vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp, _vp, _vp],
     "mxq_quantize_blockwise": [_vp, _i64, _i64, _i64, _i64, _i32, _i32, _vp, _i64, _i64, _vp,
                                _i64, _i64, _vp],
     "mxq_debug_cast_e4m3": [_vp, _i64, _vp, _vp],
@@ -94,5 +95,6 @@ mxq_quantize_mx_3d_colwise = _fwd("mxq_quantize_mx_3d_colwise")
 mxq_quantize_mx_rowwise = _fwd("mxq_quantize_mx_rowwise")
 mxq_quantize_jagged_mx_rowwise = _fwd("mxq_quantize_jagged_mx_rowwise")
 mxq_quantize_jagged_mx_colwise = _fwd("mxq_quantize_jagged_mx_colwise")
+mxq_relayout_mx_scales_grouped = _fwd("mxq_relayout_mx_scales_grouped")
 mxq_quantize_blockwise = _fwd("mxq_quantize_blockwise")
 mxq_debug_cast_e4m3 = _fwd("mxq_debug_cast_e4m3")

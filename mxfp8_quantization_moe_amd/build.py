@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmxq.so")
 SOURCES = [os.path.join(CSRC, "api.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("mxq_device.hpp", "wave_ops.hpp", "jagged_kernels.hpp",
-                                            "jagged_mx_kernels.hpp", "block_kernels.hpp", "group_tables.hpp")] + [os.path.join(ROOT, "include", "mxq.h")]
+                                            "jagged_mx_kernels.hpp", "block_kernels.hpp", "group_tables.hpp",
+                                            "relayout_kernels.hpp")] + [os.path.join(ROOT, "include", "mxq.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

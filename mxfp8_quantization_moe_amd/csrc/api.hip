@@ -10,6 +10,7 @@
 #include "block_kernels.hpp"
 #include "jagged_kernels.hpp"
 #include "jagged_mx_kernels.hpp"
+#include "relayout_kernels.hpp"
 
 namespace {
 
@@ -180,6 +181,32 @@ mxq_status run_jagged_mx_cols(const uint16_t *x, int64_t rows, int64_t cols, int
     jagged_mx_colwise_kernel<<<dim3((unsigned)(ntr * tiles_c)), dim3(kJmxThreads), 0, st>>>(
         x, ldx, (int)rows, (int)cols, offs, G, q, ldq, scales, ss_b, ss_c, (int)tiles_c,
         rceil ? 1 : 0);
+    return launch_status();
+}
+
+template <int LAYOUT, int SEG, bool XCD>
+mxq_status run_relayout(const uint8_t *scales, int64_t rows, int64_t ss_r, int64_t ss_b,
+                        const int32_t *offs, int G, int64_t extent, uint8_t *tiles,
+                        int32_t *tile_starts, hipStream_t st)
+{
+    using SH = RelayoutShape<LAYOUT, SEG>;
+    const int64_t rb = (rows + 15) / 16;
+    const int64_t rc = (rb + SH::CR - 1) / SH::CR;
+    const int64_t nchunk = std::max<int64_t>(1, (extent + (1 << SH::SHC) - 1) / (1 << SH::SHC) + G - 1);
+    const int64_t nitems = rc * nchunk;
+    if (nitems == 0 && tile_starts == nullptr)
+        return MXQ_OK;
+    // at least one workgroup (workgroup 0 writes tile_starts); a multiple of
+    // 8 for the XCD-ordered item mapping
+    int64_t grid = std::max<int64_t>(nitems, 1);
+    if (XCD)
+        grid = (grid + 7) / 8 * 8;
+    if (grid > INT32_MAX)
+        return MXQ_ERR_INVALID_ARG;
+    relayout_mx_scales_kernel<LAYOUT, SEG, XCD>
+        <<<dim3((unsigned)grid), dim3(kRelayoutThreads), relayout_lds_bytes<LAYOUT, SEG>(G), st>>>(
+            scales, ss_r, ss_b, (int)rows, (int)extent, offs, G, tiles, tile_starts, (int)nchunk,
+            (int)nitems);
     return launch_status();
 }
 
@@ -369,6 +396,36 @@ mxq_status mxq_quantize_jagged_mx_colwise(const uint16_t *x, int64_t rows, int64
                                   ss_b, rc, st);
     }
     return MXQ_ERR_UNSUPPORTED;
+}
+
+mxq_status mxq_relayout_mx_scales_grouped(const uint8_t *scales, int64_t rows, int64_t ss_r,
+                                          int64_t ss_b, const int32_t *offs, int32_t num_groups,
+                                          int64_t extent, uint8_t *tiles, int32_t *tile_starts,
+                                          void *stream)
+{
+    const int32_t G = num_groups;
+    if (rows < 0 || extent < 0 || G < 1 || G > MXQ_MAX_GROUPS || !offs)
+        return MXQ_ERR_INVALID_ARG;
+    if (rows > INT32_MAX || extent > INT32_MAX || ss_r < 0 || ss_b < 0)
+        return MXQ_ERR_INVALID_ARG;
+    // tile numbers are int32 (tile_starts): bound the largest one
+    const int64_t max_tiles = ((rows + 15) / 16) * ((extent + 511) / 512 + G - 1);
+    if (max_tiles > INT32_MAX)
+        return MXQ_ERR_INVALID_ARG;
+    if (rows > 0 && extent > 0 && (!scales || !tiles))
+        return MXQ_ERR_INVALID_ARG;
+    if ((tiles && !aligned16(tiles)) ||
+        (tile_starts && (reinterpret_cast<uintptr_t>(tile_starts) & 3u) != 0))
+        return MXQ_ERR_INVALID_ARG;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (ss_b == 1)
+        return run_relayout<0, 4, false>(scales, rows, ss_r, ss_b, offs, G, extent, tiles,
+                                        tile_starts, st);
+    if (ss_r == 1)
+        return run_relayout<1, 4, true>(scales, rows, ss_r, ss_b, offs, G, extent, tiles,
+                                        tile_starts, st);
+    return run_relayout<2, 4, false>(scales, rows, ss_r, ss_b, offs, G, extent, tiles, tile_starts,
+                                     st);
 }
 
 mxq_status mxq_quantize_blockwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t sx_r,

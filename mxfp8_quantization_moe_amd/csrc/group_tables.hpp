@@ -166,6 +166,46 @@ __device__ __forceinline__ void wave_group_tables(const int32_t *__restrict__ of
     }
 }
 
+// wave_group_tables with a third prefix: units of 2^SHC elements into s_pc
+// (which may alias s_pb when SHC == SHB).  The caller follows with a barrier.
+template <int SHA, int SHB, int SHC>
+__device__ __forceinline__ void wave_group_tables3(const int32_t *__restrict__ offs, int G,
+                                                   int extent, int *s_end, int *s_pa, int *s_pb,
+                                                   int *s_pc)
+{
+    const int lane = threadIdx.x & 63;
+    const bool valid = lane < G;
+    int hi = valid ? offs[lane] : extent;
+    hi = hi < 0 ? 0 : (hi > extent ? extent : hi);
+    int lo = __shfl_up(hi, 1, 64);
+    lo = lane == 0 ? 0 : lo;
+    const int n = valid && hi > lo ? hi - lo : 0;
+    const int ua = units_of<SHA>(n), ub = units_of<SHB>(n), uc = units_of<SHC>(n);
+    int ia = ua, ib = ub, ic = uc;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int ya = __shfl_up(ia, d, 64);
+        const int yb = __shfl_up(ib, d, 64);
+        const int yc = __shfl_up(ic, d, 64);
+        if (lane >= d) {
+            ia += ya;
+            ib += yb;
+            ic += yc;
+        }
+    }
+    if (valid) {
+        s_end[lane] = hi;
+        s_pa[lane] = ia - ua;
+        s_pb[lane] = ib - ub;
+        s_pc[lane] = ic - uc;
+    }
+    if (lane == G - 1) {
+        s_pa[G] = ia;
+        s_pb[G] = ib;
+        s_pc[G] = ic;
+    }
+}
+
 // the slot whose work covers index j: s_pre[s] <= j < s_pre[s+1], given
 // 0 <= j < s_pre[G] (slots with no work are skipped)
 __device__ __forceinline__ int find_slot(const int *s_pre, int G, int j)

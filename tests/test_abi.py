@@ -137,3 +137,27 @@ def test_jagged_mx_rejects_bad_arguments(lib):
     assert call(cw, sq_r=1, sq_c=16, cols=12, sx_r=16) == 1   # cols % 8
     assert call(cw, sq_r=64, sq_c=1) == 2          # row-major out from row-major in: no kernel
     assert call(cw, rows=0, sq_r=1, sq_c=16) == 0
+
+
+def test_relayout_rejects_bad_arguments(lib):
+    fn = lib.mxq_relayout_mx_scales_grouped
+    ok_args = dict(s=A, rows=32, ss_r=40, ss_b=1, offs=A, G=2, extent=1000, tiles=A, starts=A)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return fn(a["s"], a["rows"], a["ss_r"], a["ss_b"], a["offs"], a["G"], a["extent"],
+                  a["tiles"], a["starts"], None)
+
+    assert call(G=0) == 1
+    assert call(G=4097) == 1
+    assert call(offs=0) == 1
+    assert call(rows=-1) == 1
+    assert call(extent=-5) == 1
+    assert call(ss_r=-40) == 1
+    assert call(s=0) == 1
+    assert call(tiles=0) == 1
+    assert call(tiles=MIS) == 1                    # tiles must be 16-byte aligned
+    assert call(starts=A + 2) == 1                 # tile_starts must be 4-byte aligned
+    assert call(rows=1 << 31) == 1
+    assert call(rows=(1 << 31) - 16, extent=(1 << 31) - 1) == 1   # tile numbers past int32
+    assert call(rows=0, starts=0) == 0             # nothing to write: no launch

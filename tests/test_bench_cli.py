@@ -20,6 +20,6 @@ def test_workload_table_names_every_configuration():
     import bench
 
     src = open(os.path.join(ROOT, "bench.py")).read()
-    for name in ("moe_bwd", "moe_bwd_mx", "mx3d", "mx3d_rceil", "blockwise", "copy"):
+    for name in ("moe_bwd", "moe_bwd_mx", "mx3d", "mx3d_rceil", "blockwise", "relayout", "copy"):
         assert f'"{name}"' in src, name
     assert callable(bench.build)

@@ -1,0 +1,228 @@
+"""GPU parity of the per-group scale re-layout against the CPU oracle, byte
+for byte: tiles, tile starts, and the bytes past the last tile (canary),
+for the three input layouts (scales contiguous along blocks, along rows, or
+neither), base pointers off every 4-byte alignment, ragged row counts, empty
+groups, tokens past the last group, groups longer than one 8192-token item,
+G on both sides of the one-wave table limit, and the full (8192, 32768)
+scale shape.  Then the consumer side: a grouped GEMM on the real gfx950
+scaled MFMA that reads the tiles reproduces the grouped GEMM of the
+dequantized jagged MX operands, and agrees with the CPU model of the
+instruction."""
+import numpy as np
+import pytest
+import torch
+
+import consumer
+import mxfp8_quantization_moe_amd as mxq
+import oracle
+import workloads
+from gpu_helpers import CANARY, DEV, i32_dev, random_offsets
+from scaled_mfma_model import dequantized_gemm
+
+pytestmark = pytest.mark.gpu
+
+
+def relayout(scales_dev, offs, extent):
+    """Direct C-ABI call with canary-filled outputs; returns (tiles up to
+    capacity, tile_starts) as numpy."""
+    rows = scales_dev.shape[0]
+    G = len(offs)
+    cap = mxq.mx_tile_capacity(rows, extent, G)
+    tiles = torch.full((max(cap, 16),), CANARY, dtype=torch.uint8, device=DEV)
+    starts = torch.full((G + 1,), -7, dtype=torch.int32, device=DEV)
+    d_offs = i32_dev(offs)
+    code = mxq.mxq_relayout_mx_scales_grouped(
+        scales_dev.data_ptr(), rows, scales_dev.stride(0), scales_dev.stride(1), d_offs.data_ptr(),
+        G, extent, tiles.data_ptr(), starts.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert code == 0, mxq._capi.status_string(code)
+    torch.cuda.synchronize()
+    return tiles.cpu().numpy()[:cap], starts.cpu().numpy()
+
+
+def check(scales_np, scales_dev, offs, extent, what):
+    t, s = relayout(scales_dev, offs, extent)
+    ot, os_ = oracle.relayout_mx_scales_grouped(scales_np, offs, extent, canary=CANARY)
+    assert np.array_equal(s, os_), f"{what}: tile starts {s} vs {os_}"
+    if not np.array_equal(t, ot):
+        bad = np.flatnonzero(t != ot)
+        raise AssertionError(f"{what}: {bad.size} tile bytes differ, first at {bad[0]} "
+                             f"(tile {bad[0] // 256}, lane {(bad[0] % 256) // 4}, byte {bad[0] % 4}): "
+                             f"{t[bad[0]]} vs {ot[bad[0]]}")
+
+
+CASES = [
+    # rows, extent, G, multiple, short tail, seed
+    (37, 3000, 4, 1, 5, 1),
+    (16, 512, 1, 1, 0, 2),
+    (1, 20000, 7, 16, 0, 3),
+    (200, 40000, 3, 32, 100, 4),        # groups spanning several 8192-token items
+    (33, 70000, 300, 1, 9, 5),          # G > 64: workgroup-wide tables
+    (5, 1000, 64, 1, 0, 6),             # G = 64: one-wave tables
+    (5, 1000, 65, 1, 0, 7),
+    (300, 6000, 8, 512, 0, 8),          # every group a whole number of tiles
+]
+
+
+@pytest.mark.parametrize("rows,extent,G,mult,tail,seed", CASES)
+def test_block_contiguous_scales(rows, extent, G, mult, tail, seed):
+    offs = random_offsets(extent, G, seed, multiple=mult, short_tail=tail)
+    cap = oracle.jagged_mx_scale_capacity(extent, G)
+    s = workloads.e8m0_bytes((rows, cap), 800 + seed)
+    check(s, torch.from_numpy(s).to(DEV), offs, extent, "ss_b == 1")
+
+
+@pytest.mark.parametrize("shift", [1, 2, 3])
+def test_unaligned_base_and_pitch(shift):
+    """Base pointer and row pitch off 4-byte alignment: each row's span
+    starts at a different byte of its dword."""
+    rows, extent, G = 45, 9000, 5
+    offs = random_offsets(extent, G, 20 + shift, short_tail=3)
+    cap = oracle.jagged_mx_scale_capacity(extent, G)
+    big = workloads.e8m0_bytes((rows, cap + shift + 2), 830 + shift)
+    view = torch.from_numpy(big).to(DEV)[:, shift:shift + cap]
+    check(big[:, shift:shift + cap], view, offs, extent, f"shift {shift}")
+
+
+@pytest.mark.parametrize("cols,extent,G,mult,tail,seed", [
+    (24, 1300, 3, 1, 50, 11),
+    (300, 9000, 6, 16, 0, 12),
+    (16, 512, 1, 1, 0, 13),
+    (4096, 16384, 8, 16, 0, 14),        # the MoE x operand's scales
+    (77, 3000, 100, 1, 7, 15),
+])
+def test_row_contiguous_scales(cols, extent, G, mult, tail, seed):
+    """The colwise operand: scales stored (blocks, cols) row-major, passed as
+    the (cols, blocks) transposed view (ss_r == 1)."""
+    offs = random_offsets(extent, G, seed, multiple=mult, short_tail=tail)
+    cap = oracle.jagged_mx_scale_capacity(extent, G)
+    s = workloads.e8m0_bytes((cap, cols), 840 + seed)
+    view = torch.from_numpy(s).to(DEV).t()
+    check(s.T, view, offs, extent, "ss_r == 1")
+
+
+def test_other_strides():
+    rows, extent, G = 21, 5000, 4
+    offs = random_offsets(extent, G, 31, short_tail=2)
+    cap = oracle.jagged_mx_scale_capacity(extent, G)
+    big = workloads.e8m0_bytes((rows, 2 * cap), 850)
+    view = torch.from_numpy(big).to(DEV)[:, ::2]
+    check(big[:, ::2], view, offs, extent, "ss_b == 2")
+
+
+def test_empty_extents():
+    # no rows: only tile_starts (all zero) are written
+    t, s = relayout(torch.zeros((0, 40), dtype=torch.uint8, device=DEV), [100, 300], 300)
+    assert t.size == 0 and list(s) == [0, 0, 0]
+    # no tokens: no tiles
+    z = torch.zeros((20, 8), dtype=torch.uint8, device=DEV)
+    t, s = relayout(z, [0, 0, 0], 0)
+    assert list(s) == [0, 0, 0, 0]
+    # offsets past the extent are clamped as in the jagged MX calls
+    s_np = workloads.e8m0_bytes((20, 40), 860)
+    t, st = relayout(torch.from_numpy(s_np).to(DEV), [300, 5000], 1000)
+    ot, ost = oracle.relayout_mx_scales_grouped(s_np, [300, 1000], 1000, canary=CANARY)
+    assert np.array_equal(st, ost) and np.array_equal(t, ot[:t.size])
+
+
+def test_full_scale_shape():
+    """(8192, 32768) scale columns, 8 MoE-like groups over 2^20 tokens."""
+    s, offs = workloads.relayout_case()
+    check(s, torch.from_numpy(s).to(DEV), offs, 1 << 20, "relayout (8192, 32768)")
+
+
+# ------------------------------------------------------ the consumer side
+
+def _spread(shape, seed, axis):
+    g = workloads.rng(seed)
+    v = g.standard_normal(shape).astype(np.float32)
+    n, other = shape[axis], shape[1 - axis]
+    e = g.integers(-8, 9, size=(other, (n + 7) // 8)).repeat(8, axis=1)[:, :n]
+    v *= np.exp2(e if axis == 1 else e.T).astype(np.float32)
+    return workloads.to_bf16_bits(v)
+
+
+def _consume(qa, ta, sta, qb, tb, stb, offs, rows, cols):
+    d = {k: torch.from_numpy(np.ascontiguousarray(v)).to(DEV)
+         for k, v in dict(qa=qa, ta=ta, sta=sta, qb=qb, tb=tb, stb=stb,
+                          offs=np.asarray(offs, np.int32)).items()}
+    G = len(offs)
+    out = torch.zeros((G, rows, cols), dtype=torch.float32, device=DEV)
+    rc = consumer.load().consumer_grouped_gemm(
+        d["qa"].data_ptr(), qa.shape[1], rows, d["qb"].data_ptr(), qb.shape[1], cols,
+        d["ta"].data_ptr(), d["sta"].data_ptr(), d["tb"].data_ptr(), d["stb"].data_ptr(),
+        d["offs"].data_ptr(), G, out.data_ptr())
+    assert rc == 0
+    return out.cpu().numpy().astype(np.float64)
+
+
+# The instruction does not accumulate like sequential IEEE fp32 additions:
+# against exact float64 sums these cases are off by up to 6.7e-5 (~2^-14) of
+# the sum of |terms| (measured), so the bound is 2^-11 of that sum.  A scale
+# taken from the wrong block, row or K step changes a block's terms by a
+# factor 2^k (k != 0 for almost every block of these inputs), an error above
+# 2^-7 of the sum.
+REL = 2.0 ** -11
+
+
+def _abs_terms(qa, sa, qb, sb, offs):
+    strip = lambda q: np.where(q >= 0x80, q - 0x80, q).astype(np.uint8)
+    return dequantized_gemm(strip(qa), sa, strip(qb), sb, offs)
+
+
+def _worst(got, want, absref):
+    return max(float(np.max(np.abs(x - y) / (a + 1e-30))) for x, y, a in zip(got, want, absref))
+
+
+def _tolerance_ok(got, want, qa, sa, qb, sb, offs):
+    w = _worst(got, want, _abs_terms(qa, sa, qb, sb, offs))
+    print(f"worst error / sum|terms| = {w:.3e} (bound {REL:.3e})")
+    assert w <= REL, f"worst error {w:.3e} of the sum of |terms| (bound {REL:.3e})"
+
+
+@pytest.mark.parametrize("rows,cols,extent,offs,seed", [
+    (40, 24, 1300, [700, 700, 1250], 1),
+    (16, 16, 1100, [33, 545, 1100], 2),
+    (48, 32, 5000, [1000, 1000, 2100, 4999], 3),
+])
+def test_scaled_mfma_reads_the_oracle_tiles(rows, cols, extent, offs, seed):
+    """The oracle's quantized operands and re-laid-out scales, consumed by
+    the real instruction, give the dequantized grouped GEMM."""
+    a = _spread((rows, extent), seed, 1)
+    x = _spread((extent, cols), seed + 1, 0)
+    qa, sa = oracle.quantize_jagged_mx_rowwise(a, offs)
+    qx, sx = oracle.quantize_jagged_mx_colwise(x, offs)
+    qb, sb = np.ascontiguousarray(qx.T), sx.T
+    ta, sta = oracle.relayout_mx_scales_grouped(sa, offs, extent)
+    tb, stb = oracle.relayout_mx_scales_grouped(sb, offs, extent)
+    got = _consume(qa, ta, sta, qb, tb, stb, offs, rows, cols)
+    want = dequantized_gemm(qa, sa, qb, sb, offs)
+    _tolerance_ok(got, want, qa, sa, qb, sb, offs)
+    # the same check sees a planted layout mistake: the four bytes of every
+    # lane word reversed (K steps of a tile swapped) in A's tiles
+    bad = ta.reshape(-1, 4)[:, ::-1].reshape(-1).copy()
+    got_bad = _consume(qa, bad, sta, qb, tb, stb, offs, rows, cols)
+    assert _worst(got_bad, want, _abs_terms(qa, sa, qb, sb, offs)) > 2.0 ** -7
+
+
+def test_scaled_mfma_end_to_end_through_the_library():
+    """Jagged MX quantization and re-layout on the device, consumed by the
+    scaled MFMA: the same grouped GEMM as the oracle's operands give."""
+    rows, cols, extent = 64, 48, 3000
+    offs = [512, 512, 1700, 2990]
+    a = _spread((rows, extent), 9, 1)
+    x = _spread((extent, cols), 10, 0)
+    d_offs = i32_dev(offs)
+    to_dev = lambda b: torch.from_numpy(b.view(np.int16)).to(DEV).view(torch.bfloat16)
+    qa, sa = mxq.quantize_jagged_mx_rowwise(to_dev(a), d_offs)
+    qx, sx = mxq.quantize_jagged_mx_colwise(to_dev(x), d_offs)
+    ta, sta = mxq.relayout_mx_scales_grouped(sa, d_offs, extent)
+    tb, stb = mxq.relayout_mx_scales_grouped(sx.t(), d_offs, extent)
+    qa_np = qa.view(torch.uint8).cpu().numpy()
+    qb_np = np.ascontiguousarray(qx.view(torch.uint8).cpu().numpy().T)
+    got = _consume(qa_np, ta.cpu().numpy(), sta.cpu().numpy(), qb_np, tb.cpu().numpy(),
+                   stb.cpu().numpy(), offs, rows, cols)
+    oqa, osa = oracle.quantize_jagged_mx_rowwise(a, offs)
+    oqx, osx = oracle.quantize_jagged_mx_colwise(x, offs)
+    oqb, osb = np.ascontiguousarray(oqx.T), osx.T
+    want = dequantized_gemm(oqa, osa, oqb, osb, offs)
+    _tolerance_ok(got, want, oqa, osa, oqb, osb, offs)

@@ -19,6 +19,9 @@ page, and the token-grouped operands of the jagged scaling pages):
 * ``mx3d_sweep`` the same with 1% of 32x1 blocks zeroed and 1% scaled 2^20.
 * ``blockwise`` act (8192, 4096) and W (4096, 4096), N(0,1) with 1/8 of the
               columns Student-t(3).
+* ``relayout`` e8m0 scale bytes (8192, 32768 + 7) (uniform codes 0..254) for
+              8 MoE-like token groups over 2^20 tokens: the largest scale
+              shape of the per-group scale conversion benchmarks.
 * ``large``   tensors of more than 2^31 elements (64-bit indexing checks),
               N(0,1) drawn directly on the GPU by torch's seeded Philox
               generator (too large to draw on the host in a test); the
@@ -191,6 +194,25 @@ def blockwise_weight() -> np.ndarray:
 
 
 # ----------------------------------------------------------- byte accounting
+
+RELAYOUT_SEEDS = dict(offs=6101, scales=6102)
+
+
+def e8m0_bytes(shape, seed) -> np.ndarray:
+    """Random e8m0 scale bytes (codes 0..254; 255 is the NaN code)."""
+    return rng(seed).integers(0, 255, size=shape, dtype=np.uint8)
+
+
+def relayout_case(rows: int = 8192, tokens: int = 1 << 20, groups: int = 8):
+    """Scales of ``rows`` rows for jagged MX blocks over ``tokens`` tokens in
+    ``groups`` MoE-like token groups (offsets_moe: multiples of 16, one empty
+    group, one long group): returns (scales (rows, capacity) uint8, offs).
+    The default is the largest scale shape of the per-group conversion
+    benchmarks, (8192, 32768) scale columns."""
+    offs = offsets_moe(RELAYOUT_SEEDS["offs"], tokens=tokens, groups=groups)
+    cap = (tokens + 31) // 32 + groups - 1
+    return e8m0_bytes((rows, cap), RELAYOUT_SEEDS["scales"]), offs
+
 
 def algorithmic_bytes(numel: int, scale_bytes: int) -> int:
     """bf16 read + e4m3 write + scale write (offsets excluded)."""
