@@ -18,6 +18,9 @@ int oracle_quantize_jagged_rowwise(const uint16_t *x, int64_t rows, int64_t cols
                                    int64_t sx_c, const int32_t *offs, int32_t G, uint8_t *q,
                                    int64_t sq_r, int64_t sq_c, float *scales, int64_t ss_r,
                                    int64_t ss_g);
+int oracle_relayout_mx_scales_grouped(const uint8_t *scales, int64_t rows, int64_t ss_r,
+                                      int64_t ss_b, const int32_t *offs, int32_t G, uint8_t *out,
+                                      int32_t *tile_starts);
 int oracle_quantize_mx_3d_colwise(const uint16_t *w, int64_t E, int64_t N, int64_t K, int64_t sw_e,
                                   int64_t sw_n, int64_t sw_k, uint8_t *q, int64_t sq_e,
                                   int64_t sq_n, int64_t sq_k, uint8_t *scales, int64_t ss_e,
@@ -141,6 +144,47 @@ int main(void)
         free(oq);
         free(hs);
         free(os);
+    }
+
+    /* scale re-layout: (rows, blocks) e8m0 bytes, 3 groups over 5000 tokens */
+    {
+        const int64_t rows = 40, extent = 5000, G = 3;
+        const int32_t offs[3] = {1700, 1700, 4990};
+        const int64_t nbcap = (extent + 31) / 32 + G - 1;
+        const size_t ns = (size_t)(rows * nbcap);
+        const size_t cap = (size_t)(256 * ((rows + 15) / 16) * ((extent + 511) / 512 + G - 1));
+        uint8_t *hs = malloc(ns), *ht = malloc(cap), *ot = malloc(cap);
+        int32_t hst[4], ost[4];
+        for (size_t i = 0; i < ns; ++i)
+            hs[i] = (uint8_t)(next_bf16(&st) % 255u);
+        void *ds, *dt, *dst, *doffs;
+        CHECK_HIP(hipMalloc(&ds, ns));
+        CHECK_HIP(hipMalloc(&dt, cap));
+        CHECK_HIP(hipMalloc(&dst, sizeof hst));
+        CHECK_HIP(hipMalloc(&doffs, sizeof offs));
+        CHECK_HIP(hipMemcpy(ds, hs, ns, hipMemcpyHostToDevice));
+        CHECK_HIP(hipMemcpy(doffs, offs, sizeof offs, hipMemcpyHostToDevice));
+        CHECK_HIP(hipMemset(dt, 0xA5, cap));
+        mxq_status r = mxq_relayout_mx_scales_grouped(ds, rows, nbcap, 1, doffs, (int32_t)G, extent,
+                                                      dt, dst, NULL);
+        if (r != MXQ_OK) {
+            fprintf(stderr, "relayout: %s\n", mxq_status_string(r));
+            return 1;
+        }
+        CHECK_HIP(hipDeviceSynchronize());
+        CHECK_HIP(hipMemcpy(ht, dt, cap, hipMemcpyDeviceToHost));
+        CHECK_HIP(hipMemcpy(hst, dst, sizeof hst, hipMemcpyDeviceToHost));
+        memset(ot, 0xA5, cap);
+        oracle_relayout_mx_scales_grouped(hs, rows, nbcap, 1, offs, (int32_t)G, ot, ost);
+        ok &= same(hst, ost, sizeof hst, "relayout tile starts");
+        ok &= same(ht, ot, cap, "relayout tiles");
+        CHECK_HIP(hipFree(ds));
+        CHECK_HIP(hipFree(dt));
+        CHECK_HIP(hipFree(dst));
+        CHECK_HIP(hipFree(doffs));
+        free(hs);
+        free(ht);
+        free(ot);
     }
 
     /* host-side validation: a bad argument returns before any launch */

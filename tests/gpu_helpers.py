@@ -214,3 +214,21 @@ def random_offsets(extent, G, seed, multiple=1, empties=1, short_tail=0):
             offs[j] = offs[j - 1]
     offs = np.maximum.accumulate(offs)
     return offs.astype(np.int32)
+
+
+def relayout(scales_dev, offs, extent, stream=None):
+    """Direct C-ABI call of the scale re-layout with canary-filled outputs;
+    returns (tiles up to capacity, tile_starts) as numpy."""
+    rows = scales_dev.shape[0]
+    G = len(offs)
+    cap = mxq.mx_tile_capacity(rows, extent, G)
+    tiles = torch.full((max(cap, 16),), CANARY, dtype=torch.uint8, device=DEV)
+    starts = torch.full((G + 1,), -7, dtype=torch.int32, device=DEV)
+    d_offs = i32_dev(offs)
+    st = stream if stream is not None else torch.cuda.current_stream()
+    code = mxq.mxq_relayout_mx_scales_grouped(
+        scales_dev.data_ptr(), rows, scales_dev.stride(0), scales_dev.stride(1), d_offs.data_ptr(),
+        G, extent, tiles.data_ptr(), starts.data_ptr(), st.cuda_stream)
+    assert code == 0, mxq._capi.status_string(code)
+    st.synchronize()
+    return tiles.cpu().numpy()[:cap], starts.cpu().numpy()

@@ -1,7 +1,8 @@
 """The entry points under HIP graph capture: every call of one MoE backward
-step plus the MX and blockwise calls is captured into one graph, which is
-replayed several times with unrelated eager work and synchronisations in
-between; every replay must reproduce the eager outputs byte for byte.
+step plus the MX, blockwise and scale re-layout calls is captured into one
+graph, which is replayed several times with unrelated eager work and
+synchronisations in between; every replay must reproduce the eager outputs
+byte for byte.
 Nothing in the library allocates or records a memset, so capture needs no
 special entry point."""
 import numpy as np
@@ -36,6 +37,8 @@ def _calls(x_row, x_col, offs, w3, act):
     nb = mxq.jagged_mx_scale_capacity(R2, G)
     outs["q5"] = torch.full((R2 * C2,), 0xA5, dtype=torch.uint8, device=dev)
     outs["s5"] = torch.full((nb * C2,), 0xA5, dtype=torch.uint8, device=dev)
+    outs["t6"] = torch.full((mxq.mx_tile_capacity(C2, R2, G),), 0xA5, dtype=torch.uint8, device=dev)
+    outs["st6"] = torch.full((G + 1,), -1, dtype=torch.int32, device=dev)
     o = outs
     calls = [
         (mxq.mxq_quantize_jagged_rowwise,
@@ -53,6 +56,11 @@ def _calls(x_row, x_col, offs, w3, act):
         (mxq.mxq_quantize_jagged_mx_colwise,
          (x_col.data_ptr(), R2, C2, C2, 1, offs.data_ptr(), G, o["q5"].data_ptr(), 1, R2,
           o["s5"].data_ptr(), C2, 1, 1)),
+        # the scales just written, re-laid out for the scaled-MFMA consumer
+        # (the columns of x are the rows of its scale matrix)
+        (mxq.mxq_relayout_mx_scales_grouped,
+         (o["s5"].data_ptr(), C2, 1, C2, offs.data_ptr(), G, R2, o["t6"].data_ptr(),
+          o["st6"].data_ptr())),
     ]
     return calls, outs
 

@@ -16,27 +16,10 @@ import consumer
 import mxfp8_quantization_moe_amd as mxq
 import oracle
 import workloads
-from gpu_helpers import CANARY, DEV, i32_dev, random_offsets
+from gpu_helpers import CANARY, DEV, i32_dev, random_offsets, relayout
 from scaled_mfma_model import dequantized_gemm
 
 pytestmark = pytest.mark.gpu
-
-
-def relayout(scales_dev, offs, extent):
-    """Direct C-ABI call with canary-filled outputs; returns (tiles up to
-    capacity, tile_starts) as numpy."""
-    rows = scales_dev.shape[0]
-    G = len(offs)
-    cap = mxq.mx_tile_capacity(rows, extent, G)
-    tiles = torch.full((max(cap, 16),), CANARY, dtype=torch.uint8, device=DEV)
-    starts = torch.full((G + 1,), -7, dtype=torch.int32, device=DEV)
-    d_offs = i32_dev(offs)
-    code = mxq.mxq_relayout_mx_scales_grouped(
-        scales_dev.data_ptr(), rows, scales_dev.stride(0), scales_dev.stride(1), d_offs.data_ptr(),
-        G, extent, tiles.data_ptr(), starts.data_ptr(), torch.cuda.current_stream().cuda_stream)
-    assert code == 0, mxq._capi.status_string(code)
-    torch.cuda.synchronize()
-    return tiles.cpu().numpy()[:cap], starts.cpu().numpy()
 
 
 def check(scales_np, scales_dev, offs, extent, what):
