@@ -22,6 +22,13 @@ constexpr int kJaggedStridedWaves = 8;  // waves per workgroup: tile = 8*16*64/C
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// column-major q whose 128-row column runs start on 128-byte lines: base and
+// the column (and batch) strides on lines
+int line_aligned(const void *q, int64_t ldq, int64_t sqe)
+{
+    return ((reinterpret_cast<uintptr_t>(q) & 127u) == 0 && ldq % 128 == 0 && sqe % 128 == 0) ? 1 : 0;
+}
+
 mxq_status launch_status()
 {
     hipError_t e = hipGetLastError();
@@ -306,7 +313,7 @@ mxq_status mxq_quantize_mx_3d_colwise(const uint16_t *w, int64_t E, int64_t N, i
     block_strided_kernel<32, 1, true><<<dim3((unsigned)nblocks), dim3(kBlockThreads), 0,
                                          reinterpret_cast<hipStream_t>(stream)>>>(
         w, sw_e, sw_n, (int)N, (int)K, q, sq_e, sq_k, scales, ss_e, ss_nb, ss_k, (int)tiles_r,
-        (int)tiles_c, scale_mode == MXQ_SCALE_RCEIL);
+        (int)tiles_c, scale_mode == MXQ_SCALE_RCEIL, line_aligned(q, sq_k, sq_e));
     return launch_status();
 }
 
@@ -475,14 +482,15 @@ mxq_status mxq_quantize_blockwise(const uint16_t *x, int64_t rows, int64_t cols,
     const int64_t nblocks = tiles_r * tiles_c;
     if (nblocks > INT32_MAX)
         return MXQ_ERR_INVALID_ARG;
+    const int nt = line_aligned(q, sq_c, 0);
     if (b128x128)
         block_strided_kernel<128, 128, false><<<dim3((unsigned)nblocks), dim3(kBlockThreads), 0, st>>>(
             x, 0, sx_r, (int)rows, (int)cols, q, 0, sq_c, scales, 0, ss_rb, ss_cb, (int)tiles_r,
-            (int)tiles_c, 0);
+            (int)tiles_c, 0, nt);
     else
         block_strided_kernel<128, 1, false><<<dim3((unsigned)nblocks), dim3(kBlockThreads), 0, st>>>(
             x, 0, sx_r, (int)rows, (int)cols, q, 0, sq_c, scales, 0, ss_rb, ss_cb, (int)tiles_r,
-            (int)tiles_c, 0);
+            (int)tiles_c, 0, nt);
     return launch_status();
 }
 

@@ -102,11 +102,16 @@ __global__ __launch_bounds__(kBlockThreads) void block_contig_kernel(
 // [e*sse + rb*ss_rb + cb*ss_cb] (cb = c for BC == 1).
 // BR in {32, 128}; BC in {1, 128} (BC == 128 needs BR == 128).
 // Grid: E * tiles_r * tiles_c, tile 128 rows x 256 columns.
+// nt: nontemporal q stores, for a launch whose 128-row column runs start on
+// 128-byte lines (each output line is then one store instruction's); with
+// runs off the lines, plain stores let L2 merge the two parts of a line
+// before it goes to HBM, where a partial nontemporal write of a line costs a
+// read-modify-write of a memory burst.
 template <int BR, int BC, bool E8M0>
 __global__ __launch_bounds__(kBlockThreads) void block_strided_kernel(
     const uint16_t *__restrict__ x, int64_t sxe, int64_t ldx, int rows, int cols,
     uint8_t *__restrict__ q, int64_t sqe, int64_t ldq, void *__restrict__ scales, int64_t sse,
-    int64_t ss_rb, int64_t ss_cb, int tiles_r, int tiles_c, int rceil)
+    int64_t ss_rb, int64_t ss_cb, int tiles_r, int tiles_c, int rceil, int nt)
 {
     static_assert(BR == 32 || BR == 128, "BR");
     static_assert(BC == 1 || (BC == 128 && BR == 128), "BC");
@@ -217,7 +222,10 @@ __global__ __launch_bounds__(kBlockThreads) void block_strided_kernel(
                    elem8(v[11], jj) * sc[jj]);
         o.w = cvt4_sel<E8M0>(elem8(v[12], jj) * sc[jj], elem8(v[13], jj) * sc[jj], elem8(v[14], jj) * sc[jj],
                    elem8(v[15], jj) * sc[jj]);
-        st16_nt(qp + (int64_t)jj * ldq, o);
+        if (nt)
+            st16_nt(qp + (int64_t)jj * ldq, o);
+        else
+            st16(qp + (int64_t)jj * ldq, o);
     }
 }
 
