@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 import torch
 
+import mxfp8_quantization_moe_amd as mxq
 import oracle
 import workloads
 from gpu_helpers import (CANARY, adversarial, assert_same_bytes, bf16_dev, blockwise, i32_dev,
@@ -219,3 +220,49 @@ def test_jagged_colwise_many_equal_groups():
     bits = adversarial((16384, 72), 230)
     offs = np.arange(256, 16385, 256, dtype=np.int32)
     check_colwise(bits, offs)
+
+
+@pytest.mark.parametrize("shift,pad", [(0, 0), (16, 0), (0, 16), (48, 32)])
+def test_column_major_stores_on_and_off_the_lines(shift, pad):
+    """The block kernel takes nontemporal stores only when q, its column
+    stride and its batch stride sit on 128-byte lines, plain stores
+    otherwise; both give the oracle's bytes (MX 3D colwise and blockwise
+    128x1), and nothing outside the tensor is written."""
+    E, N, K = 2, 256, 264
+    w = adversarial((E, N, K), 950 + shift + pad)
+    ldq = N + pad
+    buf = torch.full((E * K * ldq + shift + 64,), CANARY, dtype=torch.uint8, device="cuda")
+    s = torch.full((E * (N // 32) * K,), CANARY, dtype=torch.uint8, device="cuda")
+    dw = bf16_dev(w)
+    code = mxq.mxq_quantize_mx_3d_colwise(dw.data_ptr(), E, N, K, dw.stride(0), dw.stride(1),
+                                          dw.stride(2), buf.data_ptr() + shift, K * ldq, 1, ldq,
+                                          s.data_ptr(), (N // 32) * K, K, 1, 0,
+                                          torch.cuda.current_stream().cuda_stream)
+    assert code == 0
+    torch.cuda.synchronize()
+    raw = buf.cpu().numpy()
+    q = np.lib.stride_tricks.as_strided(raw[shift:], (E, N, K), (K * ldq, 1, ldq))
+    oq, os_ = oracle.quantize_mx_3d_colwise(w)
+    assert_same_bytes(np.ascontiguousarray(q), oq, f"mx3d q (shift {shift}, pad {pad})")
+    assert_same_bytes(s.cpu().numpy().reshape(E, N // 32, K), os_, "mx3d scales")
+    assert np.all(raw[:shift] == CANARY) and np.all(raw[shift + E * K * ldq:] == CANARY)
+    if pad:
+        assert np.all(np.lib.stride_tricks.as_strided(raw[shift + N:], (E * K, pad), (ldq, 1)) == CANARY)
+
+    rows, cols = 256, 200
+    x = adversarial((rows, cols), 960 + shift + pad)
+    ldq = rows + pad
+    buf = torch.full((cols * ldq + shift + 64,), CANARY, dtype=torch.uint8, device="cuda")
+    sc = torch.full((rows // 128 * cols,), float("nan"), dtype=torch.float32, device="cuda")
+    dx = bf16_dev(x)
+    code = mxq.mxq_quantize_blockwise(dx.data_ptr(), rows, cols, dx.stride(0), dx.stride(1), 128, 1,
+                                      buf.data_ptr() + shift, 1, ldq, sc.data_ptr(), cols, 1,
+                                      torch.cuda.current_stream().cuda_stream)
+    assert code == 0
+    torch.cuda.synchronize()
+    raw = buf.cpu().numpy()
+    q = np.lib.stride_tricks.as_strided(raw[shift:], (rows, cols), (1, ldq))
+    oq, os_ = oracle.quantize_blockwise(x, 128, 1)
+    assert_same_bytes(np.ascontiguousarray(q), oq, f"blockwise 128x1 q (shift {shift}, pad {pad})")
+    assert_same_bytes(sc.cpu().numpy().reshape(rows // 128, cols), os_, "blockwise 128x1 scales")
+    assert np.all(raw[:shift] == CANARY) and np.all(raw[shift + cols * ldq:] == CANARY)
