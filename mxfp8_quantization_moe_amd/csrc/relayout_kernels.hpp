@@ -43,6 +43,7 @@
 #include <stdint.h>
 
 #include "group_tables.hpp"
+#include "mxq_device.hpp"
 
 namespace mxq {
 
@@ -278,7 +279,9 @@ __global__ __launch_bounds__(kRelayoutThreads) void relayout_mx_scales_kernel(
                 continue;
             tile = T + (int64_t)rc * KT + kt;
         }
-        *reinterpret_cast<uint4 *>(tiles + tile * 256 + 16 * seg) = make_uint4(o[0], o[1], o[2], o[3]);
+        // 16 lanes write a whole 256-byte tile: nontemporal stores (110 against
+        // 129 us on (8192, 32770) scales; nontemporal loads were slower)
+        st16_nt(tiles + tile * 256 + 16 * seg, make_uint4(o[0], o[1], o[2], o[3]));
     }
 }
 
