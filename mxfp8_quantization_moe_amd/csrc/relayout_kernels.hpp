@@ -67,12 +67,13 @@ struct RelayoutShape {
 
 // ints of group table before the staged bytes (rounded to 16 bytes).  For
 // G <= 64 one wave builds ends and three prefixes (blocks, K tiles, items);
-// for larger G the workgroup scans K tiles and items only (the tables then
-// take at most 48 KB) and sums its own group's block base.
+// for larger G the workgroup scans K tiles and items only, reading group
+// lengths from the offsets, and sums its own group's block base: the tables
+// then take at most 32 KB, so tables and stage stay under 64 KB at G = 4096.
 __host__ __device__ constexpr int relayout_table_ints(int G, int layout)
 {
     return G <= 64 ? ((G + 3 * (G + 1) + 3) / 4) * 4
-                   : ((G + (G + 1) + (layout != 1 ? G + 1 : 0) + 3) / 4) * 4;
+                   : (((G + 1) + (layout != 1 ? G + 1 : 0) + 3) / 4) * 4;
 }
 
 template <int LAYOUT, int SEG>
@@ -140,26 +141,34 @@ __global__ __launch_bounds__(kRelayoutThreads) void relayout_mx_scales_kernel(
     extern __shared__ __align__(16) int relayout_lds[];
     __shared__ int s_red[kRelayoutThreads / 64];
     const bool small = G <= 64;
-    int *s_end = relayout_lds;
-    int *s_pt = s_end + G;                                   // K tiles, G + 1
+    int *s_end = relayout_lds;                               // G <= 64 only
+    int *s_pt = relayout_lds + (small ? G : 0);              // K tiles, G + 1
     int *s_pc = LAYOUT == 1 ? s_pt : s_pt + G + 1;           // items along K, G + 1
     int *s_pb = small ? s_pt + 2 * (G + 1) : nullptr;        // blocks, G + 1 (G <= 64)
     uint8_t *stage = reinterpret_cast<uint8_t *>(relayout_lds + relayout_table_ints(G, LAYOUT));
 
+    // group length, clamped as everywhere: from the table for G <= 64, else
+    // straight from the offsets
+    auto glen = [&](int g) {
+        if (small)
+            return group_len(s_end, g);
+        int hi = offs[g], lo = g ? offs[g - 1] : 0;
+        hi = hi < 0 ? 0 : (hi > extent ? extent : hi);
+        lo = lo < 0 ? 0 : (lo > extent ? extent : lo);
+        return hi > lo ? hi - lo : 0;
+    };
     const int t = threadIdx.x;
     if (small) {
         if (t < 64)
             wave_group_tables3<9, SH::SHC, 5>(offs, G, extent, s_end, s_pt, s_pc, s_pb);
         __syncthreads();
     } else {
-        load_group_ends<kRelayoutThreads>(offs, G, extent, s_end);
         if (LAYOUT == 1)
-            slot_prefix<kRelayoutThreads>(
-                G, s_pt, [&](int g) { return units_of<9>(group_len(s_end, g)); });
+            slot_prefix<kRelayoutThreads>(G, s_pt, [&](int g) { return units_of<9>(glen(g)); });
         else
             slot_prefix2<kRelayoutThreads>(
-                G, s_pt, s_pc, [&](int g) { return units_of<9>(group_len(s_end, g)); },
-                [&](int g) { return units_of<SH::SHC>(group_len(s_end, g)); });
+                G, s_pt, s_pc, [&](int g) { return units_of<9>(glen(g)); },
+                [&](int g) { return units_of<SH::SHC>(glen(g)); });
     }
     const int RB = (rows + 15) >> 4;
     if (blockIdx.x == 0 && tile_starts != nullptr)
@@ -176,7 +185,7 @@ __global__ __launch_bounds__(kRelayoutThreads) void relayout_mx_scales_kernel(
         return;
     const int g = find_slot(s_pc, G, kc_all);
     const int kc = kc_all - s_pc[g];
-    const int n = group_len(s_end, g);
+    const int n = glen(g);
     const int nb = units_of<5>(n);
     const int KT = units_of<9>(n);
     int64_t B;
@@ -186,7 +195,7 @@ __global__ __launch_bounds__(kRelayoutThreads) void relayout_mx_scales_kernel(
         // block base of this workgroup's group: blocks of the groups before it
         int part = 0;
         for (int h = t; h < g; h += kRelayoutThreads)
-            part += units_of<5>(group_len(s_end, h));
+            part += units_of<5>(glen(h));
 #pragma unroll
         for (int d = 32; d >= 1; d >>= 1)
             part += __shfl_xor(part, d, 64);

@@ -40,6 +40,7 @@ def check_colwise(bits, offs, mode):
     (4, 5000, 300, 1, 7, 6),       # many groups
     (2, 40, 64, 1, 0, 7),          # more groups than blocks
     (40, 1, 2, 1, 0, 8),
+    (3, 9000, 4096, 1, 0, 9),      # the most groups, most of them empty
 ])
 def test_jagged_mx_rowwise_ragged(rows, cols, G, mult, tail, seed, mode):
     bits = adversarial((rows, cols), 600 + seed)
@@ -56,6 +57,7 @@ def test_jagged_mx_rowwise_ragged(rows, cols, G, mult, tail, seed, mode):
     (5000, 16, 100, 1, 9, 15),     # many groups
     (33, 8, 3, 1, 1, 16),
     (300, 512, 2, 8, 0, 17),
+    (9000, 16, 4096, 1, 0, 18),    # the most groups, most of them empty
 ])
 def test_jagged_mx_colwise_ragged(rows, cols, G, mult, tail, seed, mode):
     bits = adversarial((rows, cols), 700 + seed)

@@ -48,6 +48,7 @@ def test_small_workloads():
     (4, 77, 1, 1, 0, 5),
     (6, 300, 64, 1, 0, 6),
     (2, 5000, 300, 1, 7, 7),       # many groups: binary-search group lookup
+    (3, 9000, 4096, 1, 0, 30),     # the most groups, most of them empty
     (1, 1, 2, 1, 0, 8),
     (7, 8, 3, 1, 1, 9),
 ])

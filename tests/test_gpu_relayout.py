@@ -209,3 +209,22 @@ def test_scaled_mfma_end_to_end_through_the_library():
     oqb, osb = np.ascontiguousarray(oqx.T), osx.T
     want = dequantized_gemm(oqa, osa, oqb, osb, offs)
     _tolerance_ok(got, want, oqa, osa, oqb, osb, offs)
+
+
+@pytest.mark.parametrize("layout", [0, 1, 2])
+def test_maximum_group_count(layout):
+    """G = 4096 (the ABI's limit), most groups empty or a few tokens long:
+    the workgroup-wide tables, for each input layout."""
+    G, extent, rows = 4096, 70000, 40
+    offs = random_offsets(extent, G, 870 + layout, short_tail=3)
+    cap = oracle.jagged_mx_scale_capacity(extent, G)
+    if layout == 0:
+        s = workloads.e8m0_bytes((rows, cap), 880)
+        s_np, dev = s, torch.from_numpy(s).to(DEV)
+    elif layout == 1:
+        s = workloads.e8m0_bytes((cap, rows), 881)
+        s_np, dev = s.T, torch.from_numpy(s).to(DEV).t()
+    else:
+        s = workloads.e8m0_bytes((rows, 2 * cap), 882)
+        s_np, dev = s[:, ::2], torch.from_numpy(s).to(DEV)[:, ::2]
+    check(s_np, dev, offs, extent, f"G = 4096, layout {layout}")
