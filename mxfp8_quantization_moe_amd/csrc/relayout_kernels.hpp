@@ -35,9 +35,10 @@
 // Items of 1024 bytes per staged row, rather than 256, 512 or 2048, measured
 // fastest: smaller items pay the per-workgroup table build and latency more
 // often, larger ones lose occupancy to their LDS.
-// The host never reads the offsets: each workgroup builds the group table
-// (clamped ends, prefix counts of blocks, tiles and items) and finds its
-// group by binary search; spare workgroups of the upper-bound grid exit.
+// The host never reads the offsets: each workgroup builds the group tables
+// (prefix counts of blocks, K tiles and items; clamped ends too for G <= 64)
+// and finds its group by binary search; spare workgroups of the upper-bound
+// grid exit.
 #pragma once
 
 #include <stdint.h>
