@@ -36,7 +36,8 @@ def load() -> ctypes.CDLL:
             raise RuntimeError(f"{LIB} is not built (run build())")
         lib = ctypes.CDLL(LIB)
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-        lib.consumer_grouped_gemm.argtypes = [vp, i64, i32, vp, i64, i32, vp, vp, vp, vp, vp, i32, vp]
+        lib.consumer_grouped_gemm.argtypes = [vp, i64, i32, vp, i64, i32, vp, vp, vp, vp, vp, i32, vp,
+                                              i32, i32, i32, i32]
         lib.consumer_grouped_gemm.restype = ctypes.c_int
         _lib = lib
     return _lib

@@ -49,9 +49,11 @@ __device__ int tile_word(const uint8_t *tiles, int64_t tile, int lane)
 __global__ __launch_bounds__(64) void grouped_gemm_kernel(
     const uint8_t *qa, int64_t lda, int rows, const uint8_t *qb, int64_t ldb, int cols,
     const uint8_t *ta, const int32_t *sta, const uint8_t *tb, const int32_t *stb,
-    const int32_t *offs, float *out)
+    const int32_t *offs, float *out, int ra0, int rb0)
 {
-    const int g = blockIdx.z, ra = blockIdx.y, rb = blockIdx.x, lane = threadIdx.x;
+    const int g = blockIdx.z, lane = threadIdx.x;
+    const int ra = ra0 + (int)blockIdx.y, rb = rb0 + (int)blockIdx.x;
+    const int orows = 16 * (int)gridDim.y, ocols = 16 * (int)gridDim.x;
     const int lo = g ? offs[g - 1] : 0;
     const int hi = offs[g];
     const int n = hi > lo ? hi - lo : 0;
@@ -75,26 +77,29 @@ __global__ __launch_bounds__(64) void grouped_gemm_kernel(
         const int row = 16 * ra + 4 * grp + r;
         const int col = 16 * rb + i;
         if (row < rows && col < cols)
-            out[((int64_t)g * rows + row) * cols + col] = acc[r];
+            out[((int64_t)g * orows + row - 16 * ra0) * ocols + col - 16 * rb0] = acc[r];
     }
 }
 
 }  // namespace
 
 // qa: (rows, tokens) e4m3, row pitch lda; qb: (cols, tokens) e4m3, row pitch
-// ldb; ta/tb and sta/stb: the scale tiles and tile starts of A and B; out:
-// (G, rows, cols) fp32.  All device pointers; synchronous.  Returns 0 on
-// success.
+// ldb; ta/tb and sta/stb: the scale tiles and tile starts of A and B.  The
+// product is computed for row blocks ra0 .. ra0+nra-1 of A and row blocks
+// rb0 .. rb0+nrb-1 of B only; out: (G, 16*nra, 16*nrb) fp32, entries past
+// the last row or column untouched.  All device pointers; synchronous.
+// Returns 0 on success.
 extern "C" int consumer_grouped_gemm(const uint8_t *qa, int64_t lda, int rows, const uint8_t *qb,
                                      int64_t ldb, int cols, const uint8_t *ta, const int32_t *sta,
                                      const uint8_t *tb, const int32_t *stb, const int32_t *offs,
-                                     int G, float *out)
+                                     int G, float *out, int ra0, int nra, int rb0, int nrb)
 {
-    if (rows <= 0 || cols <= 0 || G <= 0)
+    if (rows <= 0 || cols <= 0 || G <= 0 || nra <= 0 || nrb <= 0 || ra0 < 0 || rb0 < 0 ||
+        16 * (ra0 + nra) > rows + 15 || 16 * (rb0 + nrb) > cols + 15)
         return 1;
-    dim3 grid((cols + 15) / 16, (rows + 15) / 16, G);
+    dim3 grid(nrb, nra, G);
     hipLaunchKernelGGL(grouped_gemm_kernel, grid, dim3(64), 0, 0, qa, lda, rows, qb, ldb, cols, ta,
-                       sta, tb, stb, offs, out);
+                       sta, tb, stb, offs, out, ra0, rb0);
     if (hipGetLastError() != hipSuccess)
         return 2;
     return hipDeviceSynchronize() == hipSuccess ? 0 : 3;

@@ -129,13 +129,14 @@ def _consume(qa, ta, sta, qb, tb, stb, offs, rows, cols):
          for k, v in dict(qa=qa, ta=ta, sta=sta, qb=qb, tb=tb, stb=stb,
                           offs=np.asarray(offs, np.int32)).items()}
     G = len(offs)
-    out = torch.zeros((G, rows, cols), dtype=torch.float32, device=DEV)
+    nra, nrb = (rows + 15) // 16, (cols + 15) // 16
+    out = torch.zeros((G, 16 * nra, 16 * nrb), dtype=torch.float32, device=DEV)
     rc = consumer.load().consumer_grouped_gemm(
         d["qa"].data_ptr(), qa.shape[1], rows, d["qb"].data_ptr(), qb.shape[1], cols,
         d["ta"].data_ptr(), d["sta"].data_ptr(), d["tb"].data_ptr(), d["stb"].data_ptr(),
-        d["offs"].data_ptr(), G, out.data_ptr())
+        d["offs"].data_ptr(), G, out.data_ptr(), 0, nra, 0, nrb)
     assert rc == 0
-    return out.cpu().numpy().astype(np.float64)
+    return out[:, :rows, :cols].cpu().numpy().astype(np.float64)
 
 
 # The instruction does not accumulate like sequential IEEE fp32 additions:
@@ -228,3 +229,49 @@ def test_maximum_group_count(layout):
         s = workloads.e8m0_bytes((rows, 2 * cap), 882)
         s_np, dev = s[:, ::2], torch.from_numpy(s).to(DEV)[:, ::2]
     check(s_np, dev, offs, extent, f"G = 4096, layout {layout}")
+
+
+def test_scaled_mfma_at_the_moe_backward_shapes():
+    """grad_out^T (4096, 16384) and x (16384, 4096) with the 8 MoE token
+    groups, quantized and re-laid out on the device at full size; the real
+    instruction consumes the tiles of the first and last two row blocks of
+    each operand (tile numbers near both ends of every group's range) and
+    reproduces the oracle's dequantized grouped GEMM of those rows and
+    columns."""
+    go = workloads.device_normal_bf16((4096, 16384), 31)
+    x = workloads.device_normal_bf16((16384, 4096), 32)
+    offs = workloads.moe_offsets()
+    d_offs = i32_dev(offs)
+    qa, sa = mxq.quantize_jagged_mx_rowwise(go, d_offs)
+    qx, sx = mxq.quantize_jagged_mx_colwise(x, d_offs)
+    ta, sta = mxq.relayout_mx_scales_grouped(sa, d_offs, 16384)
+    tb, stb = mxq.relayout_mx_scales_grouped(sx.t(), d_offs, 16384)
+    qa_u8 = qa.view(torch.uint8)
+    qb_u8 = qx.view(torch.uint8).t()          # (cols, tokens) view of the column-major q
+    G = offs.size
+    lib = consumer.load()
+    picks = [0, 1, 254, 255]                  # 16-row blocks sampled from each operand
+    rows_a = np.concatenate([np.arange(16 * b, 16 * b + 16) for b in picks])
+    rows_b = rows_a
+    idx = torch.from_numpy(rows_a).to(DEV)
+    a_bits = go.index_select(0, idx).view(torch.int16).cpu().numpy().view(np.uint16)
+    x_bits = np.ascontiguousarray(
+        x.index_select(1, torch.from_numpy(rows_b).to(DEV)).view(torch.int16).cpu().numpy().view(np.uint16))
+    oqa, osa = oracle.quantize_jagged_mx_rowwise(a_bits, offs)
+    oqx, osx = oracle.quantize_jagged_mx_colwise(x_bits, offs)
+    oqb, osb = np.ascontiguousarray(oqx.T), osx.T
+    want = dequantized_gemm(oqa, osa, oqb, osb, offs)           # G x (64, 64)
+    absref = _abs_terms(oqa, osa, oqb, osb, offs)
+    for ia, ba in enumerate(picks):
+        for ib, bb in enumerate(picks):
+            out = torch.zeros((G, 16, 16), dtype=torch.float32, device=DEV)
+            rc = lib.consumer_grouped_gemm(qa_u8.data_ptr(), qa_u8.stride(0), 4096,
+                                           qb_u8.data_ptr(), qb_u8.stride(0), 4096,
+                                           ta.data_ptr(), sta.data_ptr(), tb.data_ptr(),
+                                           stb.data_ptr(), d_offs.data_ptr(), G, out.data_ptr(),
+                                           ba, 1, bb, 1)
+            assert rc == 0
+            got = out.cpu().numpy().astype(np.float64)
+            sl = (slice(16 * ia, 16 * ia + 16), slice(16 * ib, 16 * ib + 16))
+            w = _worst(list(got), [m[sl] for m in want], [m[sl] for m in absref])
+            assert w <= REL, f"row blocks {ba}, {bb}: worst {w:.3e} of the sum of |terms|"
