@@ -176,14 +176,26 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
     const int t = threadIdx.x;
     const int lane = t & 63;
 
+    // Without a tail (cols a multiple of 8) the row is read through a buffer
+    // descriptor: segments past the row end, and every segment of a row past
+    // the last one (descriptor range 0), read as zeros without a memory
+    // access, so the loads carry no branch.  With loads under branches the
+    // compiler waits for every outstanding load at the first use of any, i.e.
+    // for the next row's loads too, and the two buffers would not overlap.
     auto load_row = [&](uint4 (&d)[NR], int r) __attribute__((always_inline)) {
-        const uint16_t *xr = x + (int64_t)r * ldx;
+        if constexpr (!TAIL) {
+            const bool ok = r < rows;
+            const auto rs = buffer_rsrc(x + (int64_t)(ok ? r : 0) * ldx, ok ? 2u * (uint32_t)cols : 0u);
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            const int e0 = 8 * (i * kThreads + t);
-            d[i] = e0 + 8 <= cols ? ld16_nt(xr + e0) : make_uint4(0u, 0u, 0u, 0u);
-        }
-        if constexpr (TAIL) {
+            for (int i = 0; i < NR; ++i)
+                d[i] = ldbuf16_nt(rs, 16u * (uint32_t)(i * kThreads + t));
+        } else {
+            const uint16_t *xr = x + (int64_t)r * ldx;
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                const int e0 = 8 * (i * kThreads + t);
+                d[i] = e0 + 8 <= cols ? ld16_nt(xr + e0) : make_uint4(0u, 0u, 0u, 0u);
+            }
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
                 const int e0 = 8 * (i * kThreads + t);
@@ -195,12 +207,19 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
 
     uint4 va[NR], vb[NR];
     int row = blockIdx.x;
-    // the first row's loads do not depend on the offsets: issue them before
-    // the offsets are staged in LDS so both latencies overlap
-    if (row < rows)
-        load_row(va, row);
-    for (int g = t; g < G; g += kThreads) {
-        int o = offs[g];
+    // the offsets are loaded before the first row: loads retire in order, so
+    // an offsets load issued after the row would wait for the whole row, and
+    // the group bookkeeping below (and with it the next row's loads) with it
+    // Threads past the last group store the last group's entry again (the
+    // same value): an unconditional use keeps the compiler from sinking the
+    // load below the row's loads.
+    const int g_first = t < G ? t : G - 1;
+    const int o_first = offs[g_first];
+    load_row(va, row);   // the grid never exceeds the row count
+    s_offs[g_first] = o_first < 0 ? 0 : (o_first > cols ? cols : o_first);
+    s_amax[g_first] = 0u;
+    for (int g = t + kThreads; g < G; g += kThreads) {
+        const int o = offs[g];
         s_offs[g] = o < 0 ? 0 : (o > cols ? cols : o);
         s_amax[g] = 0u;
     }
@@ -227,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
 
     auto process_row = [&](uint4 (&cur)[NR], uint4 (&nxt)[NR], int r) __attribute__((always_inline)) {
         const int next = r + (int)gridDim.x;
-        if (next < rows)
+        if (!TAIL || next < rows)
             load_row(nxt, next);
         const uint16_t *xr = x + (int64_t)r * ldx;
         if (uni == (1u << NR) - 1u) {

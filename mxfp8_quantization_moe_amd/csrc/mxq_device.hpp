@@ -184,4 +184,21 @@ __device__ __forceinline__ void st8_nt(uint8_t *p, uint2 v)
     __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t *>(p));
 }
 
+// Raw buffer access (CDNA buffer descriptor: base, no stride, a byte range).
+// A load whose bytes lie at or past `bytes` returns zeros and reads no
+// memory, so loads past the end of a row, or of every row, need no branch.
+// Branch-free loads matter for latency hiding: after loads issued under a
+// condition the compiler can no longer count how many are outstanding and
+// waits for all of them at the first use of any.  Word 3 is the gfx9-family
+// raw-buffer format; aux 2 is the nontemporal hint.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 ldbuf16_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 2);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 }  // namespace mxq
