@@ -215,6 +215,24 @@ def test_mx_every_bf16_amax(mode):
     assert_same_bytes(s, os_, f"mx rowwise {mode} scales (every amax)")
 
 
+def test_jagged_colwise_row_stride_past_2_23():
+    """A row stride past 2^23 elements (128 rows of x span more than 2^31
+    bytes): one 3150-row group (four tiles, one streamed and read again)
+    and a short group after it."""
+    rows, cols, ldx = 3200, 16, (1 << 23) + 64
+    bits = adversarial((rows, cols), 240)
+    offs = np.array([3150, 3200], dtype=np.int32)
+    buf = torch.empty((rows - 1) * ldx + cols, dtype=torch.bfloat16, device="cuda")
+    view = buf.as_strided((rows, cols), (ldx, 1))
+    view.copy_(bf16_dev(bits))
+    q, s = jagged_colwise(view, i32_dev(offs))
+    del view, buf
+    torch.cuda.empty_cache()
+    oq, os_ = oracle.quantize_jagged_colwise(bits, offs, canary=CANARY)
+    assert_same_bytes(q, oq, "colwise (row stride 2^23 + 64) q")
+    assert_same_bytes(s, os_, "colwise (row stride 2^23 + 64) scales")
+
+
 def test_jagged_colwise_many_equal_groups():
     """64 groups of 256 rows (many experts, few tokens each): whole waves
     inside one group, four groups per 1024-row block."""
