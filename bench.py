@@ -16,11 +16,21 @@ Metric: algorithmic HBM bytes (2 B bf16 read + 1 B e4m3 write + scale bytes
 per launch) divided by time.  Inputs are resident in HBM before the timed
 region; outputs are preallocated; every launch goes through the C ABI.
 
+Timing: the K timed steps run back to back with one pair of HIP events on
+the launch stream around them (``gpu_ms_per_step``) besides the host clock
+(``ms_per_step``, which gives ``value``).  A second pass of K steps puts an
+event between consecutive launches; those intervals also hold each launch's
+dispatch and the event (about 2 us, the same for every launch), so a
+kernel's ``avg_us`` (and ``roofline.avg_launch_us``) is its average interval
+less an equal share of the intervals' excess over ``gpu_ms_per_step``.  The
+raw intervals are reported as ``interval_*_us``.
+
 Prints one JSON line (rank 0).
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -346,6 +356,67 @@ def traffic_for(kernel_name: str, workload: str):
     return None
 
 
+class DeviceEvents:
+    """Timing events on the launch stream with a device-scope release
+    (hipEventReleaseToDevice), else without the system-scope fence
+    (hipEventDisableSystemFence): recording them writes back and invalidates
+    no caches for the host, so they perturb the kernels between them less
+    than default events.  Uses the HIP runtime torch has already loaded (the
+    one the launches go through); None if neither kind can be created."""
+
+    KINDS = ((0x40000000, "hipEventReleaseToDevice"), (0x20000000, "hipEventDisableSystemFence"))
+
+    def __init__(self):
+        lib = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD)
+        lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        for f in (lib.hipEventCreateWithFlags, lib.hipEventRecord, lib.hipEventElapsedTime,
+                  lib.hipEventDestroy):
+            f.restype = ctypes.c_int
+        self.lib = lib
+        self.made = []
+        self.flags, self.kind = None, None
+        for flags, kind in self.KINDS:
+            e = ctypes.c_void_p()
+            if lib.hipEventCreateWithFlags(ctypes.byref(e), flags) == 0:
+                lib.hipEventDestroy(e)
+                self.flags, self.kind = flags, kind
+                break
+        if self.flags is None:
+            raise OSError("no timing event kind accepted")
+
+    @classmethod
+    def open(cls):
+        try:
+            return cls()
+        except (OSError, AttributeError):
+            return None
+
+    def create(self):
+        e = ctypes.c_void_p()
+        if self.lib.hipEventCreateWithFlags(ctypes.byref(e), self.flags) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self.made.append(e)
+        return e
+
+    def record(self, e, stream_handle):
+        if self.lib.hipEventRecord(e, ctypes.c_void_p(stream_handle)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for e in self.made:
+            self.lib.hipEventDestroy(e)
+        self.made = []
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -376,33 +447,57 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    # timed region: K steps exactly as a caller runs them (no instrumentation)
+    dev = DeviceEvents.open()
+
+    # timed region: K steps exactly as a caller runs them, bracketed by one
+    # pair of events on the launch stream (none between launches)
+    if dev is not None:
+        g0, g1 = dev.create(), dev.create()
+    else:
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    (dev.record(g0, sh) if dev is not None else g0.record(stream))
     for k in range(K):
         for l in launches:
             l(sh)
+    (dev.record(g1, sh) if dev is not None else g1.record(stream))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gpu_ms = dev.elapsed_ms(g0, g1) if dev is not None else g0.elapsed_time(g1)
 
-    # per-kernel durations: K more steps with a HIP event on the launch stream
-    # between consecutive launches (the events themselves add a few µs per
-    # step, which is why they stay out of the timed region above)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)] for _ in range(K)]
+    # per-kernel durations: K more steps with an event on the launch stream
+    # between consecutive launches.  Each interval also holds a launch's
+    # dispatch and the event itself, the same few µs for every launch: that
+    # overhead is the intervals' excess over the event-timed step above, and
+    # a kernel's duration is its interval less an equal part of it (this
+    # matches the kernel trace's averages).
+    if dev is not None:
+        ev = [[dev.create() for _ in range(len(launches) + 1)] for _ in range(K)]
+        record = lambda e: dev.record(e, sh)
+        elapsed = dev.elapsed_ms
+        event_kind = f"hip events ({dev.kind}) on the launch stream"
+    else:
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)] for _ in range(K)]
+        record = lambda e: e.record(stream)
+        elapsed = lambda a, b: a.elapsed_time(b)
+        event_kind = "torch events on the launch stream"
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for k in range(K):
-        ev[k][0].record(stream)
+        record(ev[k][0])
         for i, l in enumerate(launches):
             l(sh)
-            ev[k][i + 1].record(stream)
+            record(ev[k][i + 1])
     torch.cuda.synchronize()
     wall_instr = time.perf_counter() - t1
 
-    per_kernel_ms = []
-    for i, l in enumerate(launches):
-        ms = [ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(K)]
-        per_kernel_ms.append(float(np.mean(ms)))
+    interval_ms = [float(np.mean([elapsed(ev[k][i], ev[k][i + 1]) for k in range(K)]))
+                   for i in range(len(launches))]
+    gpu_step_ms = gpu_ms / K
+    # the intervals add the same per-launch overhead to every kernel
+    overhead_ms = max(0.0, (sum(interval_ms) - gpu_step_ms) / len(launches))
+    per_kernel_ms = [max(m - overhead_ms, 0.05 * m) for m in interval_ms]
     step_bytes = sum(l.nbytes for l in launches)
     ms_per_step = wall * 1e3 / K
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -411,11 +506,12 @@ def main():
     dl = launches[dom]
     achieved = dl.nbytes / (per_kernel_ms[dom] * 1e-3) / 1e9
     traffic = traffic_for(dl.kernel, args.workload)
-    warm_ms = [[ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(K)] for i in range(len(launches))]
+    warm_ms = [[elapsed(ev[k][i], ev[k][i + 1]) for k in range(K)] for i in range(len(launches))]
     kernels = {l.name: {"avg_us": round(per_kernel_ms[i] * 1e3, 2),
-                        "median_us": round(float(np.median(warm_ms[i])) * 1e3, 2),
-                        "min_us": round(float(np.min(warm_ms[i])) * 1e3, 2),
-                        "max_us": round(float(np.max(warm_ms[i])) * 1e3, 2),
+                        "interval_avg_us": round(interval_ms[i] * 1e3, 2),
+                        "interval_median_us": round(float(np.median(warm_ms[i])) * 1e3, 2),
+                        "interval_min_us": round(float(np.min(warm_ms[i])) * 1e3, 2),
+                        "interval_max_us": round(float(np.max(warm_ms[i])) * 1e3, 2),
                         "algorithmic_bytes": l.nbytes,
                         "GBps": round(l.nbytes / (per_kernel_ms[i] * 1e-3) / 1e9, 1),
                         "frac_of_peak": round(l.nbytes / (per_kernel_ms[i] * 1e-3) / 1e9 / PEAK_GBPS, 4)}
@@ -426,15 +522,18 @@ def main():
         # MALL) on the same stream before every launch
         flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         for i, l in enumerate(launches):
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(args.flush_iters)]
+            if dev is not None:
+                evs = [(dev.create(), dev.create()) for _ in range(args.flush_iters)]
+            else:
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(args.flush_iters)]
             for k, (a, b) in enumerate(evs):
                 flush.fill_(k & 0xFF)
-                a.record(stream)
+                record(a)
                 l(sh)
-                b.record(stream)
+                record(b)
             torch.cuda.synchronize()
-            ms = [a.elapsed_time(b) for a, b in evs]
+            ms = [elapsed(a, b) for a, b in evs]
             kernels[l.name]["flushed_us"] = {"median": round(float(np.median(ms)) * 1e3, 2),
                                              "min": round(float(np.min(ms)) * 1e3, 2),
                                              "max": round(float(np.max(ms)) * 1e3, 2),
@@ -482,6 +581,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "gpu_ms_per_step": round(gpu_step_ms, 5),
         "ms_per_step_with_events": round(wall_instr * 1e3 / K, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -493,13 +593,15 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": dl.kernel, "algorithmic_bytes_per_launch": dl.nbytes,
-                     "avg_launch_us": round(per_kernel_ms[dom] * 1e3, 2)},
+                     "avg_launch_us": round(per_kernel_ms[dom] * 1e3, 2), "timing": event_kind},
         "copy_ceiling": ceiling,
         "kernels": kernels,
         "cpu_baseline": cpu,
         "csrc_digest": csrc_digest(),
     }
     print(json.dumps(out), flush=True)
+    if dev is not None:
+        dev.close()
     del keep
 
 
