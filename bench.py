@@ -53,7 +53,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-copy-ceiling", action="store_true",
                    help="skip timing the 4 GiB device-to-device copy used as the practical ceiling")
-    p.add_argument("--flush-iters", type=int, default=0,
+    p.add_argument("--flush-iters", type=int, default=20,
                    help="after the timed steps, time each kernel this many more times with a "
                         "1 GiB buffer written before every launch (cold L2 and MALL) and report "
                         "median/min/max; 0 = skip")
@@ -533,7 +533,7 @@ def main():
                 l(sh)
                 record(b)
             torch.cuda.synchronize()
-            ms = [elapsed(a, b) for a, b in evs]
+            ms = [max(elapsed(a, b) - overhead_ms, 0.0) for a, b in evs]   # same per-launch overhead
             kernels[l.name]["flushed_us"] = {"median": round(float(np.median(ms)) * 1e3, 2),
                                              "min": round(float(np.min(ms)) * 1e3, 2),
                                              "max": round(float(np.max(ms)) * 1e3, 2),
