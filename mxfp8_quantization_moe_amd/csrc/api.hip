@@ -110,7 +110,19 @@ mxq_status run_jagged_strided(const uint16_t *x, int64_t ext, int64_t ncols, int
     constexpr int CG = kJaggedStridedCG, SPS = 8 / CG, NW = kJaggedStridedWaves;
     const int64_t nstrips = (ncols + 8 * CG - 1) / (8 * CG);
     const int64_t nsuper = (nstrips + SPS - 1) / SPS;
-    const int64_t nblocks = 8 * SPS * ((G * nsuper + 7) / 8);
+    // items per strip (long groups and packs of short groups; only the
+    // device knows which), bounded from the extent and G alone: a long group
+    // spans more than TROWS - 15 rows, so there are at most ext / (TROWS -
+    // 14) of them; a run of short groups starts at group 0 or where a group
+    // start enters another TROWS-row block (which includes every group
+    // after a long one), so there are at most ext / TROWS + 1 runs, each
+    // packed kPackMax groups at a time; and every item owns a group.
+    // Workgroups past the items exit after building the table, which costs
+    // about a microsecond per CU each.
+    constexpr int64_t trows = 16 * NW * (64 / CG);
+    const int64_t bound = ext / (trows - 14) + ext / trows + G / kPackMax + 1;
+    const int64_t items = std::min<int64_t>(G, bound);
+    const int64_t nblocks = 8 * SPS * ((items * nsuper + 7) / 8);
     if (nblocks > INT32_MAX)
         return MXQ_ERR_INVALID_ARG;
     const size_t lds = G > 64 ? (3 * (size_t)G + 2) * sizeof(int) + (size_t)G : 0;
