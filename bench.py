@@ -53,7 +53,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-copy-ceiling", action="store_true",
                    help="skip timing the 4 GiB device-to-device copy used as the practical ceiling")
-    p.add_argument("--flush-iters", type=int, default=20,
+    p.add_argument("--flush-iters", type=int, default=0,
                    help="after the timed steps, time each kernel this many more times with a "
                         "1 GiB buffer written before every launch (cold L2 and MALL) and report "
                         "median/min/max; 0 = skip")
