@@ -17,7 +17,7 @@ import workloads
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 96
 
 
 def _groups(g, extent):
