@@ -81,19 +81,17 @@ mxq_status run_jagged_contig(const uint16_t *x, int64_t nrows, int64_t ext, int6
             x, ldx, cols, offs, G, q, ldq, scales, ss_row, ss_g);
         return launch_status();
     }
-#define MXQ_CONTIG(NR, TAIL)                                                                       \
-    jagged_contig_kernel<NR, TAIL><<<grid, block, lds, st>>>(x, ldx, rows, cols, offs, G, q, ldq,  \
-                                                            scales, ss_row, ss_g)
-    const bool tail = (ext % 8) != 0;
-    if (ext <= 2048) {
-        if (tail) MXQ_CONTIG(1, true); else MXQ_CONTIG(1, false);
-    } else if (ext <= 4096) {
-        if (tail) MXQ_CONTIG(2, true); else MXQ_CONTIG(2, false);
-    } else if (ext <= 8192) {
-        if (tail) MXQ_CONTIG(4, true); else MXQ_CONTIG(4, false);
-    } else {
-        if (tail) MXQ_CONTIG(8, true); else MXQ_CONTIG(8, false);
-    }
+#define MXQ_CONTIG(NR)                                                                             \
+    jagged_contig_kernel<NR><<<grid, block, lds, st>>>(x, ldx, rows, cols, offs, G, q, ldq, scales, \
+                                                       ss_row, ss_g)
+    if (ext <= 2048)
+        MXQ_CONTIG(1);
+    else if (ext <= 4096)
+        MXQ_CONTIG(2);
+    else if (ext <= 8192)
+        MXQ_CONTIG(4);
+    else
+        MXQ_CONTIG(8);
 #undef MXQ_CONTIG
     return launch_status();
 }

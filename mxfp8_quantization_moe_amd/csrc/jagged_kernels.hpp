@@ -162,7 +162,7 @@ __device__ __forceinline__ void store_segment(uint8_t *qr, const float *s_scale,
 // (wave, segment-slot) pairs are uniform.  Two register buffers alternate:
 // the loads of the next row are in flight while the current row is reduced,
 // scaled and stored.
-template <int NR, bool TAIL>
+template <int NR>
 __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int rows, int cols,
     const int32_t *__restrict__ offs, int G, uint8_t *__restrict__ q, int64_t ldq,
@@ -176,33 +176,21 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
     const int t = threadIdx.x;
     const int lane = t & 63;
 
-    // Without a tail (cols a multiple of 8) the row is read through a buffer
-    // descriptor: segments past the row end, and every segment of a row past
-    // the last one (descriptor range 0), read as zeros without a memory
-    // access, so the loads carry no branch.  With loads under branches the
-    // compiler waits for every outstanding load at the first use of any, i.e.
-    // for the next row's loads too, and the two buffers would not overlap.
+    // The row is read through a buffer descriptor whose range is the row's
+    // whole 8-element segments: a segment past them (the partial last one
+    // included) and every segment of a row past the last one (range 0) read
+    // as zeros without a memory access, so the loads carry no branch.  Only
+    // segments that lie wholly inside one group are used from registers; the
+    // others are read again element by element where they are reduced and
+    // stored.  With loads under branches the compiler waits for every
+    // outstanding load at the first use of any, i.e. for the next row's loads
+    // too, and the two buffers would not overlap.
     auto load_row = [&](uint4 (&d)[NR], int r) __attribute__((always_inline)) {
-        if constexpr (!TAIL) {
-            const bool ok = r < rows;
-            const auto rs = buffer_rsrc(x + (int64_t)(ok ? r : 0) * ldx, ok ? 2u * (uint32_t)cols : 0u);
+        const bool ok = r < rows;
+        const auto rs = buffer_rsrc(x + (int64_t)(ok ? r : 0) * ldx, ok ? 2u * (uint32_t)(cols & ~7) : 0u);
 #pragma unroll
-            for (int i = 0; i < NR; ++i)
-                d[i] = ldbuf16_nt(rs, 16u * (uint32_t)(i * kThreads + t));
-        } else {
-            const uint16_t *xr = x + (int64_t)r * ldx;
-#pragma unroll
-            for (int i = 0; i < NR; ++i) {
-                const int e0 = 8 * (i * kThreads + t);
-                d[i] = e0 + 8 <= cols ? ld16_nt(xr + e0) : make_uint4(0u, 0u, 0u, 0u);
-            }
-#pragma unroll
-            for (int i = 0; i < NR; ++i) {
-                const int e0 = 8 * (i * kThreads + t);
-                if (e0 < cols && e0 + 8 > cols)
-                    d[i] = load_seg(xr, e0, cols);
-            }
-        }
+        for (int i = 0; i < NR; ++i)
+            d[i] = ldbuf16_nt(rs, 16u * (uint32_t)(i * kThreads + t));
     };
 
     uint4 va[NR], vb[NR];
@@ -245,9 +233,7 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
     }
 
     auto process_row = [&](uint4 (&cur)[NR], uint4 (&nxt)[NR], int r) __attribute__((always_inline)) {
-        const int next = r + (int)gridDim.x;
-        if (!TAIL || next < rows)
-            load_row(nxt, next);
+        load_row(nxt, r + (int)gridDim.x);   // range 0 past the last row
         const uint16_t *xr = x + (int64_t)r * ldx;
         if (uni == (1u << NR) - 1u) {
             // every slot uniform: all wave maxima first (independent chains),
