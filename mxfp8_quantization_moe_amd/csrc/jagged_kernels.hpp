@@ -57,19 +57,6 @@ __device__ __forceinline__ int advance_group(const int32_t *s_offs, int G, int g
     return lo;
 }
 
-// 8 bf16 at x[e0 .. e0+8) clipped to [0, n): full 16-byte load when inside
-__device__ __forceinline__ uint4 load_seg(const uint16_t *xr, int e0, int n)
-{
-    if (e0 + 8 <= n)
-        return ld16(xr + e0);
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        if (e0 + j < n)
-            w[j >> 1] |= (uint32_t)xr[e0 + j] << (16 * (j & 1));
-    return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 // ---------------------------------------------------------------- contig
 
 // Per-segment group bookkeeping of the contig kernels.  A segment is the
@@ -331,19 +318,15 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_long_kernel(
     }
     __syncthreads();
 
+    // chunks read through a descriptor over the row's whole 8-element
+    // segments, as in jagged_contig_kernel: no load under a branch, and the
+    // partial last segment (never used from registers) reads as zeros
     uint4 v[NR];
+    const auto rs = buffer_rsrc(xr, 2u * (uint32_t)(cols & ~7));
     auto load_chunk = [&](int cbase) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            const int e0 = cbase + 8 * (i * kThreads + t);
-            v[i] = e0 + 8 <= cols ? ld16(xr + e0) : make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            const int e0 = cbase + 8 * (i * kThreads + t);
-            if (e0 < cols && e0 + 8 > cols)
-                v[i] = load_seg(xr, e0, cols);
-        }
+        for (int i = 0; i < NR; ++i)
+            v[i] = ldbuf16(rs, 2u * ((uint32_t)cbase + 8u * (uint32_t)(i * kThreads + t)));
     };
 
     for (int c = 0; c < nchunks; ++c) {

@@ -200,5 +200,10 @@ __device__ __forceinline__ uint4 ldbuf16_nt(__amdgpu_buffer_rsrc_t r, uint32_t b
     u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 2);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+__device__ __forceinline__ uint4 ldbuf16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
+{
+    u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 }  // namespace mxq
