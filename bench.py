@@ -420,7 +420,7 @@ class DeviceEvents:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         raise SystemExit(2)
     world = int(os.environ.get("WORLD_SIZE", "1"))
