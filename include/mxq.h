@@ -261,12 +261,24 @@ mxq_status mxq_quantize_blockwise(const uint16_t *x, int64_t rows, int64_t cols,
                                   int64_t ss_cb, void *stream);
 
 /*
- * Diagnostic: apply the library's own device cast (saturate to +-448, then
- * the hardware round-to-nearest-even E4M3FN conversion) to n fp32 values.
- * Used to check the device conversion against the CPU definition over whole
- * fp32 ranges.  y: n floats, out: n bytes, both device pointers.
+ * TEST-ONLY diagnostics, not part of the quantization API: the library's own
+ * device conversions applied to n fp32 values, so that tests can check them
+ * against the CPU definition over whole fp32 ranges.  y: n floats, out: n
+ * bytes, both device pointers; errors as above.
+ *
+ * mxq_debug_cast_e4m3: one value at a time, clamped to +-448, then the
+ * hardware round-to-nearest-even E4M3FN conversion.
+ * mxq_debug_cast4_e4m3: four consecutive values at a time through the packed
+ * conversion the quantization kernels use (out 4-byte aligned):
+ *   unclamped == 0  the clamped form of the e8m0 (MX) paths, any finite y;
+ *   unclamped == 1  the form of the fp32-multiplier paths, which omits the
+ *                   clamp: defined only for |y| < 464, the range those paths
+ *                   can produce (|RN32(x * 448 / max(amax, eps))| <= 448 +
+ *                   2^-15 whenever |x| <= amax).
  */
 mxq_status mxq_debug_cast_e4m3(const float *y, int64_t n, uint8_t *out, void *stream);
+mxq_status mxq_debug_cast4_e4m3(const float *y, int64_t n, uint8_t *out, int32_t unclamped,
+                                void *stream);
 
 #ifdef __cplusplus
 }

@@ -17,7 +17,8 @@ from __future__ import annotations
 from . import _capi
 from ._capi import (MXQ_ERR_INVALID_ARG, MXQ_ERR_LAUNCH, MXQ_ERR_UNSUPPORTED, MXQ_MAX_GROUPS,
                     MXQ_OK, MXQ_SCALE_FLOOR, MXQ_SCALE_RCEIL, LibraryMissing,
-                    mxq_abi_version, mxq_debug_cast_e4m3, mxq_quantize_blockwise,
+                    mxq_abi_version, mxq_debug_cast4_e4m3, mxq_debug_cast_e4m3,
+                    mxq_quantize_blockwise,
                     mxq_quantize_jagged_colwise, mxq_quantize_jagged_mx_colwise,
                     mxq_quantize_jagged_mx_rowwise, mxq_quantize_jagged_rowwise,
                     mxq_quantize_mx_3d_colwise, mxq_quantize_mx_rowwise,
@@ -31,6 +32,7 @@ __all__ = [
     "mxq_quantize_jagged_rowwise", "mxq_quantize_jagged_colwise", "mxq_quantize_mx_3d_colwise",
     "mxq_quantize_mx_rowwise", "mxq_quantize_jagged_mx_rowwise", "mxq_quantize_jagged_mx_colwise",
     "mxq_relayout_mx_scales_grouped", "mxq_quantize_blockwise", "mxq_debug_cast_e4m3",
+    "mxq_debug_cast4_e4m3", "debug_cast4_e4m3",
     "mxq_abi_version", "LibraryMissing",
 ]
 
@@ -273,4 +275,18 @@ def debug_cast_e4m3(y, *, stream=None):
     out = torch.empty(y.shape, dtype=torch.uint8, device=y.device)
     _check(mxq_debug_cast_e4m3(y.data_ptr(), y.numel(), out.data_ptr(), _stream(y, stream)),
            "mxq_debug_cast_e4m3")
+    return out
+
+
+def debug_cast4_e4m3(y, unclamped: bool, *, stream=None):
+    """Test-only: the packed conversion of the quantization kernels on an fp32
+    CUDA tensor, four values at a time; ``unclamped`` selects the form of
+    the fp32-multiplier paths (defined for |y| < 464 only), else the clamped
+    form of the e8m0 paths.  Returns uint8 codes."""
+    torch = _torch()
+    if y.dtype != torch.float32 or not y.is_cuda or not y.is_contiguous():
+        raise TypeError("y must be a contiguous float32 CUDA tensor")
+    out = torch.empty(y.shape, dtype=torch.uint8, device=y.device)
+    _check(mxq_debug_cast4_e4m3(y.data_ptr(), y.numel(), out.data_ptr(), 1 if unclamped else 0,
+                                _stream(y, stream)), "mxq_debug_cast4_e4m3")
     return out

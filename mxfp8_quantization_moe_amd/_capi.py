@@ -47,6 +47,7 @@ SIGNATURES = {
     "mxq_quantize_blockwise": [_vp, _i64, _i64, _i64, _i64, _i32, _i32, _vp, _i64, _i64, _vp,
                                _i64, _i64, _vp],
     "mxq_debug_cast_e4m3": [_vp, _i64, _vp, _vp],
+    "mxq_debug_cast4_e4m3": [_vp, _i64, _vp, _i32, _vp],
 }
 RESTYPES = {"mxq_status_string": ctypes.c_char_p}
 
@@ -98,3 +99,4 @@ mxq_quantize_jagged_mx_colwise = _fwd("mxq_quantize_jagged_mx_colwise")
 mxq_relayout_mx_scales_grouped = _fwd("mxq_relayout_mx_scales_grouped")
 mxq_quantize_blockwise = _fwd("mxq_quantize_blockwise")
 mxq_debug_cast_e4m3 = _fwd("mxq_debug_cast_e4m3")
+mxq_debug_cast4_e4m3 = _fwd("mxq_debug_cast4_e4m3")

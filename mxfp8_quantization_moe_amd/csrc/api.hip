@@ -516,6 +516,38 @@ __global__ void debug_cast_kernel(const float *__restrict__ y, int64_t n, uint8_
     for (int64_t k = i; k < n; k += stride)
         out[k] = (uint8_t)mxq::cvt1(y[k]);
 }
+
+// four consecutive values per thread through the packed conversions the
+// kernels use: cvt4 (clamped; e8m0 paths) or cvt4_nosat (fp32-multiplier
+// paths); a short last quad is padded with zeros and stored byte by byte
+__global__ void debug_cast4_kernel(const float *__restrict__ y, int64_t n, uint8_t *__restrict__ out,
+                                   int unclamped)
+{
+    const int64_t nq = (n + 3) / 4;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t k = i; k < nq; k += stride) {
+        const int64_t e = 4 * k;
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            v[j] = e + j < n ? y[e + j] : 0.0f;
+        const uint32_t r = unclamped ? mxq::cvt4_nosat(v[0], v[1], v[2], v[3])
+                                     : mxq::cvt4(v[0], v[1], v[2], v[3]);
+        if (e + 4 <= n) {
+            *reinterpret_cast<uint32_t *>(out + e) = r;
+        } else {
+            for (int j = 0; e + j < n; ++j)
+                out[e + j] = (uint8_t)(r >> (8 * j));
+        }
+    }
+}
+
+unsigned debug_grid(int64_t items)
+{
+    int64_t blocks = (items + 255) / 256;
+    return (unsigned)(blocks > 65536 ? 65536 : blocks);
+}
 }  // namespace
 
 extern "C" mxq_status mxq_debug_cast_e4m3(const float *y, int64_t n, uint8_t *out, void *stream)
@@ -526,9 +558,20 @@ extern "C" mxq_status mxq_debug_cast_e4m3(const float *y, int64_t n, uint8_t *ou
         return MXQ_OK;
     if (!y || !out)
         return MXQ_ERR_INVALID_ARG;
-    int64_t blocks = (n + 255) / 256;
-    if (blocks > 65536)
-        blocks = 65536;
-    debug_cast_kernel<<<dim3((unsigned)blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream)>>>(y, n, out);
+    debug_cast_kernel<<<dim3(debug_grid(n)), dim3(256), 0, reinterpret_cast<hipStream_t>(stream)>>>(y, n, out);
+    return launch_status();
+}
+
+extern "C" mxq_status mxq_debug_cast4_e4m3(const float *y, int64_t n, uint8_t *out, int32_t unclamped,
+                                           void *stream)
+{
+    if (n < 0 || (unclamped != 0 && unclamped != 1))
+        return MXQ_ERR_INVALID_ARG;
+    if (n == 0)
+        return MXQ_OK;
+    if (!y || !out || (reinterpret_cast<uintptr_t>(out) & 3u) != 0)
+        return MXQ_ERR_INVALID_ARG;
+    debug_cast4_kernel<<<dim3(debug_grid((n + 3) / 4)), dim3(256), 0, reinterpret_cast<hipStream_t>(stream)>>>(
+        y, n, out, unclamped);
     return launch_status();
 }

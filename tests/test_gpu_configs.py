@@ -1,148 +1,141 @@
 """GPU parity at the full workload sizes, in the launch configuration
-bench.py times.  The GPU output of the whole tensor is compared byte for byte
-with the oracle on sampled rows / columns / experts (the oracle computes those
-one by one, each sample being a complete reduction unit), and whole-output
-properties are checked at every size: no NaN codes, every scale of every
-group or block equals the multiplier of that group's exact amax, and, for the
-MX sweep, the expert-prefix property (running on W[:E] reproduces the first
-E experts of the E=64 run)."""
+bench.py times: every q byte and every scale of the five workloads is
+compared with the oracle, byte for byte.
+
+The oracle runs over the independent units of each tensor (experts, row
+blocks, column blocks) in parallel host processes (``oracle_pool``); put
+back together, the pieces are its output for the whole tensor.  The MX 3D
+sweep is checked at every E in {1, 2, 4, 16, 64}, each run expert by expert
+against the oracle (the experts of W_E are the first E experts of W_64, so
+the oracle quantizes each expert once)."""
 import numpy as np
 import pytest
 import torch
 
-import oracle
+import mxfp8_quantization_moe_amd as mxq
+import oracle_pool
 import workloads
-from gpu_helpers import (CANARY, assert_same_bytes, bf16_dev, blockwise, i32_dev, jagged_colwise,
-                         jagged_rowwise, mx_3d_colwise)
+from gpu_helpers import (CANARY, SCALE_MODES, assert_same_bytes, bf16_dev, blockwise, i32_dev,
+                         jagged_colwise, jagged_rowwise, stream_handle)
 
 pytestmark = pytest.mark.gpu
-
-
-def _fp32_scales_from_amax_bits(amax16: np.ndarray) -> np.ndarray:
-    amax = workloads.bf16_bits_to_f32(amax16.astype(np.uint16))
-    flat = np.unique(amax)
-    table = dict(zip(flat.tolist(), oracle.fp32_scale(flat).tolist()))
-    return np.vectorize(table.__getitem__, otypes=[np.float32])(amax)
 
 
 def _no_nan_codes(q: np.ndarray):
     assert not np.any((q & 0x7F) == 0x7F)
 
 
-def _sample(n, k, seed):
-    g = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, n - 1], g.choice(n, size=k, replace=False)]))
-
-
-def test_moe_bwd_rowwise_grad_out_t():
+@pytest.fixture(scope="module")
+def moe():
     go = workloads.moe_grad_out_t()
-    offs = workloads.moe_offsets()
-    q, s = jagged_rowwise(bf16_dev(go), i32_dev(offs))
-    rows = _sample(go.shape[0], 40, 1)
-    oq, os_ = oracle.quantize_jagged_rowwise(go[rows], offs, canary=CANARY)
-    assert_same_bytes(q[rows], oq, "moe_bwd rowwise q (sampled rows)")
-    assert_same_bytes(s[rows], os_, "moe_bwd rowwise scales (sampled rows)")
-    # every (row, group) scale is the multiplier of the group's exact amax
-    mag = go & 0x7FFF
-    lo = 0
-    for g, hi in enumerate(offs.tolist()):
-        amax = mag[:, lo:hi].max(axis=1) if hi > lo else np.zeros(go.shape[0], np.uint16)
-        want = _fp32_scales_from_amax_bits(amax)
-        assert_same_bytes(s[:, g].copy(), want, f"rowwise scales of group {g}")
-        lo = hi
-    _no_nan_codes(q)
-
-
-def test_moe_bwd_rowwise_transposed_view_is_identical():
-    """grad_out^T handed over as a transposed view of a row-major grad_out."""
-    go = workloads.moe_grad_out_t()
-    offs = workloads.moe_offsets()
-    q1, s1 = jagged_rowwise(bf16_dev(go), i32_dev(offs))
-    base = bf16_dev(np.ascontiguousarray(go.T))          # grad_out (16384, 4096) row-major
-    q2, s2 = jagged_rowwise(base.t(), i32_dev(offs))
-    assert np.array_equal(q1, q2)
-    assert np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
-
-
-def test_moe_bwd_colwise_x():
     x = workloads.moe_x()
     offs = workloads.moe_offsets()
-    q, s = jagged_colwise(bf16_dev(x), i32_dev(offs))
-    cols = _sample(x.shape[1], 40, 2)
-    oq, os_ = oracle.quantize_jagged_colwise(np.ascontiguousarray(x[:, cols]), offs, canary=CANARY)
-    assert_same_bytes(q[:, cols], oq, "moe_bwd colwise q (sampled columns)")
-    assert_same_bytes(s[:, cols], os_, "moe_bwd colwise scales (sampled columns)")
-    mag = x & 0x7FFF
-    lo = 0
-    for g, hi in enumerate(offs.tolist()):
-        amax = mag[lo:hi].max(axis=0) if hi > lo else np.zeros(x.shape[1], np.uint16)
-        want = _fp32_scales_from_amax_bits(amax)
-        assert_same_bytes(s[g].copy(), want, f"colwise scales of group {g}")
-        lo = hi
+    return {"go": go, "x": x, "offs": offs,
+            "rowwise": oracle_pool.split_op("quantize_jagged_rowwise", go, offs, canary=CANARY),
+            "colwise": oracle_pool.split_op("quantize_jagged_colwise", x, offs, canary=CANARY)}
+
+
+def test_moe_bwd_rowwise_grad_out_t(moe):
+    q, s = jagged_rowwise(bf16_dev(moe["go"]), i32_dev(moe["offs"]))
+    oq, os_ = moe["rowwise"]
+    assert_same_bytes(q, oq, "moe_bwd rowwise q")
+    assert_same_bytes(s, os_, "moe_bwd rowwise scales")
     _no_nan_codes(q)
 
 
-@pytest.mark.parametrize("mode", ["floor", "rceil"])
-def test_mx3d_e8(mode):
+def test_moe_bwd_rowwise_transposed_view(moe):
+    """grad_out^T handed over as a transposed view of a row-major grad_out."""
+    base = bf16_dev(np.ascontiguousarray(moe["go"].T))   # grad_out (16384, 4096) row-major
+    q, s = jagged_rowwise(base.t(), i32_dev(moe["offs"]))
+    oq, os_ = moe["rowwise"]
+    assert_same_bytes(q, oq, "moe_bwd rowwise q (transposed view)")
+    assert_same_bytes(s, os_, "moe_bwd rowwise scales (transposed view)")
+
+
+def test_moe_bwd_colwise_x(moe):
+    q, s = jagged_colwise(bf16_dev(moe["x"]), i32_dev(moe["offs"]))
+    oq, os_ = moe["colwise"]
+    assert_same_bytes(q, oq, "moe_bwd colwise q")
+    assert_same_bytes(s, os_, "moe_bwd colwise scales")
+    _no_nan_codes(q)
+
+
+def _mx3d_launch(dev_w, E, mode):
+    """The bench's launch: per-expert column-major q (N*K, 1, N), scales
+    (E, N/32, K) contiguous; canary-filled device buffers."""
+    _, N, K = dev_w.shape
+    q = torch.full((E * N * K,), CANARY, dtype=torch.uint8, device="cuda")
+    s = torch.full((E * (N // 32) * K,), CANARY, dtype=torch.uint8, device="cuda")
+    code = mxq.mxq_quantize_mx_3d_colwise(dev_w.data_ptr(), E, N, K, N * K, K, 1, q.data_ptr(),
+                                          N * K, 1, N, s.data_ptr(), (N // 32) * K, K, 1,
+                                          SCALE_MODES[mode], stream_handle())
+    assert code == 0, code
+    torch.cuda.synchronize()
+    return q, s
+
+
+def _expert_out(q, s, e, N, K):
+    """Expert e's q in logical (N, K) order and its scales (N/32, K)."""
+    qe = q[e * N * K:(e + 1) * N * K].view(K, N).t().contiguous().cpu().numpy()
+    se = s[e * (N // 32) * K:(e + 1) * (N // 32) * K].view(N // 32, K).cpu().numpy()
+    return qe, se
+
+
+def test_mx3d_e8_floor_and_rceil():
     E, N, K = 8, 8192, 5120
-    w = np.stack([workloads.mx3d_expert(e) for e in range(E)])
-    q, s = mx_3d_colwise(bf16_dev(w), mode=mode)
-    ks = _sample(K, 24, 3)
-    for e in (0, 3, 7):
-        oq, os_ = oracle.quantize_mx_3d_colwise(np.ascontiguousarray(w[e:e + 1][:, :, ks]), mode=mode)
-        assert_same_bytes(q[e:e + 1][:, :, ks], oq, f"mx3d q expert {e} (sampled columns)")
-        assert_same_bytes(s[e:e + 1][:, :, ks], os_, f"mx3d scales expert {e} (sampled columns)")
-    _no_nan_codes(q)
-
-
-@pytest.mark.timeout(600)
-def test_mx3d_sweep_prefixes_up_to_e64():
-    """E in {1, 2, 4, 16, 64} at (E, 8192, 5120) with zero and 2^20 blocks.
-    The E=64 run is checked against the oracle on sampled experts/columns,
-    and every smaller E must reproduce the first E experts of it."""
-    N, K = 8192, 5120
-    Emax = 64
-    dev_w = torch.empty((Emax, N, K), dtype=torch.bfloat16, device="cuda")
-    host = {}
-    for e in range(Emax):
-        bits = workloads.mx3d_sweep_expert(e)
+    dev_w = torch.empty((E, N, K), dtype=torch.bfloat16, device="cuda")
+    want = {}
+    for e, bits, out in oracle_pool.mx3d_experts(range(E), sweep=False, modes=("floor", "rceil")):
         dev_w[e].copy_(bf16_dev(bits))
-        if e in (0, 1, 15, 63):
-            host[e] = bits
-    q64, s64 = mx_3d_colwise(dev_w)
-    ks = _sample(K, 16, 4)
-    for e, bits in host.items():
-        oq, os_ = oracle.quantize_mx_3d_colwise(np.ascontiguousarray(bits[None][:, :, ks]))
-        assert_same_bytes(q64[e:e + 1][:, :, ks], oq, f"sweep q expert {e}")
-        assert_same_bytes(s64[e:e + 1][:, :, ks], os_, f"sweep scales expert {e}")
-    assert (s64 == 0).sum() > 0                      # all-zero blocks hit the minimum code
-    _no_nan_codes(q64)
-    for E in (1, 2, 4, 16):
-        qE, sE = mx_3d_colwise(dev_w[:E])
-        assert np.array_equal(qE, q64[:E]), E
-        assert np.array_equal(sE, s64[:E]), E
+        want[e] = out
+    for mode in ("floor", "rceil"):
+        q, s = _mx3d_launch(dev_w, E, mode)
+        for e in range(E):
+            qe, se = _expert_out(q, s, e, N, K)
+            assert_same_bytes(qe, want[e][mode][0], f"mx3d {mode} q expert {e}")
+            assert_same_bytes(se, want[e][mode][1], f"mx3d {mode} scales expert {e}")
+            _no_nan_codes(qe)
+        del q, s
+
+
+@pytest.mark.timeout(900)
+def test_mx3d_sweep_every_e_every_expert():
+    """E in {1, 2, 4, 16, 64} at (E, 8192, 5120) with zero and 2^20 blocks:
+    each run's every expert against the oracle."""
+    N, K = 8192, 5120
+    Es = (64, 16, 4, 2, 1)
+    dev_w = torch.empty((max(Es), N, K), dtype=torch.bfloat16, device="cuda")
+    want = {}
+    for e, bits, out in oracle_pool.mx3d_experts(range(max(Es)), sweep=True):
+        dev_w[e].copy_(bf16_dev(bits))
+        want[e] = out["floor"]
+    zero_blocks = 0
+    for E in Es:
+        q, s = _mx3d_launch(dev_w[:E], E, "floor")
+        for e in range(E):
+            qe, se = _expert_out(q, s, e, N, K)
+            assert_same_bytes(qe, want[e][0], f"sweep E={E} q expert {e}")
+            assert_same_bytes(se, want[e][1], f"sweep E={E} scales expert {e}")
+            if E == max(Es):
+                zero_blocks += int((se == 0).sum())
+        del q, s
+        torch.cuda.synchronize()
+    assert zero_blocks > 0                      # all-zero blocks hit the minimum code
 
 
 def test_blockwise_act_1x128():
     a = workloads.blockwise_act()
     q, s = blockwise(bf16_dev(a), 1, 128)
-    rows = _sample(a.shape[0], 40, 5)
-    oq, os_ = oracle.quantize_blockwise(a[rows], 1, 128)
-    assert_same_bytes(q[rows], oq, "blockwise 1x128 q (sampled rows)")
-    assert_same_bytes(s[rows], os_, "blockwise 1x128 scales (sampled rows)")
-    amax = (a & 0x7FFF).reshape(a.shape[0], -1, 128).max(axis=2)
-    assert_same_bytes(s, _fp32_scales_from_amax_bits(amax), "blockwise 1x128 all scales")
+    oq, os_ = oracle_pool.split_op("quantize_blockwise", a, 1, 128)
+    assert_same_bytes(q, oq, "blockwise 1x128 q")
+    assert_same_bytes(s, os_, "blockwise 1x128 scales")
     _no_nan_codes(q)
 
 
 def test_blockwise_weight_128x128():
     w = workloads.blockwise_weight()
     q, s = blockwise(bf16_dev(w), 128, 128)
-    for rb in (0, 13, 31):
-        sl = slice(128 * rb, 128 * rb + 128)
-        oq, os_ = oracle.quantize_blockwise(np.ascontiguousarray(w[sl]), 128, 128)
-        assert_same_bytes(q[sl], oq, f"blockwise 128x128 q (block row {rb})")
-        assert_same_bytes(s[rb:rb + 1], os_, f"blockwise 128x128 scales (block row {rb})")
-    amax = (w & 0x7FFF).reshape(32, 128, 32, 128).max(axis=(1, 3))
-    assert_same_bytes(s, _fp32_scales_from_amax_bits(amax), "blockwise 128x128 all scales")
+    oq, os_ = oracle_pool.split_op("quantize_blockwise", w, 128, 128, align=128)
+    assert_same_bytes(q, oq, "blockwise 128x128 q")
+    assert_same_bytes(s, os_, "blockwise 128x128 scales")
     _no_nan_codes(q)

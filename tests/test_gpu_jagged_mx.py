@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle
+import oracle_pool
 import workloads
 from gpu_helpers import (CANARY, adversarial, assert_same_bytes, bf16_dev, i32_dev,
                          jagged_mx_colwise, jagged_mx_rowwise, random_offsets)
@@ -110,36 +111,31 @@ def test_jagged_mx_empty_extents():
     assert np.all(s == CANARY)
 
 
-def _sample(n, k, seed):
-    g = np.random.default_rng(seed)
-    return np.unique(np.concatenate([[0, n - 1], g.choice(n, size=k, replace=False)]))
-
-
-def test_moe_bwd_grad_out_t_rowwise():
-    """grad_out^T (4096, 16384) with the 8 MoE token groups: sampled rows
-    against the oracle, and every row writes exactly sum ceil(n_g/32) scale
-    entries."""
+@pytest.mark.parametrize("mode", ["floor", "rceil"])
+def test_moe_bwd_grad_out_t_rowwise(mode):
+    """grad_out^T (4096, 16384) with the 8 MoE token groups, every byte and
+    scale against the oracle (run over row blocks in parallel); every row
+    writes exactly sum ceil(n_g/32) scale entries."""
     go = workloads.moe_grad_out_t()
     offs = workloads.moe_offsets()
-    q, s = jagged_mx_rowwise(bf16_dev(go), i32_dev(offs))
-    rows = _sample(go.shape[0], 24, 11)
-    oq, os_ = oracle.quantize_jagged_mx_rowwise(go[rows], offs, canary=CANARY)
-    assert_same_bytes(q[rows], oq, "moe grad_out^T jagged mx q (sampled rows)")
-    assert_same_bytes(s[rows], os_, "moe grad_out^T jagged mx scales (sampled rows)")
+    q, s = jagged_mx_rowwise(bf16_dev(go), i32_dev(offs), mode)
+    oq, os_ = oracle_pool.split_op("quantize_jagged_mx_rowwise", go, offs, mode=mode, canary=CANARY)
+    assert_same_bytes(q, oq, f"moe grad_out^T jagged mx {mode} q")
+    assert_same_bytes(s, os_, f"moe grad_out^T jagged mx {mode} scales")
     sizes = np.diff(np.concatenate([[0], offs]))
     nb = int(sum((n + 31) // 32 for n in sizes))
     assert np.all(s[:, nb:] == CANARY)
     assert not np.any((q & 0x7F) == 0x7F)
 
 
-def test_moe_bwd_x_colwise():
+@pytest.mark.parametrize("mode", ["floor", "rceil"])
+def test_moe_bwd_x_colwise(mode):
     x = workloads.moe_x()
     offs = workloads.moe_offsets()
-    q, s = jagged_mx_colwise(bf16_dev(x), i32_dev(offs))
-    cols = _sample(x.shape[1], 24, 12)
-    oq, os_ = oracle.quantize_jagged_mx_colwise(np.ascontiguousarray(x[:, cols]), offs, canary=CANARY)
-    assert_same_bytes(q[:, cols], oq, "moe x jagged mx q (sampled columns)")
-    assert_same_bytes(s[:, cols], os_, "moe x jagged mx scales (sampled columns)")
+    q, s = jagged_mx_colwise(bf16_dev(x), i32_dev(offs), mode)
+    oq, os_ = oracle_pool.split_op("quantize_jagged_mx_colwise", x, offs, mode=mode, canary=CANARY)
+    assert_same_bytes(q, oq, f"moe x jagged mx {mode} q")
+    assert_same_bytes(s, os_, f"moe x jagged mx {mode} scales")
     sizes = np.diff(np.concatenate([[0], offs]))
     nb = int(sum((n + 31) // 32 for n in sizes))
     assert np.all(s[nb:] == CANARY)
