@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <utility>
 
 #include "mxq.h"
 #include "block_kernels.hpp"
@@ -454,10 +455,9 @@ mxq_status mxq_quantize_blockwise(const uint16_t *x, int64_t rows, int64_t cols,
         return MXQ_ERR_INVALID_ARG;
     if (rows % block_r != 0 || cols % block_c != 0)
         return MXQ_ERR_INVALID_ARG;
-    const bool b1x128 = block_r == 1 && block_c == 128;
-    const bool b128x128 = block_r == 128 && block_c == 128;
-    const bool b128x1 = block_r == 128 && block_c == 1;
-    if (!b1x128 && !b128x128 && !b128x1)
+    const bool known = (block_r == 1 && block_c == 128) || (block_r == 128 && block_c == 128) ||
+                       (block_r == 128 && block_c == 1);
+    if (!known)
         return MXQ_ERR_UNSUPPORTED;
     if (rows == 0 || cols == 0)
         return MXQ_OK;
@@ -467,11 +467,25 @@ mxq_status mxq_quantize_blockwise(const uint16_t *x, int64_t rows, int64_t cols,
         return MXQ_ERR_INVALID_ARG;
     if (rows > INT32_MAX || cols > INT32_MAX)
         return MXQ_ERR_INVALID_ARG;
+    // a column-major x (a transposed view of a row-major tensor) is the
+    // row-major tensor with the block shape, the q strides and the scale
+    // strides transposed
+    if (sx_c != 1 && sx_r == 1) {
+        std::swap(rows, cols);
+        std::swap(sx_r, sx_c);
+        std::swap(block_r, block_c);
+        std::swap(sq_r, sq_c);
+        std::swap(ss_rb, ss_cb);
+    }
+    if (sx_c != 1 || !(sq_c == 1 || sq_r == 1))
+        return MXQ_ERR_UNSUPPORTED;
+    if (!aligned16(x) || sx_r % 8 != 0 || !aligned16(q))
+        return MXQ_ERR_INVALID_ARG;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    if (b1x128) {
-        if (!(sx_c == 1 && sq_c == 1))
-            return MXQ_ERR_UNSUPPORTED;
-        if (!aligned16(x) || !aligned16(q) || sx_r % 8 != 0 || sq_r % 16 != 0)
+    const bool qrow = sq_c == 1 && (sq_r != 1 || rows == 1);
+    if (block_r == 1 && qrow) {
+        // 1 x 128 along the unit stride into row-major q
+        if (rows > 1 && sq_r % 16 != 0)
             return MXQ_ERR_INVALID_ARG;
         constexpr int U = 4, LPB = 8;
         const int64_t nbpr = cols / 128, nblocks = rows * nbpr;
@@ -483,24 +497,33 @@ mxq_status mxq_quantize_blockwise(const uint16_t *x, int64_t rows, int64_t cols,
             x, sx_r, nbpr, nblocks, q, sq_r, scales, ss_rb, ss_cb, 0);
         return launch_status();
     }
-    // (128, 128) and (128, 1): row-major in, column-major out
-    if (!(sx_c == 1 && sq_r == 1))
-        return MXQ_ERR_UNSUPPORTED;
-    if (!aligned16(x) || !aligned16(q) || cols % 8 != 0 || sx_r % 8 != 0 || sq_c % 16 != 0)
+    // the 128 x 256 tile kernel: 16-row pieces of 8 columns per lane
+    if (cols % 8 != 0 || rows % 16 != 0)
         return MXQ_ERR_INVALID_ARG;
-    const int64_t tiles_r = rows / 128, tiles_c = (cols + 255) / 256;
+    const int64_t ldq = qrow ? sq_r : sq_c;
+    if (qrow ? (rows > 1 && ldq % 8 != 0) : (cols > 1 && ldq % 16 != 0))
+        return MXQ_ERR_INVALID_ARG;
+    const int64_t tiles_r = (rows + 127) / 128, tiles_c = (cols + 255) / 256;
     const int64_t nblocks = tiles_r * tiles_c;
     if (nblocks > INT32_MAX)
         return MXQ_ERR_INVALID_ARG;
-    const int nt = line_aligned(q, sq_c, 0);
-    if (b128x128)
-        block_strided_kernel<128, 128, false><<<dim3((unsigned)nblocks), dim3(kBlockThreads), 0, st>>>(
-            x, 0, sx_r, (int)rows, (int)cols, q, 0, sq_c, scales, 0, ss_rb, ss_cb, (int)tiles_r,
-            (int)tiles_c, 0, nt);
+    const dim3 grid((unsigned)nblocks), block(kBlockThreads);
+    const int nt = qrow ? 0 : line_aligned(q, ldq, 0);
+#define MXQ_STRIDED(BR, BC, QR)                                                                   \
+    block_strided_kernel<BR, BC, false, QR><<<grid, block, 0, st>>>(                              \
+        x, 0, sx_r, (int)rows, (int)cols, q, 0, ldq, scales, 0, ss_rb, ss_cb, (int)tiles_r,        \
+        (int)tiles_c, 0, nt)
+    if (block_r == 1)
+        MXQ_STRIDED(1, 128, false);
+    else if (block_c == 128 && qrow)
+        MXQ_STRIDED(128, 128, true);
+    else if (block_c == 128)
+        MXQ_STRIDED(128, 128, false);
+    else if (qrow)
+        MXQ_STRIDED(128, 1, true);
     else
-        block_strided_kernel<128, 1, false><<<dim3((unsigned)nblocks), dim3(kBlockThreads), 0, st>>>(
-            x, 0, sx_r, (int)rows, (int)cols, q, 0, sq_c, scales, 0, ss_rb, ss_cb, (int)tiles_r,
-            (int)tiles_c, 0, nt);
+        MXQ_STRIDED(128, 1, false);
+#undef MXQ_STRIDED
     return launch_status();
 }
 

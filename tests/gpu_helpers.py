@@ -121,11 +121,16 @@ def mx_rowwise(x: torch.Tensor, stream=None, expect=0, mode="floor"):
     return _gather_u8(q, (rows, cols), (ldq, 1)), _gather_u8(s, (rows, cols // 32), (cols // 32, 1))
 
 
-def blockwise(x: torch.Tensor, br: int, bc: int, stream=None, expect=0):
+def blockwise(x: torch.Tensor, br: int, bc: int, stream=None, expect=0, qlayout=None):
+    """q row-major (qlayout "row"; the default for 1 x 128) or column-major
+    ("col"; the default otherwise), pitch padded to 16 bytes; scales
+    (rows/br, cols/bc) row-major.  x may be any view with a unit stride."""
     rows, cols = x.shape
     nrb, ncb = rows // br, cols // bc
     s = f32_canary(nrb * ncb)
-    if br == 1:
+    if qlayout is None:
+        qlayout = "row" if br == 1 else "col"
+    if qlayout == "row":
         ldq = round16(cols)
         q = u8_canary(rows * ldq)
         qs = (ldq, 1)

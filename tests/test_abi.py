@@ -107,8 +107,11 @@ def test_mx_and_blockwise_reject_bad_arguments(lib):
     bw = lib.mxq_quantize_blockwise
     assert bw(A, 128, 256, 256, 1, 1, 64, A, 256, 1, A, 4, 1, None) == 2                # 1x64
     assert bw(A, 100, 256, 256, 1, 128, 128, A, 1, 112, A, 2, 1, None) == 1             # rows % 128
-    assert bw(A, 128, 256, 256, 1, 1, 128, A, 1, 128, A, 2, 1, None) == 2               # 1x128 col-major
-    assert bw(A, 128, 256, 256, 1, 128, 128, A, 256, 1, A, 2, 1, None) == 2             # 128x128 row-major
+    assert bw(A, 128, 256, 512, 2, 1, 128, A, 256, 1, A, 2, 1, None) == 2               # x: no unit stride
+    assert bw(A, 128, 256, 256, 1, 128, 128, A, 512, 2, A, 2, 1, None) == 2             # q: no unit stride
+    assert bw(A, 120, 256, 256, 1, 1, 128, A, 1, 128, A, 2, 1, None) == 1               # 1x128 col-major, rows % 16
+    assert bw(A, 256, 120, 1, 256, 128, 1, A, 120, 1, A, 120, 1, None) == 1             # its transposed view
+    assert bw(A, 128, 256, 256, 1, 128, 128, A, 252, 1, A, 2, 1, None) == 1             # row-major q pitch % 8
     assert bw(A, 0, 256, 256, 1, 128, 128, A, 1, 16, A, 2, 1, None) == 0                # empty
 
 

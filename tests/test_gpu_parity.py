@@ -191,6 +191,36 @@ def test_blockwise(br, bc, rows, cols):
     assert_same_bytes(s, os_, f"blockwise {br}x{bc} scales")
 
 
+@pytest.mark.parametrize("qlayout", ["row", "col"])
+@pytest.mark.parametrize("view", ["row_major", "transposed"])
+@pytest.mark.parametrize("br,bc,rows,cols", [
+    (1, 128, 16, 128), (1, 128, 272, 640), (1, 128, 400, 1152),
+    (128, 128, 128, 128), (128, 128, 384, 640),
+    (128, 1, 128, 16), (128, 1, 256, 328),
+])
+def test_blockwise_every_layout(br, bc, rows, cols, view, qlayout):
+    """Every block shape with x row-major or a transposed view of a
+    row-major tensor, into row-major or column-major q: the layouts the
+    blockwise backward's transposed operands need, read in place."""
+    x = adversarial((rows, cols), 900 + rows + cols + br)
+    x[:br, :bc] = 0                                             # zero block
+    if view == "row_major":
+        dx = bf16_dev(x)
+    else:
+        dx = bf16_dev(np.ascontiguousarray(x.T)).t()          # x as a transposed view
+        assert dx.stride(0) == 1
+    if view == "transposed" and qlayout == "row" and (br, bc) == (128, 1) and cols % 16:
+        # 1 x 128 blocks of the underlying tensor into its column-major q:
+        # the tile kernel takes that tensor's rows (these columns) in 16s
+        blockwise(dx, br, bc, qlayout=qlayout, expect=1)
+        return
+    q, s = blockwise(dx, br, bc, qlayout=qlayout)
+    oq, os_ = oracle.quantize_blockwise(x, br, bc)
+    what = f"blockwise {br}x{bc} {view} -> {qlayout}-major"
+    assert_same_bytes(q, oq, what + " q")
+    assert_same_bytes(s, os_, what + " scales")
+
+
 def test_no_nan_codes_anywhere():
     x = adversarial((256, 1024), 9)
     for br, bc in ((1, 128), (128, 128)):

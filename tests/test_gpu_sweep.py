@@ -90,13 +90,20 @@ def test_fixed_blocks(k):
     assert_same_bytes(s, os_, f"mx rowwise case {k} scales")
 
     br, bc = [(1, 128), (128, 128), (128, 1)][k % 3]
-    rows = br * int(g.integers(1, 300 if br == 1 else 5))
-    cols = bc * int(g.integers(1, 10)) if bc == 128 else 8 * int(g.integers(1, 100))
+    view = ("row_major", "transposed")[(k // 3) % 2]
+    qlayout = ("row", "col")[(k // 6) % 2]
+    # the tile kernel (every layout but 1 x 128 into row-major q) takes rows
+    # in 16s; the transposed view swaps the roles of rows and columns
+    m_r = 16 if br == 1 else br
+    m_c = bc if bc == 128 else (16 if view == "transposed" and qlayout == "row" else 8)
+    rows = m_r * int(g.integers(1, 40 if br == 1 else 5))
+    cols = m_c * int(g.integers(1, 10 if bc == 128 else 60))
     x = adversarial((rows, cols), 7800 + k)
-    q, s = blockwise(bf16_dev(x), br, bc)
+    dx = bf16_dev(x) if view == "row_major" else bf16_dev(np.ascontiguousarray(x.T)).t()
+    q, s = blockwise(dx, br, bc, qlayout=qlayout)
     oq, os_ = oracle.quantize_blockwise(x, br, bc)
-    assert_same_bytes(q, oq, f"blockwise {br}x{bc} case {k} q")
-    assert_same_bytes(s, os_, f"blockwise {br}x{bc} case {k} scales")
+    assert_same_bytes(q, oq, f"blockwise {br}x{bc} {view} -> {qlayout} case {k} q")
+    assert_same_bytes(s, os_, f"blockwise {br}x{bc} {view} -> {qlayout} case {k} scales")
 
 
 @pytest.mark.parametrize("k", range(N_CASES))
