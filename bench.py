@@ -1,31 +1,42 @@
 #!/usr/bin/env python3
 """Throughput benchmark of the fp8 quantization hot path on one MI355X.
 
-Default workload (``moe_bwd``): the MoE backward grad_weight operands — jagged
-rowwise quantization of grad_out^T (4096, 16384) plus jagged colwise
-quantization of x (16384, 4096), the same 8 token groups for both, bf16 in,
-e4m3 + fp32 per-group scales out.  One step = both launches.  Other
-workloads (``--workload``): ``moe_bwd_mx`` (the same operands as jagged
-MXFP8 blocks), ``mx3d`` (E=8 expert weights, 32x1 MXFP8),
-``mx3d_e{1,2,4,16,64}``, ``mx3d_rceil`` (E=8 with the rceil scale mode),
-``blockwise`` (1x128 activations + 128x128 weights), ``relayout`` (the
-per-group re-layout of (8192, 32768) e8m0 scales into scaled-MFMA tiles; its
-bytes are scale bytes read plus tile bytes written).
+Default workload (``mx3d_e64``): MXFP8 quantization of 3D expert weights W
+bf16 (64, 8192, 5120) along N in 32 x 1 blocks (e8m0 floor scales), written
+per expert column-major, the largest configuration and the shape of the 3D
+colwise kernel page's headline row; values N(0, 0.02) with 1% of the blocks
+all-zero and 1% scaled by 2^20.  One step = one launch over all 64 experts.
 
-Metric: algorithmic HBM bytes (2 B bf16 read + 1 B e4m3 write + scale bytes
-per launch) divided by time.  Inputs are resident in HBM before the timed
-region; outputs are preallocated; every launch goes through the C ABI.
+Other workloads (``--workload``): ``moe_bwd`` (jagged rowwise quantization
+of grad_out^T (4096, 16384) plus jagged colwise of x (16384, 4096), 8 token
+groups, fp32 scales), ``moe_bwd_mx`` (the same operands as jagged MXFP8),
+``mx3d`` (E = 8, N(0, 0.02)), ``mx3d_e{1,2,4,16,64}`` (the E sweep),
+``mx3d_rceil``, ``blockwise`` (1 x 128 activations (8192, 4096) + 128 x 128
+weights (4096, 4096)), ``blockwise_t`` (the transposed operands of the
+blockwise backward), ``relayout`` (per-group re-layout of (8192, 32768)
+e8m0 scales into scaled-MFMA tiles), ``copy`` (counter calibration).
 
-Timing: the K timed steps run back to back with one pair of HIP events on
-the launch stream around them (``gpu_ms_per_step``) besides the host clock
-(``ms_per_step``, which gives ``value``).  A second pass of K steps puts an
-event between consecutive launches; those intervals also hold each launch's
-dispatch and the event (about 2 us, the same for every launch), so a
-kernel's ``avg_us`` (and ``roofline.avg_launch_us``) is its average interval
-less an equal share of the intervals' excess over ``gpu_ms_per_step``.  The
-raw intervals are reported as ``interval_*_us``.
+Metric: algorithmic HBM bytes (2 B bf16 read + 1 B e4m3 write + scale
+bytes per launch) divided by time.  Inputs are resident in HBM before the
+timed region; outputs are preallocated; every launch goes through the C ABI.
 
-Prints one JSON line (rank 0).
+Timing:
+  * ``value`` / ``ms_per_step``: K steps back to back, host clock, bracketed
+    by synchronisations; ``gpu_ms_per_step``: one pair of HIP events on the
+    launch stream around the same K steps.
+  * per kernel, ``cold_us``: a 1 GiB write on the launch stream (more than
+    the L2s and the 256 MB memory-side cache), then one event pair around one
+    launch; median, min and max over ``--flush-iters`` launches.  The
+    roofline uses the dominant kernel's cold median.
+  * per kernel, ``warm_us``: one event pair around K back-to-back launches
+    of that kernel alone, divided by K (inputs partly in the caches when they
+    fit).
+The extra workloads (``--extras``, default cfg1 moe_bwd, cfg2 mx3d and cfg4
+blockwise) are timed the same way and reported under ``workloads``; the
+streaming probes under ``stream_ceiling`` give the practical HBM ceiling of
+the same traffic mix.
+
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -34,6 +45,7 @@ import ctypes
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -42,24 +54,26 @@ sys.path.insert(0, ROOT)
 
 PEAK_GBPS = 8000.0
 METRIC = "achieved HBM GB/s (bf16 read + fp8/scale write) and % of MI355X peak"
+DEFAULT_EXTRAS = "moe_bwd,mx3d,blockwise"
+FLUSH_BYTES = 1 << 30
 
 
-def parse():
+def parse(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="moe_bwd")
+    p.add_argument("--workload", default="mx3d_e64")
+    p.add_argument("--flush-iters", type=int, default=10,
+                   help="cold launches per kernel, each after a 1 GiB write (median/min/max)")
+    p.add_argument("--extras", default=DEFAULT_EXTRAS,
+                   help="comma-separated extra workloads timed after the headline one")
+    p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-copy-ceiling", action="store_true",
-                   help="skip timing the 4 GiB device-to-device copy used as the practical ceiling")
-    p.add_argument("--flush-iters", type=int, default=0,
-                   help="after the timed steps, time each kernel this many more times with a "
-                        "1 GiB buffer written before every launch (cold L2 and MALL) and report "
-                        "median/min/max; 0 = skip")
-    p.add_argument("--cpu-sample-rows", type=int, default=0,
-                   help="rows/columns per tensor for the CPU-oracle sample (0 = auto)")
-    return p.parse_args()
+    p.add_argument("--no-ceiling", action="store_true",
+                   help="skip the device copy and the streaming probes")
+    p.add_argument("--no-output-hash", action="store_true")
+    return p.parse_args(argv)
 
 
 def csrc_digest() -> str:
@@ -80,14 +94,68 @@ def csrc_digest() -> str:
     return h.hexdigest()[:16]
 
 
+# ----------------------------------------------------- input generation
+
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _gen_call(name, args):
+    import workloads
+
+    return getattr(workloads, name)(*args)
+
+
+class Generator:
+    """Seeded inputs from ``workloads``, drawn in spawned host processes
+    (numpy only: no GPU context), with the SHA-256 of every tensor's bytes
+    in the order they are handed over."""
+
+    def __init__(self):
+        self._pool = None
+        self.sha = {}
+
+    def pool(self):
+        if self._pool is None:
+            import multiprocessing as mp
+            from concurrent.futures import ProcessPoolExecutor
+
+            self._pool = ProcessPoolExecutor(max_workers=_workers(), mp_context=mp.get_context("spawn"))
+        return self._pool
+
+    def map(self, name, arglist, label):
+        """Yield workloads.<name>(*args) for each args in order, hashing the
+        concatenated bytes under ``label``."""
+        h = hashlib.sha256()
+        futs = [self.pool().submit(_gen_call, name, tuple(a)) for a in arglist]
+        for f in futs:
+            out = f.result()
+            h.update(memoryview(out).cast("B"))
+            yield out
+        self.sha[label] = h.hexdigest()
+
+    def one(self, name, label, *args):
+        return next(iter(self.map(name, [args], label)))
+
+    def close(self):
+        if self._pool is not None:
+            self._pool.shutdown(wait=True)
+            self._pool = None
+
+
 # ------------------------------------------------------------- workloads
 
 class Launch:
     """One C-ABI call with preallocated device buffers."""
 
-    def __init__(self, name, kernel, fn, args, nbytes, numel):
+    def __init__(self, name, kernel, fn, args, nbytes, numel, outputs=()):
         self.name, self.kernel, self.fn, self.args = name, kernel, fn, args
         self.nbytes, self.numel = nbytes, numel
+        self.outputs = outputs   # (label, device tensor) whose bytes are hashed
 
     def __call__(self, stream_handle):
         code = self.fn(*self.args, stream_handle)
@@ -101,9 +169,14 @@ def bf16_dev(torch, bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
 
 
-def build_moe_bwd(torch, mxq, workloads):
-    go_t = workloads.moe_grad_out_t()
-    x = workloads.moe_x()
+def _sizes(offs):
+    import numpy as np
+
+    return [int(v) for v in np.diff(np.concatenate([[0], offs]))]
+
+
+def build_moe_bwd(torch, mxq, workloads, gen):
+    go_t, x = list(gen.map("moe_grad_out_t", [()], "grad_out_t")) + list(gen.map("moe_x", [()], "x"))
     offs = workloads.moe_offsets()
     G = offs.size
     d_go, d_x = bf16_dev(torch, go_t), bf16_dev(torch, x)
@@ -118,39 +191,35 @@ def build_moe_bwd(torch, mxq, workloads):
     l1 = Launch("jagged_rowwise grad_out^T (4096,16384)", "jagged_contig_kernel",
                 mxq.mxq_quantize_jagged_rowwise,
                 (d_go.data_ptr(), R1, C1, C1, 1, d_offs.data_ptr(), G, q1.data_ptr(), C1, 1,
-                 s1.data_ptr(), G, 1), 3 * R1 * C1 + 4 * R1 * G, R1 * C1)
+                 s1.data_ptr(), G, 1), 3 * R1 * C1 + 4 * R1 * G, R1 * C1, (("q1", q1), ("s1", s1)))
     l2 = Launch("jagged_colwise x (16384,4096)", "jagged_strided_kernel",
                 mxq.mxq_quantize_jagged_colwise,
                 (d_x.data_ptr(), R2, C2, C2, 1, d_offs.data_ptr(), G, q2.data_ptr(), 1, R2,
-                 s2.data_ptr(), C2, 1), 3 * R2 * C2 + 4 * G * C2, R2 * C2)
+                 s2.data_ptr(), C2, 1), 3 * R2 * C2 + 4 * G * C2, R2 * C2, (("q2", q2), ("s2", s2)))
     desc = {"workload": "moe_bwd_jagged",
             "tensors": "grad_out^T bf16 (4096,16384) rowwise -> row-major e4m3; "
                        "x bf16 (16384,4096) colwise -> column-major e4m3",
-            "groups": int(G), "group_sizes": [int(v) for v in
-                                              (offs - __import__("numpy").concatenate([[0], offs[:-1]]))],
-            "scales": "fp32 per (row, group) and per (group, column)"}
+            "groups": int(G), "group_sizes": _sizes(offs),
+            "scales": "fp32 per (row, group) and per (group, column)",
+            "seeds": dict(workloads.MOE_SEEDS)}
 
-    def cpu_sample(oracle, n):
-        # the same two ops on n rows of grad_out^T and n columns of x
-        t0 = time.perf_counter()
-        oracle.quantize_jagged_rowwise(go_t[:n], offs)
-        oracle.quantize_jagged_colwise(x[:, :n], offs)
-        dt = time.perf_counter() - t0
+    def cpu_sample(oracle):
+        n = 1024
         nbytes = 3 * n * C1 + 4 * n * G + 3 * R2 * n + 4 * G * n
-        return dt, nbytes, (f"jagged rowwise on {n} of 4096 rows of grad_out^T and jagged colwise "
-                            f"on {n} of 4096 columns of x (all 16384 tokens, same 8 groups)")
+        xs = x[:, :n].copy()
+        return (lambda: (oracle.quantize_jagged_rowwise(go_t[:n], offs),
+                         oracle.quantize_jagged_colwise(xs, offs)),
+                nbytes, f"jagged rowwise on {n} of 4096 rows of grad_out^T and jagged colwise on "
+                        f"{n} of 4096 columns of x (all 16384 tokens, same 8 groups)")
 
     return [l1, l2], keep, desc, cpu_sample
 
 
-def build_moe_bwd_mx(torch, mxq, workloads):
+def build_moe_bwd_mx(torch, mxq, workloads, gen):
     """The MX variant of the MoE backward grad_weight operands: jagged MXFP8
     (32-element blocks restarting at each token-group start, e8m0 floor
     scales) of grad_out^T rowwise and x colwise, the same 8 groups."""
-    import numpy as np
-
-    go_t = workloads.moe_grad_out_t()
-    x = workloads.moe_x()
+    go_t, x = list(gen.map("moe_grad_out_t", [()], "grad_out_t")) + list(gen.map("moe_x", [()], "x"))
     offs = workloads.moe_offsets()
     G = offs.size
     d_go, d_x = bf16_dev(torch, go_t), bf16_dev(torch, x)
@@ -159,8 +228,7 @@ def build_moe_bwd_mx(torch, mxq, workloads):
     R2, C2 = x.shape
     nb1 = mxq.jagged_mx_scale_capacity(C1, G)
     nb2 = mxq.jagged_mx_scale_capacity(R2, G)
-    sizes = np.diff(np.concatenate([[0], offs]))
-    nb = int(sum((int(n) + 31) // 32 for n in sizes))          # blocks actually written
+    nb = int(sum((n + 31) // 32 for n in _sizes(offs)))          # blocks actually written
     q1 = torch.empty(R1 * C1, dtype=torch.uint8, device="cuda")
     s1 = torch.empty(R1 * nb1, dtype=torch.uint8, device="cuda")
     q2 = torch.empty(R2 * C2, dtype=torch.uint8, device="cuda")
@@ -169,63 +237,66 @@ def build_moe_bwd_mx(torch, mxq, workloads):
     l1 = Launch("jagged_mx_rowwise grad_out^T (4096,16384)", "jagged_mx_rowwise_kernel",
                 mxq.mxq_quantize_jagged_mx_rowwise,
                 (d_go.data_ptr(), R1, C1, C1, 1, d_offs.data_ptr(), G, q1.data_ptr(), C1, 1,
-                 s1.data_ptr(), nb1, 1, 0), 3 * R1 * C1 + R1 * nb, R1 * C1)
+                 s1.data_ptr(), nb1, 1, 0), 3 * R1 * C1 + R1 * nb, R1 * C1, (("q1", q1),))
     l2 = Launch("jagged_mx_colwise x (16384,4096)", "jagged_mx_colwise_kernel",
                 mxq.mxq_quantize_jagged_mx_colwise,
                 (d_x.data_ptr(), R2, C2, C2, 1, d_offs.data_ptr(), G, q2.data_ptr(), 1, R2,
-                 s2.data_ptr(), C2, 1, 0), 3 * R2 * C2 + nb * C2, R2 * C2)
+                 s2.data_ptr(), C2, 1, 0), 3 * R2 * C2 + nb * C2, R2 * C2, (("q2", q2),))
     desc = {"workload": "moe_bwd_jagged_mx",
             "tensors": "grad_out^T bf16 (4096,16384) 1x32 blocks per group -> row-major e4m3; "
                        "x bf16 (16384,4096) 32x1 blocks per group -> column-major e4m3",
-            "groups": int(G), "group_sizes": [int(v) for v in sizes],
-            "scales": f"e8m0 floor, {nb} blocks per row / column"}
+            "groups": int(G), "group_sizes": _sizes(offs),
+            "scales": f"e8m0 floor, {nb} blocks per row / column", "seeds": dict(workloads.MOE_SEEDS)}
 
-    def cpu_sample(oracle, n):
-        t0 = time.perf_counter()
-        oracle.quantize_jagged_mx_rowwise(go_t[:n], offs)
-        oracle.quantize_jagged_mx_colwise(np.ascontiguousarray(x[:, :n]), offs)
-        dt = time.perf_counter() - t0
-        nbytes = 3 * n * C1 + n * nb + 3 * R2 * n + nb * n
-        return dt, nbytes, (f"jagged MX rowwise on {n} of 4096 rows of grad_out^T and jagged MX "
-                            f"colwise on {n} of 4096 columns of x")
+    def cpu_sample(oracle):
+        import numpy as np
+
+        n = 1024
+        xs = np.ascontiguousarray(x[:, :n])
+        return (lambda: (oracle.quantize_jagged_mx_rowwise(go_t[:n], offs),
+                         oracle.quantize_jagged_mx_colwise(xs, offs)),
+                3 * n * C1 + n * nb + 3 * R2 * n + nb * n,
+                f"jagged MX rowwise on {n} of 4096 rows of grad_out^T and jagged MX colwise on "
+                f"{n} of 4096 columns of x")
 
     return [l1, l2], keep, desc, cpu_sample
 
 
-def build_mx3d(torch, mxq, workloads, E, sweep, rceil=False):
-    import numpy as np
-
+def build_mx3d(torch, mxq, workloads, gen, E, sweep, rceil=False):
     N, K = 8192, 5120
     w = torch.empty((E, N, K), dtype=torch.bfloat16, device="cuda")
-    for e in range(E):
-        bits = workloads.mx3d_sweep_expert(e) if sweep else workloads.mx3d_expert(e)
+    name = "mx3d_sweep_expert" if sweep else "mx3d_expert"
+    first = None
+    for e, bits in enumerate(gen.map(name, [(e,) for e in range(E)], "W")):
         w[e].copy_(bf16_dev(torch, bits))
-        if E > 8 and (e + 1) % 8 == 0:
-            print(f"[bench] generated {e + 1} of {E} experts", file=sys.stderr, flush=True)
+        if e == 0:
+            first = bits
+        if E > 8 and (e + 1) % 16 == 0:
+            print(f"[bench] {e + 1} of {E} experts on the device", file=sys.stderr, flush=True)
     q = torch.empty(E * N * K, dtype=torch.uint8, device="cuda")
     s = torch.empty(E * (N // 32) * K, dtype=torch.uint8, device="cuda")
     l = Launch(f"mx_3d_colwise ({E},{N},{K})", "block_strided_kernel<32, 1, true>",
                mxq.mxq_quantize_mx_3d_colwise,
                (w.data_ptr(), E, N, K, N * K, K, 1, q.data_ptr(), N * K, 1, N, s.data_ptr(),
-                (N // 32) * K, K, 1, 1 if rceil else 0), 3 * E * N * K + E * (N // 32) * K, E * N * K)
+                (N // 32) * K, K, 1, 1 if rceil else 0), 3 * E * N * K + E * (N // 32) * K, E * N * K,
+               (("q", q), ("scales", s)))
     mode = "rceil" if rceil else "floor"
+    seeds = dict(workloads.MX3D_SWEEP_SEEDS) if sweep else {"vals": workloads.MX3D_SEED}
     desc = {"workload": f"mx3d_E{E}" + ("_sweep" if sweep else "") + ("_rceil" if rceil else ""),
             "tensors": f"W bf16 ({E},{N},{K}) -> e4m3 per-expert column-major (N*K,1,N)",
-            "scales": f"e8m0 {mode}, (E, N/32, K)"}
+            "values": "N(0,0.02)" + (", 1% of 32x1 blocks zero, 1% x 2^20" if sweep else ""),
+            "scales": f"e8m0 {mode}, (E, N/32, K)", "seeds": seeds}
 
-    def cpu_sample(oracle, n):
-        bits = workloads.mx3d_sweep_expert(0) if sweep else workloads.mx3d_expert(0)
-        t0 = time.perf_counter()
-        oracle.quantize_mx_3d_colwise(bits[None, :, :n], mode=mode)
-        dt = time.perf_counter() - t0
-        return dt, 3 * N * n + (N // 32) * n, f"expert 0, all N, {n} of {K} columns"
+    def cpu_sample(oracle):
+        return (lambda: oracle.quantize_mx_3d_colwise(first[None], mode=mode),
+                3 * N * K + (N // 32) * K, f"expert 0 of W, whole ({N},{K})")
 
     return [l], [w, q, s], desc, cpu_sample
 
 
-def build_blockwise(torch, mxq, workloads):
-    a = workloads.blockwise_act()
-    wt = workloads.blockwise_weight()
+def build_blockwise(torch, mxq, workloads, gen):
+    a = gen.one("blockwise_act", "act")
+    wt = gen.one("blockwise_weight", "W")
     da, dw = bf16_dev(torch, a), bf16_dev(torch, wt)
     M, Kd = a.shape
     R, C = wt.shape
@@ -236,42 +307,69 @@ def build_blockwise(torch, mxq, workloads):
     l1 = Launch("blockwise 1x128 act (8192,4096)", "block_contig_kernel<128, 8, false",
                 mxq.mxq_quantize_blockwise,
                 (da.data_ptr(), M, Kd, Kd, 1, 1, 128, qa.data_ptr(), Kd, 1, sa.data_ptr(),
-                 Kd // 128, 1), 3 * M * Kd + 4 * M * (Kd // 128), M * Kd)
+                 Kd // 128, 1), 3 * M * Kd + 4 * M * (Kd // 128), M * Kd, (("qa", qa), ("sa", sa)))
     l2 = Launch("blockwise 128x128 W (4096,4096)", "block_strided_kernel<128, 128, false>",
                 mxq.mxq_quantize_blockwise,
                 (dw.data_ptr(), R, C, C, 1, 128, 128, qw.data_ptr(), 1, R, sw.data_ptr(),
-                 C // 128, 1), 3 * R * C + 4 * (R // 128) * (C // 128), R * C)
+                 C // 128, 1), 3 * R * C + 4 * (R // 128) * (C // 128), R * C, (("qw", qw), ("sw", sw)))
     desc = {"workload": "blockwise",
             "tensors": "act bf16 (8192,4096) 1x128 -> row-major e4m3; "
                        "W bf16 (4096,4096) 128x128 -> column-major e4m3",
-            "scales": "fp32 per block"}
+            "scales": "fp32 per block", "seeds": dict(workloads.BLOCKWISE_SEEDS)}
 
-    def cpu_sample(oracle, n):
-        t0 = time.perf_counter()
-        oracle.quantize_blockwise(a[:n], 1, 128)
-        oracle.quantize_blockwise(wt[: (n // 128) * 128 or 128], 128, 128)
-        dt = time.perf_counter() - t0
-        nw = (n // 128) * 128 or 128
-        return dt, 3 * n * Kd + 4 * n * (Kd // 128) + 3 * nw * C + 4 * (nw // 128) * (C // 128), \
-            f"{n} rows of act and {nw} rows of W"
+    def cpu_sample(oracle):
+        n = 2048
+        return (lambda: (oracle.quantize_blockwise(a[:n], 1, 128), oracle.quantize_blockwise(wt[:n], 128, 128)),
+                3 * n * Kd + 4 * n * (Kd // 128) + 3 * n * C + 4 * (n // 128) * (C // 128),
+                f"{n} rows of act and {n} rows of W")
 
     return [l1, l2], [da, dw, qa, sa, qw, sw], desc, cpu_sample
 
 
-def build_relayout(torch, mxq, workloads):
+def build_blockwise_t(torch, mxq, workloads, gen):
+    """The transposed operands of the blockwise backward, read in place: the
+    activations' 128 x 1 blocks of the (4096, 8192) transposed view into a
+    row-major q of the transpose (scales per 128 tokens of each column), and
+    the weights' 128 x 128 blocks of the transposed view into a row-major q."""
+    a = gen.one("blockwise_act", "act")
+    wt = gen.one("blockwise_weight", "W")
+    da, dw = bf16_dev(torch, a), bf16_dev(torch, wt)
+    M, Kd = a.shape
+    R, C = wt.shape
+    qa = torch.empty(M * Kd, dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M // 128) * Kd, dtype=torch.float32, device="cuda")
+    qw = torch.empty(R * C, dtype=torch.uint8, device="cuda")
+    sw = torch.empty((R // 128) * (C // 128), dtype=torch.float32, device="cuda")
+    # act^T: a (Kd, M) view with strides (1, Kd); 1 x 128 blocks along its rows
+    # are 128 x 1 blocks of act; q of act^T row-major (Kd, M)
+    l1 = Launch("blockwise 1x128 act^T (4096,8192) view", "block_strided_kernel<128, 1, false>",
+                mxq.mxq_quantize_blockwise,
+                (da.data_ptr(), Kd, M, 1, Kd, 1, 128, qa.data_ptr(), M, 1, sa.data_ptr(),
+                 M // 128, 1), 3 * M * Kd + 4 * Kd * (M // 128), M * Kd, (("qa", qa), ("sa", sa)))
+    l2 = Launch("blockwise 128x128 W^T (4096,4096) view", "block_strided_kernel<128, 128, false>",
+                mxq.mxq_quantize_blockwise,
+                (dw.data_ptr(), C, R, 1, C, 128, 128, qw.data_ptr(), R, 1, sw.data_ptr(),
+                 R // 128, 1), 3 * R * C + 4 * (R // 128) * (C // 128), R * C, (("qw", qw), ("sw", sw)))
+    desc = {"workload": "blockwise_t",
+            "tensors": "act^T view of bf16 (8192,4096) 1x128 -> row-major e4m3 (4096,8192); "
+                       "W^T view of bf16 (4096,4096) 128x128 -> row-major e4m3",
+            "scales": "fp32 per block", "seeds": dict(workloads.BLOCKWISE_SEEDS)}
+    return [l1, l2], [da, dw, qa, sa, qw, sw], desc, None
+
+
+def build_relayout(torch, mxq, workloads, gen):
     """Per-group re-layout of jagged MX scales into scaled-MFMA scale tiles on
     the largest scale shape of the per-group conversion benchmarks:
     (8192, 32768) e8m0 scale columns of 8 MoE-like token groups over 2^20
     tokens, stored row-major (blocks contiguous)."""
-    import numpy as np
-
     scales, offs = workloads.relayout_case()
+    gen.sha["scales"] = hashlib.sha256(memoryview(scales).cast("B")).hexdigest()
     rows, cap = scales.shape
     extent = 1 << 20
     G = offs.size
-    sizes = np.diff(np.concatenate([[0], offs]))
-    nb = int(sum((int(n) + 31) // 32 for n in sizes))
-    ntiles = ((rows + 15) // 16) * int(sum((int(n) + 511) // 512 for n in sizes))
+    sizes = _sizes(offs)
+    nb = int(sum((n + 31) // 32 for n in sizes))
+    ntiles = ((rows + 15) // 16) * int(sum((n + 511) // 512 for n in sizes))
     d_s = torch.from_numpy(scales).cuda()
     d_offs = torch.from_numpy(offs).cuda()
     tiles = torch.empty(mxq.mx_tile_capacity(rows, extent, G), dtype=torch.uint8, device="cuda")
@@ -283,20 +381,20 @@ def build_relayout(torch, mxq, workloads):
     desc = {"workload": "relayout_scales",
             "tensors": f"e8m0 scales ({rows},{nb}) row-major -> 16x16-block scaled-MFMA tiles "
                        f"({ntiles} tiles of 256 B)",
-            "groups": int(G), "group_sizes": [int(v) for v in sizes],
-            "bytes": "scale bytes read + tile bytes written (zero padding included)"}
+            "groups": int(G), "group_sizes": sizes,
+            "bytes": "scale bytes read + tile bytes written (zero padding included)",
+            "seeds": dict(workloads.RELAYOUT_SEEDS)}
 
-    def cpu_sample(oracle, n):
-        t0 = time.perf_counter()
-        oracle.relayout_mx_scales_grouped(scales[:n], offs, extent)
-        dt = time.perf_counter() - t0
-        nt = ((n + 15) // 16) * int(sum((int(v) + 511) // 512 for v in sizes))
-        return dt, n * nb + 256 * nt, f"{n} of {rows} rows, all {G} groups"
+    def cpu_sample(oracle):
+        n = 2048
+        nt = ((n + 15) // 16) * int(sum((v + 511) // 512 for v in sizes))
+        return (lambda: oracle.relayout_mx_scales_grouped(scales[:n], offs, extent),
+                n * nb + 256 * nt, f"{n} of {rows} rows, all {G} groups")
 
     return [l], [d_s, d_offs, tiles, starts], desc, cpu_sample
 
 
-def build_copy(torch):
+def build_copy(torch, mxq, workloads, gen):
     """Calibration: a plain device-to-device copy of 256 MiB (torch's copy,
     i.e. the runtime's copy kernel).  Its FETCH_SIZE / WRITE_SIZE counters
     against the known 256 MiB read and written give the scale factors that
@@ -314,23 +412,29 @@ def build_copy(torch):
     return [l], [src, dst], desc, None
 
 
-def build(name, torch, mxq, workloads):
+WORKLOADS = ("mx3d_e64", "mx3d_e1", "mx3d_e2", "mx3d_e4", "mx3d_e16", "mx3d", "mx3d_rceil",
+             "moe_bwd", "moe_bwd_mx", "blockwise", "blockwise_t", "relayout", "copy")
+
+
+def build(name, torch, mxq, workloads, gen):
     if name == "copy":
-        return build_copy(torch)
+        return build_copy(torch, mxq, workloads, gen)
     if name == "moe_bwd":
-        return build_moe_bwd(torch, mxq, workloads)
+        return build_moe_bwd(torch, mxq, workloads, gen)
     if name == "moe_bwd_mx":
-        return build_moe_bwd_mx(torch, mxq, workloads)
+        return build_moe_bwd_mx(torch, mxq, workloads, gen)
     if name == "mx3d":
-        return build_mx3d(torch, mxq, workloads, 8, sweep=False)
+        return build_mx3d(torch, mxq, workloads, gen, 8, sweep=False)
     if name == "mx3d_rceil":
-        return build_mx3d(torch, mxq, workloads, 8, sweep=False, rceil=True)
-    if name.startswith("mx3d_e"):
-        return build_mx3d(torch, mxq, workloads, int(name[len("mx3d_e"):]), sweep=True)
+        return build_mx3d(torch, mxq, workloads, gen, 8, sweep=False, rceil=True)
+    if name.startswith("mx3d_e") and name[len("mx3d_e"):].isdigit():
+        return build_mx3d(torch, mxq, workloads, gen, int(name[len("mx3d_e"):]), sweep=True)
     if name == "blockwise":
-        return build_blockwise(torch, mxq, workloads)
+        return build_blockwise(torch, mxq, workloads, gen)
+    if name == "blockwise_t":
+        return build_blockwise_t(torch, mxq, workloads, gen)
     if name == "relayout":
-        return build_relayout(torch, mxq, workloads)
+        return build_relayout(torch, mxq, workloads, gen)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -362,7 +466,7 @@ class DeviceEvents:
     (hipEventDisableSystemFence): recording them writes back and invalidates
     no caches for the host, so they perturb the kernels between them less
     than default events.  Uses the HIP runtime torch has already loaded (the
-    one the launches go through); None if neither kind can be created."""
+    one the launches go through)."""
 
     KINDS = ((0x40000000, "hipEventReleaseToDevice"), (0x20000000, "hipEventDisableSystemFence"))
 
@@ -387,13 +491,6 @@ class DeviceEvents:
         if self.flags is None:
             raise OSError("no timing event kind accepted")
 
-    @classmethod
-    def open(cls):
-        try:
-            return cls()
-        except (OSError, AttributeError):
-            return None
-
     def create(self):
         e = ctypes.c_void_p()
         if self.lib.hipEventCreateWithFlags(ctypes.byref(e), self.flags) != 0:
@@ -417,14 +514,179 @@ class DeviceEvents:
         self.made = []
 
 
-def main():
-    args = parse()
+class Timer:
+    """Cold (flushed) and warm timings of single launches on one stream."""
+
+    def __init__(self, torch, dev, sh):
+        self.torch, self.dev, self.sh = torch, dev, sh
+        self.flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+
+    def cold_ms(self, fn, iters):
+        pairs = [(self.dev.create(), self.dev.create()) for _ in range(iters)]
+        for k, (a, b) in enumerate(pairs):
+            self.flush.fill_(k & 0xFF)          # on the launch stream (torch's current stream)
+            self.dev.record(a, self.sh)
+            fn(self.sh)
+            self.dev.record(b, self.sh)
+        self.torch.cuda.synchronize()
+        return [self.dev.elapsed_ms(a, b) for a, b in pairs]
+
+    def warm_ms(self, fn, k):
+        a, b = self.dev.create(), self.dev.create()
+        fn(self.sh)
+        self.dev.record(a, self.sh)
+        for _ in range(k):
+            fn(self.sh)
+        self.dev.record(b, self.sh)
+        self.torch.cuda.synchronize()
+        return self.dev.elapsed_ms(a, b) / k
+
+
+def kernel_record(np, l, cold, warm_ms):
+    med = float(np.median(cold))
+    return {"cold_us": {"median": round(med * 1e3, 2), "min": round(float(np.min(cold)) * 1e3, 2),
+                        "max": round(float(np.max(cold)) * 1e3, 2), "iters": len(cold)},
+            "warm_us": round(warm_ms * 1e3, 2),
+            "algorithmic_bytes": l.nbytes,
+            "GBps_cold": round(l.nbytes / (med * 1e-3) / 1e9, 1),
+            "frac_of_peak_cold": round(l.nbytes / (med * 1e-3) / 1e9 / PEAK_GBPS, 4),
+            "GBps_warm": round(l.nbytes / (warm_ms * 1e-3) / 1e9, 1),
+            "kernel": l.kernel}
+
+
+def time_kernels(np, timer, launches, flush_iters, warm_steps, warmup):
+    for _ in range(max(1, warmup)):
+        for l in launches:
+            l(timer.sh)
+    timer.torch.cuda.synchronize()
+    out = {}
+    for l in launches:
+        cold = timer.cold_ms(l, flush_iters)
+        out[l.name] = kernel_record(np, l, cold, timer.warm_ms(l, warm_steps))
+    return out
+
+
+def output_sha256(torch, launches):
+    """SHA-256 of each launch's output buffers (storage order), copied back in
+    64 MiB pieces."""
+    res = {}
+    for l in launches:
+        for label, t in l.outputs:
+            h = hashlib.sha256()
+            flat = t.view(torch.uint8).reshape(-1)
+            step = 64 << 20
+            for i in range(0, flat.numel(), step):
+                h.update(memoryview(flat[i:i + step].cpu().numpy()).cast("B"))
+            res[label] = h.hexdigest()
+    return res
+
+
+def stream_ceiling(torch, dev, sh, np):
+    """Practical HBM ceiling of the quantizers' traffic: the streaming probes
+    (tests/ceiling) on 2^31 bf16 elements (4 GiB read, 2 GiB written), median
+    of 5 launches each, and the runtime's 4 GiB device-to-device copy."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import ceiling
+
+    lib = ceiling.load()
+    n = 1 << 31
+    src = torch.empty(2 * n, dtype=torch.uint8, device="cuda").fill_(0x3C)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    res = {"elements": n, "method": "event pair per launch, median of 5 (buffers far larger than the caches)"}
+    for mode, code in ceiling.MODES.items():
+        def fn(s, code=code):
+            rc = lib.ceiling_stream(src.data_ptr(), dst.data_ptr(), n, code, ctypes.c_void_p(s))
+            if rc != 0:
+                raise RuntimeError(f"ceiling_stream mode {code}: {rc}")
+        fn(sh)
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(5):
+            a, b = dev.create(), dev.create()
+            dev.record(a, sh)
+            fn(sh)
+            dev.record(b, sh)
+            torch.cuda.synchronize()
+            ms.append(dev.elapsed_ms(a, b))
+        res[f"{mode}_GBps"] = round(ceiling.bytes_moved(n, mode) / (float(np.median(ms)) * 1e-3) / 1e9, 1)
+    del src, dst
+    # the runtime's own copy kernel, counted as bytes read plus bytes written
+    m = 4 << 30
+    a8 = torch.empty(m, dtype=torch.uint8, device="cuda").fill_(1)
+    b8 = torch.empty(m, dtype=torch.uint8, device="cuda")
+    b8.copy_(a8)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(5):
+        a, b = dev.create(), dev.create()
+        dev.record(a, sh)
+        b8.copy_(a8)
+        dev.record(b, sh)
+        torch.cuda.synchronize()
+        ms.append(dev.elapsed_ms(a, b))
+    res["d2d_copy_GBps"] = round(2 * m / (float(np.median(ms)) * 1e-3) / 1e9, 1)
+    del a8, b8
+    return res
+
+
+def cpu_baseline(np, oracle, cpu_sample):
+    """The oracle on a bounded sample of the workload, pinned to one host core
+    (the calling thread's affinity), median of 3 runs."""
+    fn, nbytes, what = cpu_sample(oracle)
+    prev = None
+    core = None
+    try:
+        prev = os.sched_getaffinity(0)
+        core = min(prev)
+        os.sched_setaffinity(0, {core})
+    except (AttributeError, OSError):
+        prev = None
+    try:
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t0)
+    finally:
+        if prev is not None:
+            os.sched_setaffinity(0, prev)
+    dt = float(np.median(times))
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": what, "seconds_median": round(dt, 3), "runs": 3,
+            "pinned_core": core, "bytes": nbytes}
+
+
+def host_info(torch):
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = None
+    rocm = None
+    for p in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        if os.path.exists(p):
+            rocm = open(p).read().strip()
+            break
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity_cores": affinity,
+            "gpu": torch.cuda.get_device_name(0), "torch": torch.__version__,
+            "hip": getattr(torch.version, "hip", None), "rocm": rocm, "python": platform.python_version()}
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1:
         print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         raise SystemExit(2)
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if world != 1:
+    if int(os.environ.get("WORLD_SIZE", "1")) != 1:
         raise SystemExit("one process, one GPU: run without torch.distributed")
 
     import numpy as np
@@ -435,144 +697,86 @@ def main():
 
     mxq._capi.load()
     torch.cuda.init()
-    print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
-    launches, keep, desc, cpu_sample = build(args.workload, torch, mxq, workloads)
-    torch.cuda.synchronize()
-
+    dev = DeviceEvents()
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    gen = Generator()
+    print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
+    launches, keep, desc, cpu_sample = build(args.workload, torch, mxq, workloads, gen)
+    input_sha = dict(gen.sha)
+    torch.cuda.synchronize()
+
     for _ in range(args.warmup):
         for l in launches:
             l(sh)
     torch.cuda.synchronize()
 
-    K = args.steps
-    dev = DeviceEvents.open()
-
     # timed region: K steps exactly as a caller runs them, bracketed by one
     # pair of events on the launch stream (none between launches)
-    if dev is not None:
-        g0, g1 = dev.create(), dev.create()
-    else:
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    K = args.steps
+    g0, g1 = dev.create(), dev.create()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    (dev.record(g0, sh) if dev is not None else g0.record(stream))
-    for k in range(K):
+    dev.record(g0, sh)
+    for _ in range(K):
         for l in launches:
             l(sh)
-    (dev.record(g1, sh) if dev is not None else g1.record(stream))
+    dev.record(g1, sh)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = dev.elapsed_ms(g0, g1) if dev is not None else g0.elapsed_time(g1)
+    gpu_ms = dev.elapsed_ms(g0, g1)
+    print(f"[bench] timed {K} steps: {wall * 1e3 / K:.4f} ms per step", file=sys.stderr, flush=True)
 
-    # per-kernel durations: K more steps with an event on the launch stream
-    # between consecutive launches.  Each interval also holds a launch's
-    # dispatch and the event itself, the same few µs for every launch: that
-    # overhead is the intervals' excess over the event-timed step above, and
-    # a kernel's duration is its interval less an equal part of it (this
-    # matches the kernel trace's averages).
-    if dev is not None:
-        ev = [[dev.create() for _ in range(len(launches) + 1)] for _ in range(K)]
-        record = lambda e: dev.record(e, sh)
-        elapsed = dev.elapsed_ms
-        event_kind = f"hip events ({dev.kind}) on the launch stream"
-    else:
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)] for _ in range(K)]
-        record = lambda e: e.record(stream)
-        elapsed = lambda a, b: a.elapsed_time(b)
-        event_kind = "torch events on the launch stream"
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for k in range(K):
-        record(ev[k][0])
-        for i, l in enumerate(launches):
-            l(sh)
-            record(ev[k][i + 1])
-    torch.cuda.synchronize()
-    wall_instr = time.perf_counter() - t1
+    timer = Timer(torch, dev, sh)
+    kernels = time_kernels(np, timer, launches, args.flush_iters, K, 0)
+    out_sha = None if args.no_output_hash else output_sha256(torch, launches)
 
-    interval_ms = [float(np.mean([elapsed(ev[k][i], ev[k][i + 1]) for k in range(K)]))
-                   for i in range(len(launches))]
-    gpu_step_ms = gpu_ms / K
-    # the intervals add the same per-launch overhead to every kernel
-    overhead_ms = max(0.0, (sum(interval_ms) - gpu_step_ms) / len(launches))
-    per_kernel_ms = [max(m - overhead_ms, 0.05 * m) for m in interval_ms]
     step_bytes = sum(l.nbytes for l in launches)
     ms_per_step = wall * 1e3 / K
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dom = max(launches, key=lambda l: kernels[l.name]["cold_us"]["median"])
+    dk = kernels[dom.name]
+    achieved = dom.nbytes / (dk["cold_us"]["median"] * 1e-6) / 1e9
+    traffic = traffic_for(dom.kernel, args.workload)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic, "kernel": dom.kernel,
+            "algorithmic_bytes_per_launch": dom.nbytes,
+            "avg_launch_us": dk["cold_us"]["median"],
+            "timing": f"cold: 1 GiB write, then {dev.kind} events around one launch; "
+                      f"median of {args.flush_iters}"}
+    del keep, launches
 
-    dom = int(np.argmax(per_kernel_ms))
-    dl = launches[dom]
-    achieved = dl.nbytes / (per_kernel_ms[dom] * 1e-3) / 1e9
-    traffic = traffic_for(dl.kernel, args.workload)
-    warm_ms = [[elapsed(ev[k][i], ev[k][i + 1]) for k in range(K)] for i in range(len(launches))]
-    kernels = {l.name: {"avg_us": round(per_kernel_ms[i] * 1e3, 2),
-                        "interval_avg_us": round(interval_ms[i] * 1e3, 2),
-                        "interval_median_us": round(float(np.median(warm_ms[i])) * 1e3, 2),
-                        "interval_min_us": round(float(np.min(warm_ms[i])) * 1e3, 2),
-                        "interval_max_us": round(float(np.max(warm_ms[i])) * 1e3, 2),
-                        "algorithmic_bytes": l.nbytes,
-                        "GBps": round(l.nbytes / (per_kernel_ms[i] * 1e-3) / 1e9, 1),
-                        "frac_of_peak": round(l.nbytes / (per_kernel_ms[i] * 1e-3) / 1e9 / PEAK_GBPS, 4)}
-               for i, l in enumerate(launches)}
-
-    if args.flush_iters > 0:
-        # cold-cache timing: a 1 GiB write (more than the L2s and the 256 MB
-        # MALL) on the same stream before every launch
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        for i, l in enumerate(launches):
-            if dev is not None:
-                evs = [(dev.create(), dev.create()) for _ in range(args.flush_iters)]
-            else:
-                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                       for _ in range(args.flush_iters)]
-            for k, (a, b) in enumerate(evs):
-                flush.fill_(k & 0xFF)
-                record(a)
-                l(sh)
-                record(b)
+    extras = {}
+    if not args.no_extras:
+        for name in [n for n in args.extras.split(",") if n and n != args.workload]:
+            print(f"[bench] extra workload {name}", file=sys.stderr, flush=True)
+            gen.sha = {}
+            ls, kp, d, _ = build(name, torch, mxq, workloads, gen)
             torch.cuda.synchronize()
-            ms = [max(elapsed(a, b) - overhead_ms, 0.0) for a, b in evs]   # same per-launch overhead
-            kernels[l.name]["flushed_us"] = {"median": round(float(np.median(ms)) * 1e3, 2),
-                                             "min": round(float(np.min(ms)) * 1e3, 2),
-                                             "max": round(float(np.max(ms)) * 1e3, 2),
-                                             "iters": args.flush_iters}
-        del flush
+            extras[d["workload"]] = {"config": d, "input_sha256": dict(gen.sha),
+                                     "kernels": time_kernels(np, timer, ls, args.flush_iters, K, 2)}
+            del ls, kp
+            torch.cuda.empty_cache()
+    gen.close()
+    del timer
+    torch.cuda.empty_cache()
 
     ceiling = None
-    if not args.no_copy_ceiling:
-        # practical ceiling: a 4 GiB device-to-device copy (the runtime's copy
-        # kernel), counted as bytes read plus bytes written
-        n = 4 << 30
-        src = torch.empty(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
-        src.fill_(1)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
-        for a, b in evs:
-            a.record(stream)
-            dst.copy_(src)
-            b.record(stream)
-        torch.cuda.synchronize()
-        ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
-        copy_gbps = 2 * n / (ms * 1e-3) / 1e9
-        ceiling = {"d2d_copy_GBps": round(copy_gbps, 1), "copy_bytes": 2 * n,
-                   "frac_of_copy": round(achieved / copy_gbps, 4)}
-        del src, dst
+    if not args.no_ceiling:
+        print("[bench] streaming ceiling", file=sys.stderr, flush=True)
+        ceiling = stream_ceiling(torch, dev, sh, np)
+        ceiling["frac_of_read2_write1"] = round(achieved / ceiling["read2_write1_GBps"], 4)
+        ceiling["frac_of_d2d_copy"] = round(achieved / ceiling["d2d_copy_GBps"], 4)
 
     cpu = None
     if not args.no_cpu_baseline and cpu_sample is not None:
         import oracle
 
-        n = args.cpu_sample_rows or {"moe_bwd": 4096, "moe_bwd_mx": 2048,
-                                     "blockwise": 2048, "relayout": 8192}.get(args.workload, 256)
-        print(f"[bench] timing the CPU oracle on a sample (n={n})", file=sys.stderr, flush=True)
-        dt, nbytes, what = cpu_sample(oracle, n)
-        cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": what, "seconds": round(dt, 2)}
+        print("[bench] timing the CPU oracle on a sample (one core, 3 runs)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(np, oracle, cpu_sample)
 
+    desc = dict(desc)
+    desc["io"] = "bf16 in; e4m3 q and e8m0 or fp32 scales out; fp32 arithmetic"
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -581,8 +785,7 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
-        "gpu_ms_per_step": round(gpu_step_ms, 5),
-        "ms_per_step_with_events": round(wall_instr * 1e3 / K, 5),
+        "gpu_ms_per_step": round(gpu_ms / K, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -590,19 +793,18 @@ def main():
         "data": "synthetic",
         "pct_of_peak": round(100.0 * value / PEAK_GBPS, 2),
         "config": desc,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": dl.kernel, "algorithmic_bytes_per_launch": dl.nbytes,
-                     "avg_launch_us": round(per_kernel_ms[dom] * 1e3, 2), "timing": event_kind},
-        "copy_ceiling": ceiling,
+        "roofline": roof,
         "kernels": kernels,
+        "workloads": extras,
+        "stream_ceiling": ceiling,
         "cpu_baseline": cpu,
+        "inputs": {"sha256": input_sha, "generator": "numpy PCG64 SeedSequence, rounded once to bf16 (RNE)"},
+        "outputs_sha256": out_sha,
+        "host": host_info(torch),
         "csrc_digest": csrc_digest(),
     }
     print(json.dumps(out), flush=True)
-    if dev is not None:
-        dev.close()
-    del keep
+    dev.close()
 
 
 if __name__ == "__main__":

@@ -1,0 +1,100 @@
+// Streaming probes for the practical HBM ceiling of the quantization
+// kernels' traffic (bench infrastructure, not part of libmxq).
+//
+// Every probe walks n bf16 elements of a contiguous buffer with 16-byte
+// nontemporal loads and / or 8-byte nontemporal stores of one byte per
+// element, the access sizes and hints the quantizers use, and does no
+// arithmetic worth the name:
+//   mode 0  2 bytes read + 1 byte written per element (the quantizers' mix);
+//   mode 1  2 bytes read per element (a word is stored only if the XOR of
+//           everything read equals a value that never occurs, which keeps
+//           the loads alive);
+//   mode 2  1 byte written per element.
+// A workgroup of 256 threads handles 4 x 2048 consecutive elements, each
+// thread issuing its four loads before its first store.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+constexpr int64_t kPerBlock = (int64_t)kThreads * 8 * kUnroll;
+
+// high byte of each of the eight bf16 values of a 16-byte load
+__device__ __forceinline__ u32x2 pack_high_bytes(u32x4 v)
+{
+    u32x2 r;
+    r.x = ((v.x >> 8) & 0xffu) | ((v.x >> 16) & 0xff00u) | (((v.y >> 8) & 0xffu) << 16) |
+          ((v.y & 0xff000000u));
+    r.y = ((v.z >> 8) & 0xffu) | ((v.z >> 16) & 0xff00u) | (((v.w >> 8) & 0xffu) << 16) |
+          ((v.w & 0xff000000u));
+    return r;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void stream_kernel(const uint16_t *__restrict__ in,
+                                                          uint8_t *__restrict__ out, int64_t n)
+{
+    const int64_t base = (int64_t)blockIdx.x * kPerBlock + 8 * threadIdx.x;
+    u32x4 v[kUnroll];
+    if constexpr (MODE != 2) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t e = base + (int64_t)u * kThreads * 8;
+            v[u] = e < n ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(in + e))
+                         : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    if constexpr (MODE == 0) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t e = base + (int64_t)u * kThreads * 8;
+            if (e < n)
+                __builtin_nontemporal_store(pack_high_bytes(v[u]), reinterpret_cast<u32x2 *>(out + e));
+        }
+    } else if constexpr (MODE == 1) {
+        uint32_t acc = 0u;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+        if (acc == 0x9E3779B9u && base < n)
+            out[(blockIdx.x * kThreads + threadIdx.x) & 1023] = (uint8_t)acc;
+    } else {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t e = base + (int64_t)u * kThreads * 8;
+            if (e < n) {
+                const uint32_t w = (uint32_t)e;
+                __builtin_nontemporal_store(u32x2{w, w ^ 0x5a5a5a5au}, reinterpret_cast<u32x2 *>(out + e));
+            }
+        }
+    }
+}
+
+}  // namespace
+
+// n: elements, a multiple of 8; in: 2n bytes (mode 0, 1), out: n bytes
+// (mode 0, 2) or 1024 bytes (mode 1); both 16-byte aligned.  Returns 0, or
+// -1 for bad arguments, or the HIP error of the launch.
+extern "C" int ceiling_stream(const void *in, void *out, int64_t n, int mode, void *stream)
+{
+    if (n <= 0 || n % 8 != 0 || mode < 0 || mode > 2 || !out || (mode != 2 && !in))
+        return -1;
+    const int64_t blocks = (n + kPerBlock - 1) / kPerBlock;
+    if (blocks > INT32_MAX)
+        return -1;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const uint16_t *x = reinterpret_cast<const uint16_t *>(in);
+    uint8_t *y = reinterpret_cast<uint8_t *>(out);
+    if (mode == 0)
+        stream_kernel<0><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(x, y, n);
+    else if (mode == 1)
+        stream_kernel<1><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(x, y, n);
+    else
+        stream_kernel<2><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(x, y, n);
+    return (int)hipGetLastError();
+}

@@ -19,7 +19,10 @@ def test_workload_table_names_every_configuration():
     sys.path.insert(0, ROOT)
     import bench
 
-    src = open(os.path.join(ROOT, "bench.py")).read()
-    for name in ("moe_bwd", "moe_bwd_mx", "mx3d", "mx3d_rceil", "blockwise", "relayout", "copy"):
-        assert f'"{name}"' in src, name
+    for name in ("mx3d_e64", "moe_bwd", "moe_bwd_mx", "mx3d", "mx3d_rceil", "blockwise",
+                 "blockwise_t", "relayout", "copy"):
+        assert name in bench.WORKLOADS, name
     assert callable(bench.build)
+    args = bench.parse([])
+    assert args.workload == "mx3d_e64" and args.gpus == 1
+    assert set(args.extras.split(",")) == {"moe_bwd", "mx3d", "blockwise"}
