@@ -73,6 +73,9 @@ def parse(argv=None):
     p.add_argument("--no-ceiling", action="store_true",
                    help="skip the device copy and the streaming probes")
     p.add_argument("--no-output-hash", action="store_true")
+    p.add_argument("--gen-workers", type=int, default=-1,
+                   help="host processes drawing the inputs (-1: one per core, at most 16; 0: draw "
+                        "in this process, e.g. under a profiler that would follow child processes)")
     return p.parse_args(argv)
 
 
@@ -115,8 +118,9 @@ class Generator:
     (numpy only: no GPU context), with the SHA-256 of every tensor's bytes
     in the order they are handed over."""
 
-    def __init__(self):
+    def __init__(self, workers: int = -1):
         self._pool = None
+        self.workers = _workers() if workers < 0 else workers
         self.sha = {}
 
     def pool(self):
@@ -124,16 +128,19 @@ class Generator:
             import multiprocessing as mp
             from concurrent.futures import ProcessPoolExecutor
 
-            self._pool = ProcessPoolExecutor(max_workers=_workers(), mp_context=mp.get_context("spawn"))
+            self._pool = ProcessPoolExecutor(max_workers=self.workers, mp_context=mp.get_context("spawn"))
         return self._pool
 
     def map(self, name, arglist, label):
         """Yield workloads.<name>(*args) for each args in order, hashing the
         concatenated bytes under ``label``."""
         h = hashlib.sha256()
-        futs = [self.pool().submit(_gen_call, name, tuple(a)) for a in arglist]
-        for f in futs:
-            out = f.result()
+        if self.workers == 0:
+            results = (_gen_call(name, tuple(a)) for a in arglist)
+        else:
+            futs = [self.pool().submit(_gen_call, name, tuple(a)) for a in arglist]
+            results = (f.result() for f in futs)
+        for out in results:
             h.update(memoryview(out).cast("B"))
             yield out
         self.sha[label] = h.hexdigest()
@@ -700,7 +707,7 @@ def main(argv=None):
     dev = DeviceEvents()
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    gen = Generator()
+    gen = Generator(args.gen_workers)
     print(f"[bench] building workload {args.workload}", file=sys.stderr, flush=True)
     launches, keep, desc, cpu_sample = build(args.workload, torch, mxq, workloads, gen)
     input_sha = dict(gen.sha)
