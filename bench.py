@@ -31,8 +31,9 @@ Timing:
   * per kernel, ``warm_us``: one event pair around K back-to-back launches
     of that kernel alone, divided by K (inputs partly in the caches when they
     fit).
-The extra workloads (``--extras``, default cfg1 moe_bwd, cfg2 mx3d and cfg4
-blockwise) are timed the same way and reported under ``workloads``; the
+The extra workloads (``--extras``, default the MoE jagged operands without
+and with a workspace, the E=8 MX 3D weights and the blockwise operands) are
+timed the same way and reported under ``workloads``; the
 streaming probes under ``stream_ceiling`` give the practical HBM ceiling of
 the same traffic mix.
 
@@ -54,7 +55,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_GBPS = 8000.0
 METRIC = "achieved HBM GB/s (bf16 read + fp8/scale write) and % of MI355X peak"
-DEFAULT_EXTRAS = "moe_bwd,mx3d,blockwise"
+DEFAULT_EXTRAS = "moe_bwd,moe_bwd_ws,mx3d,blockwise"
 FLUSH_BYTES = 1 << 30
 
 
@@ -182,7 +183,9 @@ def _sizes(offs):
     return [int(v) for v in np.diff(np.concatenate([[0], offs]))]
 
 
-def build_moe_bwd(torch, mxq, workloads, gen):
+def build_moe_bwd(torch, mxq, workloads, gen, ws=False):
+    """ws: the colwise operand through the call with a workspace (long token
+    groups split across workgroups, every element read once)."""
     go_t, x = list(gen.map("moe_grad_out_t", [()], "grad_out_t")) + list(gen.map("moe_x", [()], "x"))
     offs = workloads.moe_offsets()
     G = offs.size
@@ -195,15 +198,23 @@ def build_moe_bwd(torch, mxq, workloads, gen):
     q2 = torch.empty(R2 * C2, dtype=torch.uint8, device="cuda")
     s2 = torch.empty(G * C2, dtype=torch.float32, device="cuda")
     keep = [d_go, d_x, d_offs, q1, s1, q2, s2]
-    l1 = Launch("jagged_rowwise grad_out^T (4096,16384)", "jagged_contig_kernel",
+    l1 = Launch("jagged_rowwise grad_out^T (4096,16384)", "jagged_contig_kernel<8>",
                 mxq.mxq_quantize_jagged_rowwise,
                 (d_go.data_ptr(), R1, C1, C1, 1, d_offs.data_ptr(), G, q1.data_ptr(), C1, 1,
                  s1.data_ptr(), G, 1), 3 * R1 * C1 + 4 * R1 * G, R1 * C1, (("q1", q1), ("s1", s1)))
-    l2 = Launch("jagged_colwise x (16384,4096)", "jagged_strided_kernel",
-                mxq.mxq_quantize_jagged_colwise,
-                (d_x.data_ptr(), R2, C2, C2, 1, d_offs.data_ptr(), G, q2.data_ptr(), 1, R2,
-                 s2.data_ptr(), C2, 1), 3 * R2 * C2 + 4 * G * C2, R2 * C2, (("q2", q2), ("s2", s2)))
-    desc = {"workload": "moe_bwd_jagged",
+    cargs = (d_x.data_ptr(), R2, C2, C2, 1, d_offs.data_ptr(), G, q2.data_ptr(), 1, R2, s2.data_ptr(), C2, 1)
+    if ws:
+        nws = mxq.mxq_jagged_colwise_workspace_bytes(R2, C2, G)
+        d_ws = torch.zeros(max(nws, 4) // 4, dtype=torch.int32, device="cuda")
+        keep.append(d_ws)
+        l2 = Launch("jagged_colwise (workspace) x (16384,4096)", "jagged_strided_kernel<8, 3, 8, true>",
+                    mxq.mxq_quantize_jagged_colwise_ws, cargs + (d_ws.data_ptr(), nws),
+                    3 * R2 * C2 + 4 * G * C2, R2 * C2, (("q2", q2), ("s2", s2)))
+    else:
+        l2 = Launch("jagged_colwise x (16384,4096)", "jagged_strided_kernel<8, 3, 8, false>",
+                    mxq.mxq_quantize_jagged_colwise, cargs,
+                    3 * R2 * C2 + 4 * G * C2, R2 * C2, (("q2", q2), ("s2", s2)))
+    desc = {"workload": "moe_bwd_jagged" + ("_ws" if ws else ""),
             "tensors": "grad_out^T bf16 (4096,16384) rowwise -> row-major e4m3; "
                        "x bf16 (16384,4096) colwise -> column-major e4m3",
             "groups": int(G), "group_sizes": _sizes(offs),
@@ -241,7 +252,7 @@ def build_moe_bwd_mx(torch, mxq, workloads, gen):
     q2 = torch.empty(R2 * C2, dtype=torch.uint8, device="cuda")
     s2 = torch.empty(nb2 * C2, dtype=torch.uint8, device="cuda")
     keep = [d_go, d_x, d_offs, q1, s1, q2, s2]
-    l1 = Launch("jagged_mx_rowwise grad_out^T (4096,16384)", "jagged_mx_rowwise_kernel",
+    l1 = Launch("jagged_mx_rowwise grad_out^T (4096,16384)", "jagged_mx_rowwise_kernel<8>",
                 mxq.mxq_quantize_jagged_mx_rowwise,
                 (d_go.data_ptr(), R1, C1, C1, 1, d_offs.data_ptr(), G, q1.data_ptr(), C1, 1,
                  s1.data_ptr(), nb1, 1, 0), 3 * R1 * C1 + R1 * nb, R1 * C1, (("q1", q1),))
@@ -282,7 +293,7 @@ def build_mx3d(torch, mxq, workloads, gen, E, sweep, rceil=False):
             print(f"[bench] {e + 1} of {E} experts on the device", file=sys.stderr, flush=True)
     q = torch.empty(E * N * K, dtype=torch.uint8, device="cuda")
     s = torch.empty(E * (N // 32) * K, dtype=torch.uint8, device="cuda")
-    l = Launch(f"mx_3d_colwise ({E},{N},{K})", "block_strided_kernel<32, 1, true>",
+    l = Launch(f"mx_3d_colwise ({E},{N},{K})", "block_strided_kernel<32, 1, true, false>",
                mxq.mxq_quantize_mx_3d_colwise,
                (w.data_ptr(), E, N, K, N * K, K, 1, q.data_ptr(), N * K, 1, N, s.data_ptr(),
                 (N // 32) * K, K, 1, 1 if rceil else 0), 3 * E * N * K + E * (N // 32) * K, E * N * K,
@@ -311,11 +322,11 @@ def build_blockwise(torch, mxq, workloads, gen):
     sa = torch.empty(M * (Kd // 128), dtype=torch.float32, device="cuda")
     qw = torch.empty(R * C, dtype=torch.uint8, device="cuda")
     sw = torch.empty((R // 128) * (C // 128), dtype=torch.float32, device="cuda")
-    l1 = Launch("blockwise 1x128 act (8192,4096)", "block_contig_kernel<128, 8, false",
+    l1 = Launch("blockwise 1x128 act (8192,4096)", "block_contig_kernel<128, 8, false, 4>",
                 mxq.mxq_quantize_blockwise,
                 (da.data_ptr(), M, Kd, Kd, 1, 1, 128, qa.data_ptr(), Kd, 1, sa.data_ptr(),
                  Kd // 128, 1), 3 * M * Kd + 4 * M * (Kd // 128), M * Kd, (("qa", qa), ("sa", sa)))
-    l2 = Launch("blockwise 128x128 W (4096,4096)", "block_strided_kernel<128, 128, false>",
+    l2 = Launch("blockwise 128x128 W (4096,4096)", "block_strided_kernel<128, 128, false, false>",
                 mxq.mxq_quantize_blockwise,
                 (dw.data_ptr(), R, C, C, 1, 128, 128, qw.data_ptr(), 1, R, sw.data_ptr(),
                  C // 128, 1), 3 * R * C + 4 * (R // 128) * (C // 128), R * C, (("qw", qw), ("sw", sw)))
@@ -349,11 +360,11 @@ def build_blockwise_t(torch, mxq, workloads, gen):
     sw = torch.empty((R // 128) * (C // 128), dtype=torch.float32, device="cuda")
     # act^T: a (Kd, M) view with strides (1, Kd); 1 x 128 blocks along its rows
     # are 128 x 1 blocks of act; q of act^T row-major (Kd, M)
-    l1 = Launch("blockwise 1x128 act^T (4096,8192) view", "block_strided_kernel<128, 1, false>",
+    l1 = Launch("blockwise 1x128 act^T (4096,8192) view", "block_strided_kernel<128, 1, false, false>",
                 mxq.mxq_quantize_blockwise,
                 (da.data_ptr(), Kd, M, 1, Kd, 1, 128, qa.data_ptr(), M, 1, sa.data_ptr(),
                  M // 128, 1), 3 * M * Kd + 4 * Kd * (M // 128), M * Kd, (("qa", qa), ("sa", sa)))
-    l2 = Launch("blockwise 128x128 W^T (4096,4096) view", "block_strided_kernel<128, 128, false>",
+    l2 = Launch("blockwise 128x128 W^T (4096,4096) view", "block_strided_kernel<128, 128, false, false>",
                 mxq.mxq_quantize_blockwise,
                 (dw.data_ptr(), C, R, 1, C, 128, 128, qw.data_ptr(), R, 1, sw.data_ptr(),
                  R // 128, 1), 3 * R * C + 4 * (R // 128) * (C // 128), R * C, (("qw", qw), ("sw", sw)))
@@ -420,7 +431,7 @@ def build_copy(torch, mxq, workloads, gen):
 
 
 WORKLOADS = ("mx3d_e64", "mx3d_e1", "mx3d_e2", "mx3d_e4", "mx3d_e16", "mx3d", "mx3d_rceil",
-             "moe_bwd", "moe_bwd_mx", "blockwise", "blockwise_t", "relayout", "copy")
+             "moe_bwd", "moe_bwd_ws", "moe_bwd_mx", "blockwise", "blockwise_t", "relayout", "copy")
 
 
 def build(name, torch, mxq, workloads, gen):
@@ -428,6 +439,8 @@ def build(name, torch, mxq, workloads, gen):
         return build_copy(torch, mxq, workloads, gen)
     if name == "moe_bwd":
         return build_moe_bwd(torch, mxq, workloads, gen)
+    if name == "moe_bwd_ws":
+        return build_moe_bwd(torch, mxq, workloads, gen, ws=True)
     if name == "moe_bwd_mx":
         return build_moe_bwd_mx(torch, mxq, workloads, gen)
     if name == "mx3d":

@@ -35,6 +35,8 @@
  *                        not a multiple of 8.
  *   MXQ_ERR_UNSUPPORTED  a layout combination with no kernel (see each call).
  *   MXQ_ERR_LAUNCH       the launch failed (hipGetLastError after launch).
+ *   MXQ_ERR_WORKSPACE    a call that takes scratch memory was given less than
+ *                        it needs for these extents (nothing is launched).
  * A zero extent is not an error: the call writes whatever scales the
  * definition still assigns (an empty group's scale) and returns MXQ_OK.
  */
@@ -54,7 +56,8 @@ typedef enum mxq_status {
     MXQ_OK = 0,
     MXQ_ERR_INVALID_ARG = 1,
     MXQ_ERR_UNSUPPORTED = 2,
-    MXQ_ERR_LAUNCH = 3
+    MXQ_ERR_LAUNCH = 3,
+    MXQ_ERR_WORKSPACE = 4
 } mxq_status;
 
 /*
@@ -120,6 +123,39 @@ mxq_status mxq_quantize_jagged_colwise(const uint16_t *x, int64_t rows, int64_t 
                                        int64_t sx_c, const int32_t *offs, int32_t num_groups,
                                        uint8_t *q, int64_t sq_r, int64_t sq_c, float *scales,
                                        int64_t ss_g, int64_t ss_c, void *stream);
+
+/*
+ * Jagged COLWISE quantization with a caller's workspace: the same operation,
+ * arguments and results as mxq_quantize_jagged_colwise.  Source: as above;
+ * the pages' kernels keep a whole token group of a column block in one
+ * program, which on a GPU with 256 compute units leaves the longest group's
+ * columns on a few of them.
+ *
+ * For a row-major x and column-major q, token groups longer than the rows one
+ * workgroup holds (3072) are cut into chunks quantized by separate
+ * workgroups, which exchange their column maxima through the workspace, so
+ * every element is read from memory once (the call without a workspace reads
+ * the rows of such groups twice).  The column-major-in layout needs no
+ * workspace and runs as mxq_quantize_jagged_colwise.
+ *
+ * workspace        device memory of at least
+ *                  mxq_jagged_colwise_workspace_bytes(rows, cols, num_groups)
+ *                  bytes, 4-byte aligned, filled with zeros before its first
+ *                  use; every call leaves it filled with zeros again, so it
+ *                  can be reused by later calls (and graph replays) without
+ *                  clearing.  Owned by the caller.  Two calls that overlap in
+ *                  time must not share a workspace.
+ * workspace_bytes  its size; too small -> MXQ_ERR_WORKSPACE, before any launch.
+ */
+mxq_status mxq_quantize_jagged_colwise_ws(const uint16_t *x, int64_t rows, int64_t cols,
+                                          int64_t sx_r, int64_t sx_c, const int32_t *offs,
+                                          int32_t num_groups, uint8_t *q, int64_t sq_r,
+                                          int64_t sq_c, float *scales, int64_t ss_g, int64_t ss_c,
+                                          void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Workspace bytes mxq_quantize_jagged_colwise_ws needs for these extents (a
+ * bound that holds for any offsets); -1 for invalid arguments. */
+int64_t mxq_jagged_colwise_workspace_bytes(int64_t rows, int64_t cols, int32_t num_groups);
 
 /*
  * MXFP8 quantization of 3D expert weights along N ("colwise", 32 x 1 blocks).
@@ -276,6 +312,21 @@ mxq_status mxq_quantize_blockwise(const uint16_t *x, int64_t rows, int64_t cols,
  *                   can produce (|RN32(x * 448 / max(amax, eps))| <= 448 +
  *                   2^-15 whenever |x| <= amax).
  */
+/*
+ * TEST-ONLY: mxq_quantize_jagged_colwise_ws for a row-major x and a
+ * column-major q with the bound on how long a chunk waits for the other
+ * chunks of its token group set by the caller (in polls); 0 looks once, a
+ * negative value never waits, so the chunks reduce their groups' rows
+ * themselves (the path taken when the others do not arrive in time).  Other
+ * layouts -> MXQ_ERR_INVALID_ARG.
+ */
+mxq_status mxq_debug_jagged_colwise_ws_spin(const uint16_t *x, int64_t rows, int64_t cols,
+                                            int64_t sx_r, int64_t sx_c, const int32_t *offs,
+                                            int32_t num_groups, uint8_t *q, int64_t sq_r,
+                                            int64_t sq_c, float *scales, int64_t ss_g,
+                                            int64_t ss_c, void *workspace,
+                                            int64_t workspace_bytes, int32_t spin_limit,
+                                            void *stream);
 mxq_status mxq_debug_cast_e4m3(const float *y, int64_t n, uint8_t *out, void *stream);
 mxq_status mxq_debug_cast4_e4m3(const float *y, int64_t n, uint8_t *out, int32_t unclamped,
                                 void *stream);

@@ -15,7 +15,9 @@ quantize multipliers ``448 / max(amax, 1e-12)``; e8m0 scales are
 from __future__ import annotations
 
 from . import _capi
-from ._capi import (MXQ_ERR_INVALID_ARG, MXQ_ERR_LAUNCH, MXQ_ERR_UNSUPPORTED, MXQ_MAX_GROUPS,
+from ._capi import (MXQ_ERR_INVALID_ARG, MXQ_ERR_LAUNCH, MXQ_ERR_UNSUPPORTED, MXQ_ERR_WORKSPACE,
+                    MXQ_MAX_GROUPS, mxq_debug_jagged_colwise_ws_spin,
+                    mxq_jagged_colwise_workspace_bytes, mxq_quantize_jagged_colwise_ws,
                     MXQ_OK, MXQ_SCALE_FLOOR, MXQ_SCALE_RCEIL, LibraryMissing,
                     mxq_abi_version, mxq_debug_cast4_e4m3, mxq_debug_cast_e4m3,
                     mxq_quantize_blockwise,
@@ -32,7 +34,9 @@ __all__ = [
     "mxq_quantize_jagged_rowwise", "mxq_quantize_jagged_colwise", "mxq_quantize_mx_3d_colwise",
     "mxq_quantize_mx_rowwise", "mxq_quantize_jagged_mx_rowwise", "mxq_quantize_jagged_mx_colwise",
     "mxq_relayout_mx_scales_grouped", "mxq_quantize_blockwise", "mxq_debug_cast_e4m3",
-    "mxq_debug_cast4_e4m3", "debug_cast4_e4m3",
+    "mxq_debug_cast4_e4m3", "debug_cast4_e4m3", "jagged_colwise_workspace",
+    "mxq_quantize_jagged_colwise_ws", "mxq_jagged_colwise_workspace_bytes",
+    "mxq_debug_jagged_colwise_ws_spin",
     "mxq_abi_version", "LibraryMissing",
 ]
 
@@ -117,10 +121,24 @@ def quantize_jagged_rowwise(x, offs, *, stream=None):
     return q, s
 
 
-def quantize_jagged_colwise(x, offs, *, stream=None):
+def jagged_colwise_workspace(rows: int, cols: int, num_groups: int, device=None):
+    """A zero-filled workspace for ``quantize_jagged_colwise(...,
+    workspace=ws)`` on (rows, cols) with num_groups groups.  Every call
+    leaves it zero-filled, so it can be kept and reused by calls that do not
+    overlap in time."""
+    torch = _torch()
+    n = mxq_jagged_colwise_workspace_bytes(rows, cols, num_groups)
+    if n < 0:
+        raise MXQError(MXQ_ERR_INVALID_ARG, "mxq_jagged_colwise_workspace_bytes")
+    return torch.zeros(max(n, 4) // 4, dtype=torch.int32, device=device or "cuda")
+
+
+def quantize_jagged_colwise(x, offs, *, workspace=None, stream=None):
     """Per-(group, column) scaling with groups along dim 0 of ``x`` (rows,
     cols).  Returns ``(q, scales)``: q (rows, cols) column-major e4m3, scales
-    (G, cols) fp32."""
+    (G, cols) fp32.  With a ``workspace`` (``jagged_colwise_workspace``),
+    groups longer than one workgroup's rows are split across workgroups and
+    every element is read once."""
     torch = _torch()
     _require_bf16_cuda(x, 2, "x")
     _require_offs(offs, x)
@@ -128,10 +146,16 @@ def quantize_jagged_colwise(x, offs, *, stream=None):
     G = offs.numel()
     q = _empty_colmajor_u8(torch, rows, cols, x.device)
     s = torch.empty((G, cols), dtype=torch.float32, device=x.device)
-    code = mxq_quantize_jagged_colwise(
-        x.data_ptr(), rows, cols, x.stride(0), x.stride(1), offs.data_ptr(), G, q.data_ptr(),
-        q.stride(0), q.stride(1), s.data_ptr(), s.stride(0), s.stride(1), _stream(x, stream))
-    _check(code, "mxq_quantize_jagged_colwise")
+    args = (x.data_ptr(), rows, cols, x.stride(0), x.stride(1), offs.data_ptr(), G, q.data_ptr(),
+            q.stride(0), q.stride(1), s.data_ptr(), s.stride(0), s.stride(1))
+    if workspace is None:
+        _check(mxq_quantize_jagged_colwise(*args, _stream(x, stream)), "mxq_quantize_jagged_colwise")
+    else:
+        if not workspace.is_cuda or workspace.device != x.device or not workspace.is_contiguous():
+            raise TypeError("workspace must be a contiguous CUDA tensor on x's device")
+        nbytes = workspace.numel() * workspace.element_size()
+        _check(mxq_quantize_jagged_colwise_ws(*args, workspace.data_ptr(), nbytes, _stream(x, stream)),
+               "mxq_quantize_jagged_colwise_ws")
     return q, s
 
 

@@ -18,6 +18,7 @@ MXQ_OK = 0
 MXQ_ERR_INVALID_ARG = 1
 MXQ_ERR_UNSUPPORTED = 2
 MXQ_ERR_LAUNCH = 3
+MXQ_ERR_WORKSPACE = 4
 MXQ_SCALE_FLOOR = 0
 MXQ_SCALE_RCEIL = 1
 MXQ_MAX_GROUPS = 4096
@@ -46,10 +47,15 @@ SIGNATURES = {
     "mxq_relayout_mx_scales_grouped": [_vp, _i64, _i64, _i64, _vp, _i32, _i64, _vp, _vp, _vp],
     "mxq_quantize_blockwise": [_vp, _i64, _i64, _i64, _i64, _i32, _i32, _vp, _i64, _i64, _vp,
                                _i64, _i64, _vp],
+    "mxq_quantize_jagged_colwise_ws": [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _i64, _i64,
+                                       _vp, _i64, _i64, _vp, _i64, _vp],
+    "mxq_jagged_colwise_workspace_bytes": [_i64, _i64, _i32],
+    "mxq_debug_jagged_colwise_ws_spin": [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _i64, _i64,
+                                         _vp, _i64, _i64, _vp, _i64, _i32, _vp],
     "mxq_debug_cast_e4m3": [_vp, _i64, _vp, _vp],
     "mxq_debug_cast4_e4m3": [_vp, _i64, _vp, _i32, _vp],
 }
-RESTYPES = {"mxq_status_string": ctypes.c_char_p}
+RESTYPES = {"mxq_status_string": ctypes.c_char_p, "mxq_jagged_colwise_workspace_bytes": _i64}
 
 _lib = None
 
@@ -98,5 +104,8 @@ mxq_quantize_jagged_mx_rowwise = _fwd("mxq_quantize_jagged_mx_rowwise")
 mxq_quantize_jagged_mx_colwise = _fwd("mxq_quantize_jagged_mx_colwise")
 mxq_relayout_mx_scales_grouped = _fwd("mxq_relayout_mx_scales_grouped")
 mxq_quantize_blockwise = _fwd("mxq_quantize_blockwise")
+mxq_quantize_jagged_colwise_ws = _fwd("mxq_quantize_jagged_colwise_ws")
+mxq_jagged_colwise_workspace_bytes = _fwd("mxq_jagged_colwise_workspace_bytes")
+mxq_debug_jagged_colwise_ws_spin = _fwd("mxq_debug_jagged_colwise_ws_spin")
 mxq_debug_cast_e4m3 = _fwd("mxq_debug_cast_e4m3")
 mxq_debug_cast4_e4m3 = _fwd("mxq_debug_cast4_e4m3")

@@ -20,6 +20,15 @@ using namespace mxq;
 constexpr int kJaggedStridedCG = 8;     // 64-column strips (full 128-byte row pieces)
 constexpr int kJaggedStridedTiles = 3;  // register tiles per lane (233 VGPRs, 2 waves per SIMD)
 constexpr int kJaggedStridedWaves = 8;  // waves per workgroup: tile = 8*16*64/CG = 1024 rows
+// the colwise kernel with a workspace: 4-wave workgroups (two per CU, so one
+// workgroup's loads overlap another's exchange and stores), tiles of 512
+// rows, chunks of 3 tiles (measured against 8 waves and 2 tiles)
+constexpr int kSplitTiles = 3;
+constexpr int kSplitWaves = 4;
+// polls of a split colwise chunk waiting for the other chunks of its group
+// (each a device-scope load and a short sleep, about a microsecond) before
+// it reduces the group's rows itself
+constexpr int kColwiseSpinLimit = 4000;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -97,37 +106,73 @@ mxq_status run_jagged_contig(const uint16_t *x, int64_t nrows, int64_t ext, int6
     return launch_status();
 }
 
-// jagged, reduction across rows of a (ext, ncols) row-major view, column-major q
+// Grid and workspace of the colwise (strided) kernel on an (ext, ncols)
+// view with G groups.  Items per strip (long groups and packs of short
+// groups; only the device knows which) are bounded from the extent and G
+// alone: a long group spans more than TROWS - 15 rows, so there are at most
+// ext / (TROWS - 14) of them; a run of short groups starts at group 0 or
+// where a group start enters another TROWS-row block (which includes every
+// group after a long one), so there are at most ext / TROWS + 1 runs, each
+// packed kPackMax groups at a time; and every item owns a group.  In split
+// mode a long group of span n (rows from its 16-row-aligned start) makes
+// ceil(n / CH) items, i.e. fewer than n / CH more than one, and the spans of
+// at most min(G, ext / (TROWS - 14)) long groups add up to at most the
+// extent plus 15 rows each.  Workgroups past the items exit after building
+// the table, which costs about a microsecond per CU each.
+struct ColwisePlan {
+    int64_t nsuper, items, nblocks, ws_bytes;
+};
+
+ColwisePlan colwise_plan(int64_t ext, int64_t ncols, int64_t G, bool split)
+{
+    constexpr int CG = kJaggedStridedCG, SPS = 8 / CG;
+    const int NW = split ? kSplitWaves : kJaggedStridedWaves;
+    const int64_t trows = 16 * NW * (64 / CG);
+    const int64_t chunk = kSplitTiles * trows;
+    ColwisePlan p;
+    const int64_t nstrips = (ncols + 8 * CG - 1) / (8 * CG);
+    p.nsuper = (nstrips + SPS - 1) / SPS;
+    const int64_t nlong = ext / (trows - 14);
+    const int64_t bound = nlong + ext / trows + G / kPackMax + 1;
+    p.items = std::min<int64_t>(G, bound);
+    if (split)
+        p.items += (ext + 15 * std::min<int64_t>(G, nlong)) / chunk;
+    p.nblocks = 8 * SPS * ((p.items * p.nsuper + 7) / 8);
+    // one set per (first item of a long group, strip)
+    p.ws_bytes = split ? p.items * p.nsuper * SPS * kSetWords * (int64_t)sizeof(uint32_t) : 0;
+    return p;
+}
+
+// jagged, reduction across rows of a (ext, ncols) row-major view, column-major
+// q; split mode exchanges column maxima through ws (zero between calls)
 mxq_status run_jagged_strided(const uint16_t *x, int64_t ext, int64_t ncols, int64_t ldx,
                               const int32_t *offs, int32_t G, uint8_t *q, int64_t ldq,
-                              float *scales, int64_t ss_g, int64_t ss_col, hipStream_t st)
+                              float *scales, int64_t ss_g, int64_t ss_col, hipStream_t st,
+                              uint32_t *ws = nullptr, int64_t ws_bytes = 0,
+                              int spin_limit = kColwiseSpinLimit)
 {
     if (ncols == 0)
         return MXQ_OK;
     if (ncols % 8 != 0 || ncols > INT32_MAX)
         return MXQ_ERR_INVALID_ARG;
-    constexpr int CG = kJaggedStridedCG, SPS = 8 / CG, NW = kJaggedStridedWaves;
-    const int64_t nstrips = (ncols + 8 * CG - 1) / (8 * CG);
-    const int64_t nsuper = (nstrips + SPS - 1) / SPS;
-    // items per strip (long groups and packs of short groups; only the
-    // device knows which), bounded from the extent and G alone: a long group
-    // spans more than TROWS - 15 rows, so there are at most ext / (TROWS -
-    // 14) of them; a run of short groups starts at group 0 or where a group
-    // start enters another TROWS-row block (which includes every group
-    // after a long one), so there are at most ext / TROWS + 1 runs, each
-    // packed kPackMax groups at a time; and every item owns a group.
-    // Workgroups past the items exit after building the table, which costs
-    // about a microsecond per CU each.
-    constexpr int64_t trows = 16 * NW * (64 / CG);
-    const int64_t bound = ext / (trows - 14) + ext / trows + G / kPackMax + 1;
-    const int64_t items = std::min<int64_t>(G, bound);
-    const int64_t nblocks = 8 * SPS * ((items * nsuper + 7) / 8);
-    if (nblocks > INT32_MAX)
+    constexpr int CG = kJaggedStridedCG, NW = kJaggedStridedWaves, T = kJaggedStridedTiles;
+    constexpr int NWS = kSplitWaves, TS = kSplitTiles;
+    const bool split = ws != nullptr;
+    const ColwisePlan p = colwise_plan(ext, ncols, G, split);
+    if (p.nblocks > INT32_MAX || p.items > INT32_MAX)
         return MXQ_ERR_INVALID_ARG;
+    if (split && ws_bytes < p.ws_bytes)
+        return MXQ_ERR_WORKSPACE;
     const size_t lds = G > 64 ? (3 * (size_t)G + 2) * sizeof(int) + (size_t)G : 0;
-    jagged_strided_kernel<CG, kJaggedStridedTiles, NW>
-        <<<dim3((unsigned)nblocks), dim3(64 * NW), lds, st>>>(x, ldx, (int)ext, (int)ncols, offs, G, q,
-                                                           ldq, scales, ss_g, ss_col, (int)nsuper);
+    const dim3 grid((unsigned)p.nblocks), block(64 * (split ? NWS : NW));
+    if (split)
+        jagged_strided_kernel<CG, TS, NWS, true><<<grid, block, lds, st>>>(
+            x, ldx, (int)ext, (int)ncols, offs, G, q, ldq, scales, ss_g, ss_col, (int)p.nsuper,
+            (int)p.items, ws, spin_limit);
+    else
+        jagged_strided_kernel<CG, T, NW, false><<<grid, block, lds, st>>>(
+            x, ldx, (int)ext, (int)ncols, offs, G, q, ldq, scales, ss_g, ss_col, (int)p.nsuper,
+            (int)p.items, nullptr, 0);
     return launch_status();
 }
 
@@ -241,6 +286,7 @@ const char *mxq_status_string(int status)
     case MXQ_ERR_INVALID_ARG: return "MXQ_ERR_INVALID_ARG";
     case MXQ_ERR_UNSUPPORTED: return "MXQ_ERR_UNSUPPORTED";
     case MXQ_ERR_LAUNCH: return "MXQ_ERR_LAUNCH";
+    case MXQ_ERR_WORKSPACE: return "MXQ_ERR_WORKSPACE";
     default: return "MXQ_ERR_UNKNOWN";
     }
 }
@@ -294,6 +340,40 @@ mxq_status mxq_quantize_jagged_colwise(const uint16_t *x, int64_t rows, int64_t 
         return run_jagged_contig(x, cols, rows, sx_c, offs, num_groups, q, sq_c, scales, ss_c, ss_g, st);
     }
     return MXQ_ERR_UNSUPPORTED;
+}
+
+int64_t mxq_jagged_colwise_workspace_bytes(int64_t rows, int64_t cols, int32_t num_groups)
+{
+    if (rows < 0 || cols < 0 || num_groups < 1 || num_groups > MXQ_MAX_GROUPS)
+        return -1;
+    return colwise_plan(rows, cols, num_groups, true).ws_bytes;
+}
+
+mxq_status mxq_quantize_jagged_colwise_ws(const uint16_t *x, int64_t rows, int64_t cols,
+                                          int64_t sx_r, int64_t sx_c, const int32_t *offs,
+                                          int32_t num_groups, uint8_t *q, int64_t sq_r,
+                                          int64_t sq_c, float *scales, int64_t ss_g, int64_t ss_c,
+                                          void *workspace, int64_t workspace_bytes, void *stream)
+{
+    mxq_status s = check_jagged_common(x, rows, cols, offs, num_groups, q, scales);
+    if (s != MXQ_OK)
+        return s;
+    if (workspace_bytes < 0 || (workspace && (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0))
+        return MXQ_ERR_INVALID_ARG;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (cols == 0)
+        return MXQ_OK;
+    if (sx_c == 1 && sq_r == 1) {
+        if (sx_r % 8 != 0 || sq_c % 16 != 0)
+            return MXQ_ERR_INVALID_ARG;
+        if (!workspace)
+            return MXQ_ERR_WORKSPACE;
+        return run_jagged_strided(x, rows, cols, sx_r, offs, num_groups, q, sq_c, scales, ss_g, ss_c,
+                                  st, reinterpret_cast<uint32_t *>(workspace), workspace_bytes);
+    }
+    // the other layout reads every row once without a workspace
+    return mxq_quantize_jagged_colwise(x, rows, cols, sx_r, sx_c, offs, num_groups, q, sq_r, sq_c,
+                                       scales, ss_g, ss_c, stream);
 }
 
 mxq_status mxq_quantize_mx_3d_colwise(const uint16_t *w, int64_t E, int64_t N, int64_t K,
@@ -583,6 +663,23 @@ extern "C" mxq_status mxq_debug_cast_e4m3(const float *y, int64_t n, uint8_t *ou
         return MXQ_ERR_INVALID_ARG;
     debug_cast_kernel<<<dim3(debug_grid(n)), dim3(256), 0, reinterpret_cast<hipStream_t>(stream)>>>(y, n, out);
     return launch_status();
+}
+
+// the split colwise path with a given wait bound (see include/mxq.h)
+extern "C" mxq_status mxq_debug_jagged_colwise_ws_spin(
+    const uint16_t *x, int64_t rows, int64_t cols, int64_t sx_r, int64_t sx_c, const int32_t *offs,
+    int32_t num_groups, uint8_t *q, int64_t sq_r, int64_t sq_c, float *scales, int64_t ss_g,
+    int64_t ss_c, void *workspace, int64_t workspace_bytes, int32_t spin_limit, void *stream)
+{
+    mxq_status s = check_jagged_common(x, rows, cols, offs, num_groups, q, scales);
+    if (s != MXQ_OK)
+        return s;
+    if (!(sx_c == 1 && sq_r == 1) || !workspace || workspace_bytes < 0 ||
+        (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0 || sx_r % 8 != 0 || sq_c % 16 != 0)
+        return MXQ_ERR_INVALID_ARG;
+    return run_jagged_strided(x, rows, cols, sx_r, offs, num_groups, q, sq_c, scales, ss_g, ss_c,
+                              reinterpret_cast<hipStream_t>(stream),
+                              reinterpret_cast<uint32_t *>(workspace), workspace_bytes, spin_limit);
 }
 
 extern "C" mxq_status mxq_debug_cast4_e4m3(const float *y, int64_t n, uint8_t *out, int32_t unclamped,

@@ -378,6 +378,32 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_long_kernel(
 // one wave, lane g holding group g), then the packs in group order.
 constexpr int kPackMax = 16;
 
+// Split path (a caller's workspace): a long group's 16-row-aligned span
+// [lo & ~15, hi) is cut into nc = ceil(span / CH) chunks of
+// csz = round16(ceil(span / nc)) <= CH rows (the last one shorter), each
+// chunk an item of its own that holds its rows in registers; the chunks of
+// one (group, strip) exchange their column maxima through the workspace, so
+// no row is read twice.
+__device__ __forceinline__ int chunk_count(int lo, int hi, int ch)
+{
+    const int span = hi - (lo & ~15);
+    return (span + ch - 1) / ch;
+}
+__device__ __forceinline__ int chunk_rows(int lo, int hi, int nc)
+{
+    const int span = hi - (lo & ~15);
+    return ((span + nc - 1) / nc + 15) & ~15;
+}
+
+// Workspace of the split path: one set of kSetWords 32-bit words per
+// (long group, column strip), addressed by the group's first item index:
+// the strip's column maxima (|bf16| bit patterns, at most 64 words), the
+// arrival count (word 64) and the departure count (word 65).  Zero between
+// calls: the last chunk to leave a set clears it.
+constexpr int kSetWords = 72;
+constexpr int kSetArrive = 64;
+constexpr int kSetDepart = 65;
+
 // Workgroup -> (item, column strip).  SPS = 8 / CG strips of 8*CG columns
 // (16*CG bytes of a row) make one 128-byte "superstrip"; the SPS workgroups
 // of a superstrip get block ids that differ by 8, so with the round-robin
@@ -390,7 +416,7 @@ struct StripMap {
 };
 
 template <int SPS>
-__device__ __forceinline__ StripMap map_strip(int b, int nsuper, int G)
+__device__ __forceinline__ StripMap map_strip(int b, int nsuper, int max_items)
 {
     const int x = b & 7;               // XCD slot
     const int k = b >> 3;
@@ -399,7 +425,7 @@ __device__ __forceinline__ StripMap map_strip(int b, int nsuper, int G)
     StripMap m;
     m.item = S / nsuper;
     m.strip = (S % nsuper) * SPS + sub;
-    m.valid = m.item < G;
+    m.valid = m.item < max_items;
     return m;
 }
 
@@ -407,7 +433,8 @@ __device__ __forceinline__ StripMap map_strip(int b, int nsuper, int G)
 // (clamped group ends), s_lead (1 for a group that starts a pack), s_lpre /
 // s_ppre (exclusive prefix counts of long groups / pack leaders by group
 // index; long groups then go in index order).  TR = rows per tile.
-template <int NTH, int TR>
+// In split mode (CH > 0) s_lpre counts a long group's chunks instead of 1.
+template <int NTH, int TR, int CH>
 __device__ void strided_table(const int32_t *__restrict__ offs, int G, int rows, int *s_end,
                               uint8_t *s_lead, int *s_lpre, int *s_ppre)
 {
@@ -456,7 +483,12 @@ __device__ void strided_table(const int32_t *__restrict__ offs, int G, int rows,
         }
         __syncthreads();
     }
-    slot_prefix2<NTH>(G, s_lpre, s_ppre, [&](int g) { return is_long(g) ? 1 : 0; },
+    slot_prefix2<NTH>(G, s_lpre, s_ppre,
+                      [&](int g) {
+                          if (!is_long(g))
+                              return 0;
+                          return CH > 0 ? chunk_count(lo_of(g), s_end[g], CH) : 1;
+                      },
                       [&](int g) { return (int)s_lead[g]; });
 }
 
@@ -477,18 +509,32 @@ __device__ void strided_table(const int32_t *__restrict__ offs, int G, int rows,
 // L2 merges the parts, where nontemporal partial writes would each cost HBM
 // a read-modify-write (55.5 against 52.2 us on the MoE x operand, 72 against
 // 52 us with q 16 bytes off the lines).
-template <int CG, int T, int NW>
+//
+// SPLIT: long groups come as chunks of at most T tiles (see chunk_count),
+// so every row is read once; the chunks of one (group, strip) publish their
+// column maxima to the workspace `ws` with device-scope atomics, count their
+// arrival, wait for the others (at most spin_limit polls; past it, or at
+// once for a negative limit, a chunk reduces its group's rows of the strip
+// itself, which is always correct),
+// and count their departure; the last to leave clears the set.  Chunks of a
+// set have consecutive item numbers, and workgroups are dispatched in order,
+// so the waits are short.  max_items: the grid's item bound.
+template <int CG, int T, int NW, bool SPLIT = false>
 __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int rows, int cols,
     const int32_t *__restrict__ offs, int G, uint8_t *__restrict__ q, int64_t ldq,
-    float *__restrict__ scales, int64_t ss_g, int64_t ss_c, int nsuper)
+    float *__restrict__ scales, int64_t ss_g, int64_t ss_c, int nsuper, int max_items,
+    uint32_t *__restrict__ ws, int spin_limit)
 {
     constexpr int QD = 64 / CG;       // 16-row pieces per wave
     constexpr int WROWS = 16 * QD;    // rows per wave
     constexpr int TROWS = NW * WROWS; // rows per register tile
     constexpr int SW = 8 * CG;        // strip width in columns
     constexpr int NTH = 64 * NW;
+    constexpr int CH = SPLIT ? T * TROWS : 0;   // rows per chunk of a long group
     static_assert(T >= 2, "a pack spans up to two tiles");
+    static_assert(SW + 2 <= kSetWords, "a strip's maxima and two counters fit a set");
+    static_assert(!SPLIT || CG == 8, "split mode numbers workgroups one strip per superstrip");
 
     // group tables: 64 ends in static LDS; for G > 64 the launch passes
     // (3G + 2) ints and G bytes of dynamic LDS.  Little LDS lets the next
@@ -503,7 +549,7 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
     __shared__ float s_scale[SW];
     __shared__ uint32_t s_pk[kPackMax][SW];   // pack: column maxima, then multipliers
 
-    const StripMap sm = map_strip<8 / CG>(blockIdx.x, nsuper, G);
+    const StripMap sm = map_strip<8 / CG>(blockIdx.x, nsuper, max_items);
     if (!sm.valid)
         return;
 
@@ -513,8 +559,10 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
     const int cg = lane % CG;
     const int qd = lane / CG;
 
-    // this workgroup's item: a long group g, or a pack of short groups [g0, g1)
-    __shared__ int s_sel[3];
+    // this workgroup's item: a long group g (in split mode: its chunk k, and
+    // the group's first item number, which names its workspace set), or a
+    // pack of short groups [g0, g1)
+    __shared__ int s_sel[4];
     if (G <= 64) {
         // one wave builds the table with lane g holding group g
         if (w == 0) {
@@ -540,19 +588,28 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
             const bool lead = valid && !lng && ((lane - run) % kPackMax) == 0;
             const uint64_t mlong = __ballot(lng);
             const uint64_t mlead = __ballot(lead);
-            const int nl = __popcll(mlong);
+            // items of each long group: 1, or its chunks in split mode
+            const int nch = lng ? (SPLIT ? chunk_count(lo, hi, CH) : 1) : 0;
+            int nl = nch;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1)
+                nl += __shfl_xor(nl, d, 64);
             const int item = sm.item;
             if (item < nl) {
-                // rank of a long group: longer first, ties by index
-                int r = 0;
+                // long groups in rank order: longer first, ties by index; the
+                // group's first item is the count of items ranked before it
+                int first = 0;
                 for (int h = 0; h < G; ++h) {
                     const int lh = __builtin_amdgcn_readlane(len, h);
+                    const int nh = __builtin_amdgcn_readlane(nch, h);
                     const bool hl = (mlong >> h) & 1ull;
-                    r += hl && ((lh > len) || (lh == len && h < lane));
+                    first += (hl && ((lh > len) || (lh == len && h < lane))) ? nh : 0;
                 }
-                if (lng && r == item) {
+                if (lng && first <= item && item < first + nch) {
                     s_sel[0] = 0;
                     s_sel[1] = lane;
+                    s_sel[2] = item - first;
+                    s_sel[3] = first;
                 }
             } else if (lane == 0) {
                 int k = item - nl;
@@ -575,12 +632,15 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
         }
         __syncthreads();
     } else {
-        strided_table<NTH, TROWS>(offs, G, rows, s_end, s_lead, s_lpre, s_ppre);
+        strided_table<NTH, TROWS, CH>(offs, G, rows, s_end, s_lead, s_lpre, s_ppre);
         if (t == 0) {
             const int nlong = s_lpre[G], npack = s_ppre[G];
             if (sm.item < nlong) {
+                const int g = find_slot(s_lpre, G, sm.item);
                 s_sel[0] = 0;
-                s_sel[1] = find_slot(s_lpre, G, sm.item);
+                s_sel[1] = g;
+                s_sel[2] = sm.item - s_lpre[g];
+                s_sel[3] = s_lpre[g];
             } else if (sm.item < nlong + npack) {
                 const int pk = sm.item - nlong;
                 const int g0 = find_slot(s_ppre, G, pk);
@@ -786,25 +846,39 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
         return;
     }
 
-    // ---- a long group
+    // ---- a long group (in split mode, chunk k of it)
     const int g = s_sel[1];
     const int lo = g ? s_end[g - 1] : 0;
     int hi = s_end[g];
     hi = hi < lo ? lo : hi;
 
-    const int cbase = sm.strip * SW + 8 * cg;
+    // rows this workgroup holds: [clo, chi) inside [lo, hi), tiles from rbeg
+    int rbeg = lo & ~15, clo = lo, chi = hi, nc = 1, k = 0, strip = sm.strip;
+    if constexpr (SPLIT) {
+        // a long group's workgroups run strip-major over its chunks, so the
+        // chunks of one (group, strip), which wait for each other, have
+        // consecutive workgroup numbers (one strip per superstrip here)
+        nc = chunk_count(lo, hi, CH);
+        const int local = (sm.item - s_sel[3]) * nsuper + sm.strip;
+        strip = local / nc;
+        k = local % nc;
+        const int csz = chunk_rows(lo, hi, nc);
+        rbeg = (lo & ~15) + k * csz;
+        clo = rbeg > lo ? rbeg : lo;
+        chi = rbeg + csz < hi ? rbeg + csz : hi;
+    }
+    const int nit = chi > clo ? (chi - rbeg + TROWS - 1) / TROWS : 0;
+    const int cbase = strip * SW + 8 * cg;
     const bool col_ok = cbase < cols;
-    const int rbeg = lo & ~15;
-    const int nit = hi > lo ? (hi - rbeg + TROWS - 1) / TROWS : 0;
 
     uint4 v[T][16];
 
-    // one register tile: 16 rows x 8 columns per lane; rows outside [lo, hi)
-    // are neither read nor counted.  Tiles that will be read again (keep)
-    // use ordinary loads, the others the streaming hint.
+    // one register tile: 16 rows x 8 columns per lane; rows outside
+    // [clo, chi) are neither read nor counted.  Tiles that will be read
+    // again (keep) use ordinary loads, the others the streaming hint.
     auto load_tile = [&](uint4 (&d)[16], int it, bool keep) {
         const int rb = rbeg + it * TROWS + w * WROWS + 16 * qd;
-        const bool full = rb >= lo && rb + 16 <= hi;
+        const bool full = rb >= clo && rb + 16 <= chi;
         const uint16_t *p = x + (int64_t)rb * ldx + cbase;
         if (col_ok && full) {
 #pragma unroll
@@ -814,8 +888,8 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int r = rb + i;
-                d[i] = (col_ok && r >= lo && r < hi) ? ld16(p + (int64_t)i * ldx)
-                                                      : make_uint4(0u, 0u, 0u, 0u);
+                d[i] = (col_ok && r >= clo && r < chi) ? ld16(p + (int64_t)i * ldx)
+                                                        : make_uint4(0u, 0u, 0u, 0u);
             }
         }
     };
@@ -832,7 +906,7 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
         if (!col_ok)
             return;
         const int rb = rbeg + it * TROWS + w * WROWS + 16 * qd;
-        const bool full = rb >= lo && rb + 16 <= hi;
+        const bool full = rb >= clo && rb + 16 <= chi;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             uint4 o;
@@ -852,7 +926,7 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int r = rb + i;
-                    if (r >= lo && r < hi)
+                    if (r >= clo && r < chi)
                         p[i] = (uint8_t)(ow[i >> 2] >> (8 * (i & 3)));
                 }
             }
@@ -864,15 +938,17 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
 #pragma unroll
     for (int tt = 0; tt < T; ++tt)
         if (tt < nit)
-            load_tile(v[tt], tt, tt == T - 1 && nit > T);
+            load_tile(v[tt], tt, !SPLIT && tt == T - 1 && nit > T);
 #pragma unroll
     for (int tt = 0; tt < T; ++tt)
         if (tt < nit)
             accumulate(mx, v[tt]);
-    // tiles beyond the register window stream through the last buffer
-    for (int it = T; it < nit; ++it) {
-        load_tile(v[T - 1], it, true);
-        accumulate(mx, v[T - 1]);
+    if constexpr (!SPLIT) {
+        // tiles beyond the register window stream through the last buffer
+        for (int it = T; it < nit; ++it) {
+            load_tile(v[T - 1], it, true);
+            accumulate(mx, v[T - 1]);
+        }
     }
 
 #pragma unroll
@@ -886,15 +962,86 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
         }
     }
     __syncthreads();
+    uint32_t acol = 0u;   // column t's maximum (t < SW)
     if (t < SW) {
-        uint32_t a = 0u;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww)
-            a = umax(a, s_red[ww][t]);
-        const float s = fp32_scale(a);
+            acol = umax(acol, s_red[ww][t]);
+    }
+    if constexpr (SPLIT) {
+        if (nc > 1) {
+            // Every global access of the exchange hands its result to LDS
+            // before the next barrier: a barrier does not wait for a
+            // thread's outstanding global operations, only the use of their
+            // results does, so this is what orders one thread's atomics
+            // before another thread's arrival or departure.
+            __shared__ int s_flag;
+            __shared__ uint32_t s_col[SW];
+            uint32_t *const set = ws + ((int64_t)s_sel[3] * nsuper + strip) * kSetWords;
+            if (t < SW)
+                s_col[t] = umax(acol, __hip_atomic_fetch_max(set + t, acol, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT));
+            __syncthreads();   // all of this workgroup's maxima are in
+            if (t == 0) {
+                __hip_atomic_fetch_add(set + kSetArrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                // a negative limit takes the fallback without looking
+                int n = 0;
+                bool all = false;
+                while (spin_limit >= 0 &&
+                       !(all = __hip_atomic_load(set + kSetArrive, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)nc) &&
+                       n < spin_limit) {
+                    __builtin_amdgcn_s_sleep(2);
+                    ++n;
+                }
+                s_flag = all ? 1 : 0;
+            }
+            __syncthreads();
+            if (s_flag) {
+                if (t < SW)
+                    s_col[t] = __hip_atomic_load(set + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                // the other chunks did not arrive in time: reduce every row of
+                // the group in this strip here (8 lanes per row, 16 bytes each)
+                if (t < SW)
+                    s_col[t] = 0u;
+                __syncthreads();
+                uint32_t m[4] = {0u, 0u, 0u, 0u};
+                const int pc = t & 7;
+                const int c0 = strip * SW + 8 * pc;
+                if (c0 < cols) {
+                    for (int r = lo + (t >> 3); r < hi; r += NTH / 8) {
+                        const uint4 vv = ld16(x + (int64_t)r * ldx + c0);
+                        m[0] = absmax2(m[0], vv.x);
+                        m[1] = absmax2(m[1], vv.y);
+                        m[2] = absmax2(m[2], vv.z);
+                        m[3] = absmax2(m[3], vv.w);
+                    }
+                }
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    atomicMax(&s_col[8 * pc + 2 * d], m[d] & 0xffffu);
+                    atomicMax(&s_col[8 * pc + 2 * d + 1], m[d] >> 16);
+                }
+            }
+            __syncthreads();   // every read of the set has returned
+            if (t == 0) {
+                const uint32_t prev = __hip_atomic_fetch_add(set + kSetDepart, 1u, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT);
+                s_flag = prev == (uint32_t)nc - 1 ? 2 : 0;
+            }
+            __syncthreads();
+            if (s_flag == 2 && t < kSetWords)
+                __hip_atomic_store(set + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (t < SW)
+                acol = s_col[t];
+        }
+    }
+    if (t < SW) {
+        const float s = fp32_scale(acol);
         s_scale[t] = s;
-        const int c = sm.strip * SW + t;
-        if (c < cols)
+        const int c = strip * SW + t;
+        if (c < cols && k == 0)
             scales[(int64_t)g * ss_g + (int64_t)c * ss_c] = s;
     }
     __syncthreads();
@@ -909,14 +1056,19 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
     for (int tt = 0; tt < T - 1; ++tt)
         if (tt < nit)
             store_tile(v[tt], tt, sc);
-    // the last buffer holds tile nit-1 (or T-1); walk the streamed tiles
-    // backwards so the most recently read ones are re-read first
-    for (int it = (nit > T ? nit : T) - 1; it >= T - 1; --it) {
-        if (it >= nit)
-            continue;
-        if (it != nit - 1)
-            load_tile(v[T - 1], it, true);
-        store_tile(v[T - 1], it, sc);
+    if constexpr (SPLIT) {
+        if (T - 1 < nit)
+            store_tile(v[T - 1], T - 1, sc);
+    } else {
+        // the last buffer holds tile nit-1 (or T-1); walk the streamed tiles
+        // backwards so the most recently read ones are re-read first
+        for (int it = (nit > T ? nit : T) - 1; it >= T - 1; --it) {
+            if (it >= nit)
+                continue;
+            if (it != nit - 1)
+                load_tile(v[T - 1], it, true);
+            store_tile(v[T - 1], it, sc);
+        }
     }
 }
 

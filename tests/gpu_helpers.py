@@ -237,3 +237,31 @@ def relayout(scales_dev, offs, extent, stream=None):
     assert code == 0, mxq._capi.status_string(code)
     st.synchronize()
     return tiles.cpu().numpy()[:cap], starts.cpu().numpy()
+
+
+def colwise_workspace(rows: int, cols: int, G: int) -> torch.Tensor:
+    """A zero-filled workspace for the colwise call with a workspace."""
+    n = mxq.mxq_jagged_colwise_workspace_bytes(rows, cols, G)
+    assert n >= 0
+    return torch.zeros(max(n, 4) // 4, dtype=torch.int32, device=DEV)
+
+
+def jagged_colwise_ws(x: torch.Tensor, offs: torch.Tensor, ws: torch.Tensor, spin=None, stream=None,
+                      expect=0, ws_bytes=None):
+    """The colwise call with a workspace (``spin``: the test-only entry with
+    that wait bound); column-major q (column stride padded), scales (G, cols)."""
+    rows, cols = x.shape
+    G = offs.numel()
+    ldq = round16(max(rows, 1))
+    q = u8_canary(cols * ldq)
+    s = f32_canary(G * cols)
+    nbytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    args = (x.data_ptr(), rows, cols, x.stride(0), x.stride(1), offs.data_ptr(), G, q.data_ptr(), 1,
+            ldq, s.data_ptr(), cols, 1, ws.data_ptr(), nbytes)
+    if spin is None:
+        code = mxq.mxq_quantize_jagged_colwise_ws(*args, stream_handle(stream))
+    else:
+        code = mxq.mxq_debug_jagged_colwise_ws_spin(*args, spin, stream_handle(stream))
+    assert code == expect, code
+    torch.cuda.synchronize()
+    return _gather_u8(q, (rows, cols), (1, ldq)), _gather_f32(s, (G, cols), (cols, 1))

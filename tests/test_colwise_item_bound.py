@@ -2,7 +2,11 @@
 column strip (long groups, and packs of up to 16 consecutive short groups
 whose starts fall in one 1024-row block) must never exceed the bound the
 library sizes its grid with, min(G, ext // 1010 + ext // 1024 + G // 16 + 1),
-for any non-decreasing offsets.  Items are counted here the way the kernel
+for any non-decreasing offsets.  With a workspace (split mode) a long group
+of span n rows from its 16-row-aligned start makes ceil(n / 1536) items, and
+the bound (with 512-row tiles, 4-wave workgroups) grows by
+(ext + 15 * min(G, ext // 498)) // 1536; the workspace
+holds one set per item number.  Items are counted here the way the kernel
 forms them; a bound that fell short would leave items without a workgroup
 (their bytes and scales unwritten)."""
 import numpy as np
@@ -12,32 +16,78 @@ TROWS = 1024
 PACK = 16
 
 
-def count_items(offs, ext):
-    """Long groups plus packs, by the kernel's rules."""
+SPLIT_TROWS = 512             # 4-wave workgroups with a workspace
+CHUNK = 3 * SPLIT_TROWS
+
+
+def count_items(offs, ext, split=False):
+    """Long groups (their chunks in split mode) plus packs, by the kernel's
+    rules."""
     G = len(offs)
+    tr = SPLIT_TROWS if split else TROWS
     ends = np.clip(np.asarray(offs, dtype=np.int64), 0, ext)
     los = np.concatenate([[0], ends[:-1]])
-    lng = (ends > los) & (ends - (los & ~15) > TROWS)
-    items = int(lng.sum())
+    lng = (ends > los) & (ends - (los & ~15) > tr)
+    if split:
+        span = ends - (los & ~15)
+        items = int(np.where(lng, (span + CHUNK - 1) // CHUNK, 0).sum())
+    else:
+        items = int(lng.sum())
     run = -1
     for g in range(G):
-        if g == 0 or lng[g] or lng[g - 1] or los[g] // TROWS != los[g - 1] // TROWS:
+        if g == 0 or lng[g] or lng[g - 1] or los[g] // tr != los[g - 1] // tr:
             run = g
         if not lng[g] and (g - run) % PACK == 0:
             items += 1
     return items
 
 
-def bound(ext, G):
-    return min(G, ext // (TROWS - 14) + ext // TROWS + G // PACK + 1)
+def bound(ext, G, split=False):
+    tr = SPLIT_TROWS if split else TROWS
+    b = min(G, ext // (tr - 14) + ext // tr + G // PACK + 1)
+    if split:
+        b += (ext + 15 * min(G, ext // (tr - 14))) // CHUNK
+    return b
+
+
+def check(offs, ext):
+    G = len(offs)
+    assert count_items(offs, ext) <= bound(ext, G)
+    assert count_items(offs, ext, True) <= bound(ext, G, True)
+
+
+def test_split_chunks_fit_their_rows():
+    """Every chunk of a long group holds at most CHUNK rows and the chunks
+    cover the group: csz = round16(ceil(span / nc)), nc = ceil(span / CHUNK);
+    the last chunk holds rows while nc < CHUNK / 16 (spans up to 96 chunks;
+    a longer group's empty last chunk still takes part in the exchange)."""
+    for span in list(range(SPLIT_TROWS + 1, 4 * CHUNK + 40)) + [16383, 16384, 100000, 196607]:
+        nc = -(-span // CHUNK)
+        csz = (-(-span // nc) + 15) // 16 * 16
+        assert csz <= CHUNK and nc * csz >= span
+        assert (nc - 1) * csz < span          # the last chunk holds rows
+
+
+def test_library_agrees_on_the_workspace_size():
+    from mxfp8_quantization_moe_amd import _capi
+    try:
+        lib = _capi.load()
+    except _capi.LibraryMissing:
+        pytest.skip("library not built")
+    for ext, cols, G in ((16384, 4096, 8), (1000, 64, 1), (65536, 8, 4096), (0, 8, 3)):
+        nstrips = -(-cols // 64)
+        want = bound(ext, G, True) * nstrips * 72 * 4
+        assert lib.mxq_jagged_colwise_workspace_bytes(ext, cols, G) == want
+    assert lib.mxq_jagged_colwise_workspace_bytes(-1, 8, 1) == -1
+    assert lib.mxq_jagged_colwise_workspace_bytes(8, 8, 0) == -1
 
 
 def test_moe_and_uniform_cases():
     import workloads
-    assert count_items(workloads.moe_offsets(), 16384) <= bound(16384, 8)
+    check(workloads.moe_offsets(), 16384)
     for G in (1, 8, 32, 64, 128, 4096):
         offs = (np.arange(1, G + 1) * (16384 // G)).astype(np.int64)
-        assert count_items(offs, 16384) <= bound(16384, G)
+        check(offs, 16384)
 
 
 @pytest.mark.parametrize("seed", range(40))
@@ -50,7 +100,7 @@ def test_random_offsets(seed):
     cuts = np.sort(g.integers(0, ext // mult + 1, size=G)) * mult
     cuts[-1] = ext if g.random() < 0.7 else cuts[-1]
     cuts = np.maximum.accumulate(cuts)
-    assert count_items(cuts, ext) <= bound(ext, G)
+    check(cuts, ext)
 
 
 def test_worst_cases():
@@ -63,12 +113,19 @@ def test_worst_cases():
             e += 1010
             ends += [min(ext, e + k) for k in range(1, 40)]
         ends = np.maximum.accumulate(np.array(ends or [ext], dtype=np.int64))
-        G = len(ends)
-        assert count_items(ends, ext) <= bound(ext, G)
+        check(ends, ext)
     # one short group starting in every block, and runs of exactly 16 + 1
     for ext in (4096, 65536):
         ends = np.arange(1, ext // TROWS + 1) * TROWS - 1
-        assert count_items(ends, ext) <= bound(ext, len(ends))
+        check(ends, ext)
         ends = np.repeat(np.arange(0, ext, 512), 17)[: 4096]
         ends = np.maximum.accumulate(ends)
-        assert count_items(ends, ext) <= bound(ext, len(ends))
+        check(ends, ext)
+    # long groups whose spans each just exceed a chunk multiple, from a
+    # start at 15 mod 16 (the most chunks per row)
+    for ext in (20000, 100000):
+        for L in (499, 513, 1010, 1537, 3073, 6145, 9217):
+            ends = np.arange(15 + L, ext + 1, L, dtype=np.int64)
+            if ends.size == 0:
+                continue
+            check(ends, ext)
