@@ -51,6 +51,8 @@ extern "C" {
 
 #define MXQ_ABI_VERSION 1
 #define MXQ_MAX_GROUPS 4096
+/* size of the device array behind mxq_quantize_jagged_colwise_noalloc */
+#define MXQ_NOALLOC_SCRATCH_BYTES (4 << 20)
 
 typedef enum mxq_status {
     MXQ_OK = 0,
@@ -156,6 +158,27 @@ mxq_status mxq_quantize_jagged_colwise_ws(const uint16_t *x, int64_t rows, int64
 /* Workspace bytes mxq_quantize_jagged_colwise_ws needs for these extents (a
  * bound that holds for any offsets); -1 for invalid arguments. */
 int64_t mxq_jagged_colwise_workspace_bytes(int64_t rows, int64_t cols, int32_t num_groups);
+
+/*
+ * Jagged COLWISE quantization that allocates nothing, for callers that
+ * cannot allocate device memory or call hipMalloc (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * operation, arguments and results of mxq_quantize_jagged_colwise_ws, with
+ * the workspace taken from a fixed device array inside the library (one per
+ * GPU, MXQ_NOALLOC_SCRATCH_BYTES = 4 MiB, held until the process ends; zero
+ * at load, and every call leaves it zero).  Extents whose
+ * workspace (mxq_jagged_colwise_workspace_bytes) exceeds it ->
+ * MXQ_ERR_WORKSPACE before any launch (e.g. 16384 x 4096 with 8 groups needs
+ * 331,776 bytes).  Calls on one GPU share the array: calls that overlap in
+ * time on one GPU race and must be serialized (e.g. issued on one stream).
+ * The array's device address is looked up on the first call on each device
+ * (MXQ_ERR_LAUNCH if that fails).
+ */
+mxq_status mxq_quantize_jagged_colwise_noalloc(const uint16_t *x, int64_t rows, int64_t cols,
+                                               int64_t sx_r, int64_t sx_c, const int32_t *offs,
+                                               int32_t num_groups, uint8_t *q, int64_t sq_r,
+                                               int64_t sq_c, float *scales, int64_t ss_g,
+                                               int64_t ss_c, void *stream);
 
 /*
  * MXFP8 quantization of 3D expert weights along N ("colwise", 32 x 1 blocks).

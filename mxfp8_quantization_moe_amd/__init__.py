@@ -18,6 +18,7 @@ from . import _capi
 from ._capi import (MXQ_ERR_INVALID_ARG, MXQ_ERR_LAUNCH, MXQ_ERR_UNSUPPORTED, MXQ_ERR_WORKSPACE,
                     MXQ_MAX_GROUPS, mxq_debug_jagged_colwise_ws_spin,
                     mxq_jagged_colwise_workspace_bytes, mxq_quantize_jagged_colwise_ws,
+                    mxq_quantize_jagged_colwise_noalloc, MXQ_NOALLOC_SCRATCH_BYTES,
                     MXQ_OK, MXQ_SCALE_FLOOR, MXQ_SCALE_RCEIL, LibraryMissing,
                     mxq_abi_version, mxq_debug_cast4_e4m3, mxq_debug_cast_e4m3,
                     mxq_quantize_blockwise,
@@ -36,7 +37,7 @@ __all__ = [
     "mxq_relayout_mx_scales_grouped", "mxq_quantize_blockwise", "mxq_debug_cast_e4m3",
     "mxq_debug_cast4_e4m3", "debug_cast4_e4m3", "jagged_colwise_workspace",
     "mxq_quantize_jagged_colwise_ws", "mxq_jagged_colwise_workspace_bytes",
-    "mxq_debug_jagged_colwise_ws_spin",
+    "mxq_debug_jagged_colwise_ws_spin", "mxq_quantize_jagged_colwise_noalloc",
     "mxq_abi_version", "LibraryMissing",
 ]
 

@@ -22,6 +22,7 @@ MXQ_ERR_WORKSPACE = 4
 MXQ_SCALE_FLOOR = 0
 MXQ_SCALE_RCEIL = 1
 MXQ_MAX_GROUPS = 4096
+MXQ_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -50,6 +51,8 @@ SIGNATURES = {
     "mxq_quantize_jagged_colwise_ws": [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _i64, _i64,
                                        _vp, _i64, _i64, _vp, _i64, _vp],
     "mxq_jagged_colwise_workspace_bytes": [_i64, _i64, _i32],
+    "mxq_quantize_jagged_colwise_noalloc": [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _i64,
+                                            _i64, _vp, _i64, _i64, _vp],
     "mxq_debug_jagged_colwise_ws_spin": [_vp, _i64, _i64, _i64, _i64, _vp, _i32, _vp, _i64, _i64,
                                          _vp, _i64, _i64, _vp, _i64, _i32, _vp],
     "mxq_debug_cast_e4m3": [_vp, _i64, _vp, _vp],
@@ -107,5 +110,6 @@ mxq_quantize_blockwise = _fwd("mxq_quantize_blockwise")
 mxq_quantize_jagged_colwise_ws = _fwd("mxq_quantize_jagged_colwise_ws")
 mxq_jagged_colwise_workspace_bytes = _fwd("mxq_jagged_colwise_workspace_bytes")
 mxq_debug_jagged_colwise_ws_spin = _fwd("mxq_debug_jagged_colwise_ws_spin")
+mxq_quantize_jagged_colwise_noalloc = _fwd("mxq_quantize_jagged_colwise_noalloc")
 mxq_debug_cast_e4m3 = _fwd("mxq_debug_cast_e4m3")
 mxq_debug_cast4_e4m3 = _fwd("mxq_debug_cast4_e4m3")

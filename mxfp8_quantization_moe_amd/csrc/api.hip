@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <utility>
 
 #include "mxq.h"
@@ -247,6 +248,59 @@ mxq_status run_jagged_mx_cols(const uint16_t *x, int64_t rows, int64_t cols, int
     return launch_status();
 }
 
+// The colwise call that allocates nothing keeps its exchange sets in this
+// file-scope device array (one copy per GPU, held until the process ends).
+// In host code its name is a host-side stand-in: kernels get the device
+// address, looked up once per device with that device current.
+constexpr int64_t kScratchBytes = MXQ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint32_t scratch[kScratchBytes / sizeof(uint32_t)];
+
+// device that runs `st` (the calling thread's current device for the null
+// stream), or -1
+int stream_device(hipStream_t st)
+{
+    int dev = -1;
+    if (st) {
+        hipDevice_t d = 0;
+        if (hipStreamGetDevice(st, &d) != hipSuccess)
+            return -1;
+        dev = (int)d;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return -1;
+    }
+    return dev;
+}
+
+// device address of `scratch` on device dev (nullptr on failure)
+uint32_t *scratch_on(int dev)
+{
+    static std::atomic<uint32_t *> addr[64];
+    static std::mutex init;
+    if (dev < 0 || dev >= 64)
+        return nullptr;
+    uint32_t *p = addr[dev].load(std::memory_order_acquire);
+    if (p)
+        return p;
+    std::lock_guard<std::mutex> lock(init);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (p)
+        return p;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess)
+        return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess)
+        return nullptr;
+    void *sym = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&sym, HIP_SYMBOL(scratch));
+    if (cur != dev)
+        (void)hipSetDevice(cur);
+    if (e != hipSuccess || !sym)
+        return nullptr;
+    p = static_cast<uint32_t *>(sym);
+    addr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
 template <int LAYOUT, int SEG, bool XCD>
 mxq_status run_relayout(const uint8_t *scales, int64_t rows, int64_t ss_r, int64_t ss_b,
                         const int32_t *offs, int G, int64_t extent, uint8_t *tiles,
@@ -340,6 +394,33 @@ mxq_status mxq_quantize_jagged_colwise(const uint16_t *x, int64_t rows, int64_t 
         return run_jagged_contig(x, cols, rows, sx_c, offs, num_groups, q, sq_c, scales, ss_c, ss_g, st);
     }
     return MXQ_ERR_UNSUPPORTED;
+}
+
+mxq_status mxq_quantize_jagged_colwise_noalloc(const uint16_t *x, int64_t rows, int64_t cols,
+                                               int64_t sx_r, int64_t sx_c, const int32_t *offs,
+                                               int32_t num_groups, uint8_t *q, int64_t sq_r,
+                                               int64_t sq_c, float *scales, int64_t ss_g,
+                                               int64_t ss_c, void *stream)
+{
+    mxq_status s = check_jagged_common(x, rows, cols, offs, num_groups, q, scales);
+    if (s != MXQ_OK)
+        return s;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (cols == 0)
+        return MXQ_OK;
+    if (sx_c == 1 && sq_r == 1) {
+        if (sx_r % 8 != 0 || sq_c % 16 != 0)
+            return MXQ_ERR_INVALID_ARG;
+        if (colwise_plan(rows, cols, num_groups, true).ws_bytes > kScratchBytes)
+            return MXQ_ERR_WORKSPACE;
+        uint32_t *ws = scratch_on(stream_device(st));
+        if (!ws)
+            return MXQ_ERR_LAUNCH;
+        return run_jagged_strided(x, rows, cols, sx_r, offs, num_groups, q, sq_c, scales, ss_g, ss_c,
+                                  st, ws, kScratchBytes);
+    }
+    return mxq_quantize_jagged_colwise(x, rows, cols, sx_r, sx_c, offs, num_groups, q, sq_r, sq_c,
+                                       scales, ss_g, ss_c, stream);
 }
 
 int64_t mxq_jagged_colwise_workspace_bytes(int64_t rows, int64_t cols, int32_t num_groups)
