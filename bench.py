@@ -11,7 +11,9 @@ Other workloads (``--workload``): ``moe_bwd`` (jagged rowwise quantization
 of grad_out^T (4096, 16384) plus jagged colwise of x (16384, 4096), 8 token
 groups, fp32 scales), ``moe_bwd_mx`` (the same operands as jagged MXFP8),
 ``mx3d`` (E = 8, N(0, 0.02)), ``mx3d_e{1,2,4,16,64}`` (the E sweep),
-``mx3d_rceil``, ``blockwise`` (1 x 128 activations (8192, 4096) + 128 x 128
+``mx3d_rceil``, ``rowwise_g64`` (the jagged rowwise operand with 64 groups of
+256 columns), ``moe_bwd_mx_unaligned`` (jagged MX rowwise with group starts off
+8-element boundaries), ``blockwise`` (1 x 128 activations (8192, 4096) + 128 x 128
 weights (4096, 4096)), ``blockwise_t`` (the transposed operands of the
 blockwise backward), ``relayout`` (per-group re-layout of (8192, 32768)
 e8m0 scales into scaled-MFMA tiles), ``copy`` (counter calibration).
@@ -233,6 +235,55 @@ def build_moe_bwd(torch, mxq, workloads, gen, ws=False):
     return [l1, l2], keep, desc, cpu_sample
 
 
+def build_rowwise_groups(torch, mxq, workloads, gen, G=64):
+    """Jagged rowwise quantization of grad_out^T (4096, 16384) with G equal
+    token groups (64 groups of 256 columns by default): the many-groups
+    kernel."""
+    import numpy as np
+
+    go_t = gen.one("moe_grad_out_t", "grad_out_t")
+    R, C = go_t.shape
+    offs = (np.arange(1, G + 1) * (C // G)).astype(np.int32)
+    d_go = bf16_dev(torch, go_t)
+    d_offs = torch.from_numpy(offs).cuda()
+    q = torch.empty(R * C, dtype=torch.uint8, device="cuda")
+    s = torch.empty(R * G, dtype=torch.float32, device="cuda")
+    l = Launch(f"jagged_rowwise grad_out^T (4096,16384), {G} groups", "jagged_contig_seg_kernel<8>",
+               mxq.mxq_quantize_jagged_rowwise,
+               (d_go.data_ptr(), R, C, C, 1, d_offs.data_ptr(), G, q.data_ptr(), C, 1, s.data_ptr(), G, 1),
+               3 * R * C + 4 * R * G, R * C, (("q", q), ("s", s)))
+    desc = {"workload": f"rowwise_g{G}", "tensors": "grad_out^T bf16 (4096,16384) rowwise -> row-major e4m3",
+            "groups": G, "group_sizes": [C // G] * G, "scales": "fp32 per (row, group)",
+            "seeds": {"go_vals": workloads.MOE_SEEDS["go_vals"]}}
+    return [l], [d_go, d_offs, q, s], desc, None
+
+
+def build_moe_bwd_mx_unaligned(torch, mxq, workloads, gen):
+    """Jagged MX rowwise on grad_out^T with the MoE groups moved off
+    8-element boundaries (ends 6016, 8947, 9189, 9189, 10113, 13671, 14322,
+    16384): blocks whose starts are not multiples of 8."""
+    import numpy as np
+
+    go_t = gen.one("moe_grad_out_t", "grad_out_t")
+    R, C = go_t.shape
+    offs = np.minimum(workloads.moe_offsets() + np.array([0, 3, 5, 5, 1, 7, 2, 0]), C).astype(np.int32)
+    G = offs.size
+    d_go = bf16_dev(torch, go_t)
+    d_offs = torch.from_numpy(offs).cuda()
+    nb1 = mxq.jagged_mx_scale_capacity(C, G)
+    nb = int(sum((n + 31) // 32 for n in _sizes(offs)))
+    q = torch.empty(R * C, dtype=torch.uint8, device="cuda")
+    s = torch.empty(R * nb1, dtype=torch.uint8, device="cuda")
+    l = Launch("jagged_mx_rowwise grad_out^T (4096,16384), starts off 8", "jagged_mx_rowwise_kernel<8>",
+               mxq.mxq_quantize_jagged_mx_rowwise,
+               (d_go.data_ptr(), R, C, C, 1, d_offs.data_ptr(), G, q.data_ptr(), C, 1, s.data_ptr(), nb1, 1, 0),
+               3 * R * C + R * nb, R * C, (("q", q),))
+    desc = {"workload": "moe_bwd_mx_unaligned", "tensors": "grad_out^T bf16 (4096,16384) 1x32 blocks per group",
+            "groups": int(G), "group_sizes": _sizes(offs), "scales": f"e8m0 floor, {nb} blocks per row",
+            "seeds": dict(workloads.MOE_SEEDS)}
+    return [l], [d_go, d_offs, q, s], desc, None
+
+
 def build_moe_bwd_mx(torch, mxq, workloads, gen):
     """The MX variant of the MoE backward grad_weight operands: jagged MXFP8
     (32-element blocks restarting at each token-group start, e8m0 floor
@@ -431,7 +482,8 @@ def build_copy(torch, mxq, workloads, gen):
 
 
 WORKLOADS = ("mx3d_e64", "mx3d_e1", "mx3d_e2", "mx3d_e4", "mx3d_e16", "mx3d", "mx3d_rceil",
-             "moe_bwd", "moe_bwd_ws", "moe_bwd_mx", "blockwise", "blockwise_t", "relayout", "copy")
+             "moe_bwd", "moe_bwd_ws", "moe_bwd_mx", "moe_bwd_mx_unaligned", "rowwise_g64", "blockwise",
+             "blockwise_t", "relayout", "copy")
 
 
 def build(name, torch, mxq, workloads, gen):
@@ -443,6 +495,10 @@ def build(name, torch, mxq, workloads, gen):
         return build_moe_bwd(torch, mxq, workloads, gen, ws=True)
     if name == "moe_bwd_mx":
         return build_moe_bwd_mx(torch, mxq, workloads, gen)
+    if name == "moe_bwd_mx_unaligned":
+        return build_moe_bwd_mx_unaligned(torch, mxq, workloads, gen)
+    if name.startswith("rowwise_g") and name[len("rowwise_g"):].isdigit():
+        return build_rowwise_groups(torch, mxq, workloads, gen, int(name[len("rowwise_g"):]))
     if name == "mx3d":
         return build_mx3d(torch, mxq, workloads, gen, 8, sweep=False)
     if name == "mx3d_rceil":

@@ -26,6 +26,11 @@ constexpr int kJaggedStridedWaves = 8;  // waves per workgroup: tile = 8*16*64/C
 // rows, chunks of 3 tiles (measured against 8 waves and 2 tiles)
 constexpr int kSplitTiles = 3;
 constexpr int kSplitWaves = 4;
+// the rowwise kernel folds segment maxima through LDS (one atomic per run of
+// a group per thread) above this many groups; at most this many it reduces
+// each 512-column wave slot with one wave maximum when the slot lies in one
+// group
+constexpr int kContigSegGroups = 16;
 // polls of a split colwise chunk waiting for the other chunks of its group
 // (each a device-scope load and a short sleep, about a microsecond) before
 // it reduces the group's rows itself
@@ -81,20 +86,32 @@ mxq_status run_jagged_contig(const uint16_t *x, int64_t nrows, int64_t ext, int6
         return MXQ_OK;
     if (nrows > INT32_MAX)
         return MXQ_ERR_INVALID_ARG;
-    const size_t lds = (size_t)3 * G * sizeof(uint32_t);
-    // persistent grid: a few workgroups per compute unit, each walking rows
-    const int64_t per_cu = 4;
+    // many groups: the segment-fold reduction (slots of 512 columns would
+    // otherwise hold several groups and take the general path)
+    const bool seg = G > kContigSegGroups;
+    // persistent grid: as many workgroups per compute unit as fit (four;
+    // three for the segment-fold kernel on long rows, whose 140 VGPRs allow
+    // three waves per SIMD), each walking rows
+    const int64_t per_cu = (seg && ext > 4096) ? 3 : 4;
     const int64_t nwg = std::min<int64_t>(nrows, per_cu * device_cu_count(st));
     const dim3 grid((unsigned)nwg), block(kThreads);
     const int rows = (int)nrows, cols = (int)ext;
     if (ext > 8 * kThreads * 8) {
-        jagged_contig_long_kernel<8><<<dim3((unsigned)nrows), block, lds, st>>>(
-            x, ldx, cols, offs, G, q, ldq, scales, ss_row, ss_g);
+        jagged_contig_long_kernel<8><<<dim3((unsigned)nrows), block, (size_t)3 * G * sizeof(uint32_t),
+                                       st>>>(x, ldx, cols, offs, G, q, ldq, scales, ss_row, ss_g);
         return launch_status();
     }
 #define MXQ_CONTIG(NR)                                                                             \
-    jagged_contig_kernel<NR><<<grid, block, lds, st>>>(x, ldx, rows, cols, offs, G, q, ldq, scales, \
-                                                       ss_row, ss_g)
+    do {                                                                                           \
+        const size_t lds = ((3 * (size_t)G + 3) & ~(size_t)3) * sizeof(uint32_t) +                \
+                           (seg ? 2 : 1) * (size_t)NR * kThreads * sizeof(uint32_t);               \
+        if (seg)                                                                                   \
+            jagged_contig_seg_kernel<NR><<<grid, block, lds, st>>>(x, ldx, rows, cols, offs, G, q,  \
+                                                                   ldq, scales, ss_row, ss_g);     \
+        else                                                                                       \
+            jagged_contig_kernel<NR><<<grid, block, lds, st>>>(x, ldx, rows, cols, offs, G, q, ldq, \
+                                                               scales, ss_row, ss_g);              \
+    } while (0)
     if (ext <= 2048)
         MXQ_CONTIG(1);
     else if (ext <= 4096)

@@ -76,14 +76,109 @@ __device__ __forceinline__ SegInfo seg_info(const int32_t *s_offs, int G, int g_
     return si;
 }
 
+// Element j of a segment that is not wholly inside one group: from the
+// segment's registers by a select of one 64-bit half and a shift (no
+// indexed register access, so nothing goes to scratch memory), except in a row's partial
+// last segment, which the loads return as zeros and which is read again
+// from memory.
+__device__ __forceinline__ uint32_t seg_elem(const uint16_t *xr, const uint4 &v, int e0, int j,
+                                             int cols)
+{
+    if (e0 + 8 > cols)
+        return (uint32_t)xr[e0 + j];
+    const uint64_t lo = ((uint64_t)v.y << 32) | v.x, hi = ((uint64_t)v.w << 32) | v.z;
+    return (uint32_t)((j < 4 ? lo : hi) >> (16 * (j & 3))) & 0xffffu;
+}
+
+// Reduce, element by element, a segment that is not wholly inside one group.
+__device__ __forceinline__ void reduce_segment_elementwise(uint32_t *s_amax, const int32_t *s_offs,
+                                                           int G, const uint16_t *xr, const uint4 &v,
+                                                           const SegInfo &si, int e0, int cols)
+{
+    int gj = si.g;
+#pragma unroll 1
+    for (int j = 0; j < 8 && e0 + j < cols; ++j) {
+        gj = advance_group(s_offs, G, gj, e0 + j);
+        if (gj < G)
+            atomicMax(&s_amax[gj], seg_elem(xr, v, e0, j, cols) & 0x7fffu);
+    }
+}
+
+// A segment with exactly one group boundary inside: elements [0, b) in its
+// own group g, [b, 8) in group g2 (or in no group when g2 == G), packed as
+// b | 8 | g2 << 4, worked out once per workgroup (the boundaries are the same
+// for every row); 0 for any other segment.
+__device__ __forceinline__ uint32_t segment_split(const int32_t *s_offs, int G, const SegInfo &si,
+                                                  int e0, int cols)
+{
+    if (!si.inb || si.fast || si.g >= G || e0 + 8 > cols)
+        return 0u;
+    const int b = s_offs[si.g] - e0;   // group g ends inside the segment
+    if (b <= 0 || b >= 8)
+        return 0u;
+    const int g2 = advance_group(s_offs, G, si.g + 1, e0 + b);
+    if (g2 < G && s_offs[g2] < e0 + 8)
+        return 0u;   // a second boundary inside: element by element
+    return (uint32_t)b | 8u | ((uint32_t)g2 << 4);
+}
+
+// the two maxima of a split segment (sp = segment_split(...) != 0), out of line
+__device__ __attribute__((noinline)) void reduce_split(uint32_t *s_amax, int G, uint4 v, int g1,
+                                                       uint32_t sp)
+{
+    const int b = (int)(sp & 7u), g2 = (int)(sp >> 4);
+    uint32_t m1 = 0u, m2 = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t a = elem8_bits(v, j) & 0x7fffu;
+        if (j < b)
+            m1 = a > m1 ? a : m1;
+        else
+            m2 = a > m2 ? a : m2;
+    }
+    if (m1 != 0u)
+        atomicMax(&s_amax[g1], m1);
+    if (g2 < G && m2 != 0u)
+        atomicMax(&s_amax[g2], m2);
+}
+
+// Scale and store a split segment: each element times its own group's
+// multiplier (every element is within its group's amax, so no clamp is
+// needed); 8 bytes at once unless the second part lies past the last group.
+// Out of line: the rare paths would otherwise take registers from the
+// kernels' common path.
+__device__ __attribute__((noinline)) void store_split(uint8_t *qr, const float *s_scale, int G,
+                                                      uint4 v, int g1, uint32_t sp, int e0)
+{
+    const int b = (int)(sp & 7u), g2 = (int)(sp >> 4);
+    const float s1 = s_scale[g1], s2 = g2 < G ? s_scale[g2] : 0.0f;
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        y[j] = elem8(v, j) * (j < b ? s1 : s2);
+    uint2 o;
+    o.x = cvt4_nosat(y[0], y[1], y[2], y[3]);
+    o.y = cvt4_nosat(y[4], y[5], y[6], y[7]);
+    if (g2 < G) {
+        st8_nt(qr + e0, o);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < b)
+                qr[e0 + j] = (uint8_t)((j < 4 ? o.x : o.y) >> (8 * (j & 3)));
+    }
+}
+
 // Reduce one segment's |x| max into s_amax for every group it touches.
 // `uni`: the caller knows every lane of the wave has a fast segment of the
 // same group gw (one wave max, one atomic); otherwise lanes are grouped by a
 // ballot loop (lanes hold consecutive segments, so few iterations), and the
-// segments that straddle a group boundary fall back to per-element atomics.
+// segments that straddle a group boundary take their split or per-element
+// atomics.
 __device__ __forceinline__ void reduce_segment(uint32_t *s_amax, const int32_t *s_offs, int G,
                                                const uint16_t *xr, const uint4 &v, const SegInfo &si,
-                                               int e0, int cols, bool uni, int gw_uni, int lane)
+                                               int e0, int cols, bool uni, int gw_uni, int lane,
+                                               uint32_t sp)
 {
     const uint32_t m = si.fast ? fold2(absmax_u4(v)) : 0u;
     if (uni) {
@@ -106,28 +201,25 @@ __device__ __forceinline__ void reduce_segment(uint32_t *s_amax, const int32_t *
             atomicMax(&s_amax[gw], wm);
         pending = pending && !mine;
     }
-    if (si.inb && !si.fast) {
-        // rare: re-read the elements one by one (the line is in cache) rather
-        // than index the segment's registers with a runtime element number
-        int gj = si.g;
-#pragma unroll 1
-        for (int j = 0; j < 8 && e0 + j < cols; ++j) {
-            gj = advance_group(s_offs, G, gj, e0 + j);
-            if (gj < G)
-                atomicMax(&s_amax[gj], (uint32_t)xr[e0 + j] & 0x7fffu);
-        }
-    }
+    if (sp != 0u)
+        reduce_split(s_amax, G, v, si.g, sp);
+    else if (si.inb && !si.fast && si.g < G)
+        reduce_segment_elementwise(s_amax, s_offs, G, xr, v, si, e0, cols);
 }
 
 // Scale and store one segment (row-major q row qr).
 __device__ __forceinline__ void store_segment(uint8_t *qr, const float *s_scale, const int32_t *s_offs,
                                               int G, const uint16_t *xr, const uint4 &v,
-                                              const SegInfo &si, int e0, int cols)
+                                              const SegInfo &si, int e0, int cols, uint32_t sp)
 {
-    if (!si.inb)
+    if (!si.inb || si.g >= G)
         return;
     if (si.fast) {
         st8_nt(qr + e0, quant8_fp32scale(v, s_scale[si.g]));
+        return;
+    }
+    if (sp != 0u) {
+        store_split(qr, s_scale, G, v, si.g, sp, e0);
         return;
     }
     int gj = si.g;
@@ -135,7 +227,8 @@ __device__ __forceinline__ void store_segment(uint8_t *qr, const float *s_scale,
     for (int j = 0; j < 8 && e0 + j < cols; ++j) {
         gj = advance_group(s_offs, G, gj, e0 + j);
         if (gj < G)
-            qr[e0 + j] = (uint8_t)cvt1(__uint_as_float((uint32_t)xr[e0 + j] << 16) * s_scale[gj]);
+            qr[e0 + j] = (uint8_t)cvt1(__uint_as_float(seg_elem(xr, v, e0, j, cols) << 16) *
+                                       s_scale[gj]);
     }
 }
 
@@ -149,8 +242,19 @@ __device__ __forceinline__ void store_segment(uint8_t *qr, const float *s_scale,
 // (wave, segment-slot) pairs are uniform.  Two register buffers alternate:
 // the loads of the next row are in flight while the current row is reduced,
 // scaled and stored.
-template <int NR>
-__global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
+//
+// SEG (many groups, chosen on the host from G): the wave slots that hold
+// several groups would take the general reduction; instead every lane
+// writes its segment maxima to its wave's part of LDS, and lane l then
+// folds NR consecutive entries of its own wave (NR consecutive segments of
+// one slot, NR*8 columns) into runs of one group, with one LDS atomic per
+// run; a wave's LDS operations complete in order, so this needs no
+// workgroup barrier.  The group of each folded segment is worked out once
+// per workgroup.  Dynamic LDS: 3*G words, rounded up to 4, plus NR*256 words
+// of segment maxima (SEG) and NR*256 words of segment splits (segment_split,
+// for every lane's segments).
+template <int NR, bool SEG>
+__device__ __forceinline__ void jagged_contig_body(
     const uint16_t *__restrict__ x, int64_t ldx, int rows, int cols,
     const int32_t *__restrict__ offs, int G, uint8_t *__restrict__ q, int64_t ldq,
     float *__restrict__ scales, int64_t ss_r, int64_t ss_g)
@@ -159,6 +263,8 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
     int32_t *s_offs = reinterpret_cast<int32_t *>(smem);
     uint32_t *s_amax = smem + G;
     float *s_scale = reinterpret_cast<float *>(smem + 2 * G);
+    uint32_t *s_seg = smem + ((3 * G + 3) & ~3);   // SEG: NR*256 segment maxima in column order
+    uint32_t *s_split = s_seg + (SEG ? NR * kThreads : 0);   // NR*256 segment splits
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -210,6 +316,7 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
         for (int i = 0; i < NR; ++i) {
             const int e0 = 8 * (i * kThreads + t);
             si[i] = seg_info(s_offs, G, g, e0, cols);
+            s_split[i * kThreads + t] = segment_split(s_offs, G, si[i], e0, cols);
             g = si[i].g;
             gw[i] = __builtin_amdgcn_readfirstlane(si[i].g);
             const bool same = si[i].fast && si[i].g == gw[i];
@@ -219,10 +326,76 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
         }
     }
 
+    // SEG: groups of this thread's NR consecutive segments (G where a
+    // segment is not wholly inside one group: those are reduced element by
+    // element by the lane that loads them)
+    int sgv[SEG ? NR : 1];
+    auto sg = [&](int j) __attribute__((always_inline)) { return sgv[j]; };
+    // the folded entries NR*lane + j of this wave: slot (NR*lane + j) / 64,
+    // lane (NR*lane + j) % 64 of that slot, i.e. segment fold_seg + j
+    const int wv = t >> 6;
+    const int fold_seg = 256 * ((NR * lane) / 64) + 64 * wv + (NR * lane) % 64;
+    if constexpr (SEG) {
+        int g = advance_group(s_offs, G, 0, 8 * fold_seg);
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            const SegInfo sj = seg_info(s_offs, G, g, 8 * (fold_seg + j), cols);
+            g = sj.g;
+            sgv[j] = sj.fast ? sj.g : G;
+        }
+    }
+
     auto process_row = [&](uint4 (&cur)[NR], uint4 (&nxt)[NR], int r) __attribute__((always_inline)) {
         load_row(nxt, r + (int)gridDim.x);   // range 0 past the last row
         const uint16_t *xr = x + (int64_t)r * ldx;
-        if (uni == (1u << NR) - 1u) {
+        if constexpr (SEG) {
+            uint32_t *const wseg = s_seg + wv * (NR * 64);   // this wave's entries
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                wseg[i * 64 + lane] = si[i].fast ? fold2(absmax_u4(cur[i])) : 0u;
+                if (si[i].inb && !si[i].fast && si[i].g < G) {
+                    const uint32_t sp = s_split[i * kThreads + t];
+                    if (sp != 0u)
+                        reduce_split(s_amax, G, cur[i], si[i].g, sp);
+                    else
+                        reduce_segment_elementwise(s_amax, s_offs, G, xr, cur[i], si[i],
+                                                   8 * (i * kThreads + t), cols);
+                }
+            }
+            // this wave's writes are done before its reads (LDS operations of
+            // a wave complete in order; the wait and the memory clobber keep
+            // the compiler from moving the reads above the writes)
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+            __asm__ __volatile__("" ::: "memory");
+            uint32_t m[NR];
+            if constexpr (NR % 4 == 0) {
+#pragma unroll
+                for (int j = 0; j < NR; j += 4) {
+                    const uint4 w4 = *reinterpret_cast<const uint4 *>(wseg + NR * lane + j);
+                    m[j] = w4.x;
+                    m[j + 1] = w4.y;
+                    m[j + 2] = w4.z;
+                    m[j + 3] = w4.w;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NR; ++j)
+                    m[j] = wseg[NR * lane + j];
+            }
+            uint32_t acc = m[0];
+#pragma unroll
+            for (int j = 1; j < NR; ++j) {
+                if (sg(j) == sg(j - 1)) {
+                    acc = umax(acc, m[j]);
+                } else {
+                    if (acc != 0u && sg(j - 1) < G)
+                        atomicMax(&s_amax[sg(j - 1)], acc);
+                    acc = m[j];
+                }
+            }
+            if (acc != 0u && sg(NR - 1) < G)
+                atomicMax(&s_amax[sg(NR - 1)], acc);
+        } else if (uni == (1u << NR) - 1u) {
             // every slot uniform: all wave maxima first (independent chains),
             // then one lane merges consecutive slots of the same group and
             // issues one LDS atomic per run
@@ -252,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
 #pragma unroll
             for (int i = 0; i < NR; ++i)
                 reduce_segment(s_amax, s_offs, G, xr, cur[i], si[i], 8 * (i * kThreads + t), cols,
-                               (uni >> i) & 1u, gw[i], lane);
+                               (uni >> i) & 1u, gw[i], lane, si[i].fast ? 0u : s_split[i * kThreads + t]);
         }
         __syncthreads();
         // scales; s_amax is reset for the next row, whose atomics come after
@@ -276,7 +449,8 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
         } else {
 #pragma unroll
             for (int i = 0; i < NR; ++i)
-                store_segment(qr, s_scale, s_offs, G, xr, cur[i], si[i], 8 * (i * kThreads + t), cols);
+                store_segment(qr, s_scale, s_offs, G, xr, cur[i], si[i], 8 * (i * kThreads + t), cols,
+                              si[i].fast ? 0u : s_split[i * kThreads + t]);
         }
     };
 
@@ -288,6 +462,27 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_kernel(
         process_row(vb, va, row);
         row += gridDim.x;
     }
+}
+
+// The few-groups kernel is held to four waves per SIMD (the persistent grid
+// runs four workgroups per CU; 128 VGPRs, nothing spilled); the many-groups
+// kernel needs more registers and runs three workgroups per CU.
+template <int NR>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void jagged_contig_kernel(
+    const uint16_t *__restrict__ x, int64_t ldx, int rows, int cols,
+    const int32_t *__restrict__ offs, int G, uint8_t *__restrict__ q, int64_t ldq,
+    float *__restrict__ scales, int64_t ss_r, int64_t ss_g)
+{
+    jagged_contig_body<NR, false>(x, ldx, rows, cols, offs, G, q, ldq, scales, ss_r, ss_g);
+}
+
+template <int NR>
+__global__ __launch_bounds__(kThreads) void jagged_contig_seg_kernel(
+    const uint16_t *__restrict__ x, int64_t ldx, int rows, int cols,
+    const int32_t *__restrict__ offs, int G, uint8_t *__restrict__ q, int64_t ldq,
+    float *__restrict__ scales, int64_t ss_r, int64_t ss_g)
+{
+    jagged_contig_body<NR, true>(x, ldx, rows, cols, offs, G, q, ldq, scales, ss_r, ss_g);
 }
 
 // Rows longer than one register chunk (cols > 2048*NR): one workgroup per
@@ -338,7 +533,7 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_long_kernel(
             const int e0 = cbase + 8 * (i * kThreads + t);
             const SegInfo si = seg_info(s_offs, G, g, e0, cols);
             g = si.g;
-            reduce_segment(s_amax, s_offs, G, xr, v[i], si, e0, cols, false, 0, lane);
+            reduce_segment(s_amax, s_offs, G, xr, v[i], si, e0, cols, false, 0, lane, 0u);
         }
     }
     __syncthreads();
@@ -358,7 +553,7 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_long_kernel(
             const int e0 = cbase + 8 * (i * kThreads + t);
             const SegInfo si = seg_info(s_offs, G, g, e0, cols);
             g = si.g;
-            store_segment(qr, s_scale, s_offs, G, xr, v[i], si, e0, cols);
+            store_segment(qr, s_scale, s_offs, G, xr, v[i], si, e0, cols, 0u);
         }
     }
 }

@@ -13,7 +13,8 @@
 //
 //  * jagged_mx_rowwise_kernel — blocks along the unit-stride dim.  Four lanes
 //    share a block (8 elements each, one 16-byte load when the block starts
-//    on an 8-element boundary), a workgroup covers 64 block slots x RW rows,
+//    on an 8-element boundary, else the one or two aligned 16-byte chunks
+//    that cover the piece, shifted), a workgroup covers 64 block slots x RW rows,
 //    loads all RW rows before reducing, and reduces each block with a
 //    quad-lane DPP max.
 //  * jagged_mx_colwise_kernel — blocks across rows, output column-major.  A
@@ -35,6 +36,24 @@
 namespace mxq {
 
 constexpr int kJmxThreads = 256;
+
+// Elements sh .. sh + pn - 1 of the 16 bf16 values in lo (elements 0..7)
+// and hi (8..15), as an 8-element piece whose elements past pn are zero
+// (0 <= sh < 8, 1 <= pn <= 8): 64-bit funnel shifts and a mask, no indexed
+// register access.
+__device__ __forceinline__ uint4 shift_piece(const uint4 &lo, const uint4 &hi, int sh, int pn)
+{
+    const uint64_t q0 = ((uint64_t)lo.y << 32) | lo.x, q1 = ((uint64_t)lo.w << 32) | lo.z;
+    const uint64_t q2 = ((uint64_t)hi.y << 32) | hi.x, q3 = ((uint64_t)hi.w << 32) | hi.z;
+    const bool up = sh >= 4;
+    const uint64_t a = up ? q1 : q0, b = up ? q2 : q1, c = up ? q3 : q2;
+    const int s = 16 * (sh & 3);
+    uint64_t o0 = s ? (a >> s) | (b << (64 - s)) : a;
+    uint64_t o1 = s ? (b >> s) | (c << (64 - s)) : b;
+    o0 &= pn >= 4 ? ~0ull : (1ull << (16 * pn)) - 1;
+    o1 &= pn >= 8 ? ~0ull : pn > 4 ? (1ull << (16 * (pn - 4))) - 1 : 0ull;
+    return make_uint4((uint32_t)o0, (uint32_t)(o0 >> 32), (uint32_t)o1, (uint32_t)(o1 >> 32));
+}
 
 // x: (rows, cols), row r at x + r*ldx (ldx % 8 == 0), unit column stride;
 // groups along the columns.  q: row-major, ldq % 16 == 0.
@@ -81,6 +100,12 @@ __global__ __launch_bounds__(kJmxThreads) void jagged_mx_rowwise_kernel(
         pn = pn < 0 ? 0 : (pn > 8 ? 8 : pn);
     }
     const bool fast = pn == 8 && (p0 & 7) == 0;
+    // other pieces inside the row's whole 8-element chunks: the one or two
+    // aligned chunks that cover them, shifted into place (only a piece that
+    // reaches into a partial last chunk is read element by element)
+    const bool tail = pn > 0 && p0 + pn > (cols & ~7);
+    const bool shifted = pn > 0 && !fast && !tail;
+    const int a0 = p0 & ~7, sh = p0 & 7;
 
     uint4 v[RW];
 #pragma unroll
@@ -88,8 +113,22 @@ __global__ __launch_bounds__(kJmxThreads) void jagged_mx_rowwise_kernel(
         const int r = r0 + i;
         v[i] = (fast && r < rows) ? ld16_nt(x + (int64_t)r * ldx + p0) : make_uint4(0u, 0u, 0u, 0u);
     }
-    if (!fast && pn > 0) {
-        // a piece that is short or does not start on an 8-element boundary
+    if (shifted) {
+        // the piece is p0 + [0, pn) with sh = p0 - a0; a second chunk is
+        // needed when sh + pn > 8, and then lies before cols & ~7 as well
+#pragma unroll
+        for (int i = 0; i < RW; ++i) {
+            const int r = r0 + i;
+            if (r < rows) {
+                const uint16_t *xp = x + (int64_t)r * ldx + a0;
+                const uint4 lo = ld16(xp);
+                const uint4 hi = sh + pn > 8 ? ld16(xp + 8) : make_uint4(0u, 0u, 0u, 0u);
+                v[i] = shift_piece(lo, hi, sh, pn);
+            }
+        }
+    }
+    if (tail) {
+        // a piece that reaches into the row's partial last chunk
 #pragma unroll
         for (int i = 0; i < RW; ++i) {
             const int r = r0 + i;

@@ -51,6 +51,13 @@ def test_small_workloads():
     (3, 9000, 4096, 1, 0, 30),     # the most groups, most of them empty
     (1, 1, 2, 1, 0, 8),
     (7, 8, 3, 1, 1, 9),
+    (8, 16384, 17, 1, 0, 40),      # many groups off 8-column boundaries, full register window
+    (8, 16384, 64, 1, 0, 41),
+    (8, 16384, 64, 16, 3, 42),
+    (2000, 16384, 33, 8, 0, 43),   # more rows than workgroups: each walks several rows
+    (1500, 12000, 100, 1, 5, 44),
+    (4, 16384, 4096, 1, 0, 45),    # every 8-column segment in two groups
+    (16, 8192, 17, 1, 9, 46),
 ])
 def test_jagged_rowwise_ragged(rows, cols, G, mult, tail, seed):
     bits = adversarial((rows, cols), 100 + seed)
