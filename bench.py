@@ -209,7 +209,7 @@ def build_moe_bwd(torch, mxq, workloads, gen, ws=False):
         nws = mxq.mxq_jagged_colwise_workspace_bytes(R2, C2, G)
         d_ws = torch.zeros(max(nws, 4) // 4, dtype=torch.int32, device="cuda")
         keep.append(d_ws)
-        l2 = Launch("jagged_colwise (workspace) x (16384,4096)", "jagged_strided_kernel<8, 3, 8, true>",
+        l2 = Launch("jagged_colwise (workspace) x (16384,4096)", "jagged_strided_kernel<8, 3, 4, true>",
                     mxq.mxq_quantize_jagged_colwise_ws, cargs + (d_ws.data_ptr(), nws),
                     3 * R2 * C2 + 4 * G * C2, R2 * C2, (("q2", q2), ("s2", s2)))
     else:

@@ -105,6 +105,17 @@ __global__ __launch_bounds__(kBlockThreads) void block_contig_kernel(
 // Blocks (BR, BC): (32, 1) and (128, 1) down the rows of one column,
 // (128, 128), and (1, 128) along one row.
 // Grid: E * tiles_r * tiles_c, tile 128 rows x 256 columns.
+// Tile order (a permutation of the grid; any order gives the same output):
+// chunk == 0: column tile fastest, then row tile, then batch entry.
+// chunk > 0: the dispatcher hands workgroup ids to the 8 XCDs in turn (id
+// mod 8), so ids are renumbered for XCD x to take chunks x, x + 8, x + 16, ...
+// of `chunk` consecutive tiles, counted in column-pair order (the two column
+// tiles of a pair side by side, then down the rows, pair after pair; an odd
+// last column tile alone); a partial last round of 8 chunks keeps its ids.
+// Each XCD then sweeps a compact 512-column x (chunk/2 x 128)-row region: its
+// reads are 1 KB row pieces and its column-major writes run down whole
+// columns, which measured faster than the plain order on grids of many
+// residency rounds (the 64-expert weights) and no faster on small ones.
 // nt: nontemporal q stores, for a column-major launch whose 128-row column
 // runs start on 128-byte lines; with runs off the lines, plain stores let L2
 // merge the two parts of a line before it goes to HBM, where a partial
@@ -115,7 +126,7 @@ template <int BR, int BC, bool E8M0, bool QROW = false>
 __global__ __launch_bounds__(kBlockThreads) void block_strided_kernel(
     const uint16_t *__restrict__ x, int64_t sxe, int64_t ldx, int rows, int cols,
     uint8_t *__restrict__ q, int64_t sqe, int64_t ldq, void *__restrict__ scales, int64_t sse,
-    int64_t ss_rb, int64_t ss_cb, int tiles_r, int tiles_c, int rceil, int nt)
+    int64_t ss_rb, int64_t ss_cb, int tiles_r, int tiles_c, int rceil, int nt, int chunk)
 {
     static_assert((BC == 1 && (BR == 32 || BR == 128)) || (BC == 128 && (BR == 128 || BR == 1)),
                   "block shape");
@@ -131,10 +142,33 @@ __global__ __launch_bounds__(kBlockThreads) void block_strided_kernel(
     const int cg = lane & 7;
     const int qd = lane >> 3;
 
-    const int64_t bid = blockIdx.x;
-    const int tc = (int)(bid % tiles_c);
-    const int tr = (int)((bid / tiles_c) % tiles_r);
-    const int64_t e = bid / ((int64_t)tiles_c * tiles_r);
+    int tc, tr;
+    int64_t e;
+    if (chunk > 0) {
+        uint32_t bid = blockIdx.x;
+        const uint32_t ck = (uint32_t)chunk, span = 8u * ck, full = gridDim.x / span * span;
+        if (bid < full) {
+            const uint32_t l = bid >> 3;
+            bid = ((l / ck) * 8u + (bid & 7u)) * ck + l % ck;
+        }
+        const uint32_t per_e = (uint32_t)tiles_r * (uint32_t)tiles_c;
+        const uint32_t l = bid % per_e, pair_tiles = 2u * (uint32_t)tiles_r;
+        const uint32_t paired = (uint32_t)(tiles_c >> 1) * pair_tiles;
+        e = bid / per_e;
+        if (l < paired) {
+            const uint32_t m = l % pair_tiles;
+            tc = (int)(2u * (l / pair_tiles) + (m & 1u));
+            tr = (int)(m >> 1);
+        } else {
+            tc = tiles_c - 1;
+            tr = (int)(l - paired);
+        }
+    } else {
+        const int64_t bid = blockIdx.x;
+        tc = (int)(bid % tiles_c);
+        tr = (int)((bid / tiles_c) % tiles_r);
+        e = bid / ((int64_t)tiles_c * tiles_r);
+    }
 
     const int r0 = tr * 128 + 16 * qd;
     const int c0 = tc * 256 + 64 * w + 8 * cg;

@@ -31,6 +31,7 @@ SPLIT_AXIS = {
     "quantize_jagged_mx_colwise": 1,
     "quantize_mx_rowwise": 0,
     "quantize_blockwise": 0,
+    "quantize_mx_3d_colwise": 0,
 }
 
 _pool = None
@@ -103,7 +104,8 @@ def split_op(name: str, x: np.ndarray, *args, align: int = 1, parts: int = 0, ax
 def _positional(name: str):
     return {"quantize_jagged_rowwise": ("offs",), "quantize_jagged_colwise": ("offs",),
             "quantize_jagged_mx_rowwise": ("offs",), "quantize_jagged_mx_colwise": ("offs",),
-            "quantize_mx_rowwise": (), "quantize_blockwise": ("block_r", "block_c")}[name]
+            "quantize_mx_rowwise": (), "quantize_blockwise": ("block_r", "block_c"),
+            "quantize_mx_3d_colwise": ()}[name]
 
 
 def _mx3d_expert_job(e: int, sweep: bool, modes, keep_bits: bool, shape):

@@ -10,6 +10,7 @@ import torch
 
 import mxfp8_quantization_moe_amd as mxq
 import oracle
+import oracle_pool
 import workloads
 from gpu_helpers import (CANARY, adversarial, assert_same_bytes, bf16_dev, blockwise, i32_dev,
                          jagged_colwise, jagged_rowwise, mx_3d_colwise, mx_rowwise, random_offsets)
@@ -158,6 +159,24 @@ def test_mx_3d_colwise(E, N, K, seed, mode):
     oq, os_ = oracle.quantize_mx_3d_colwise(w, mode=mode)
     assert_same_bytes(q, oq, "mx 3d q")
     assert_same_bytes(s, os_, "mx 3d scales")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("E,N,K", [(2731, 160, 520), (8200, 32, 264)])
+def test_mx_3d_colwise_many_tiles(E, N, K):
+    """Grids of more than 16384 tiles, which the kernel walks in XCD chunks of
+    column-tile pairs: an odd last column tile (3 tiles of 256, 256 and 8
+    columns; 2 of 256 and 8), a ragged last row tile (160 = 128 + 32 rows)
+    or a single one (32 rows), and grids that are not a whole number of
+    8-chunk rounds (16386 and 16400 tiles), against the oracle on every
+    expert."""
+    w = workloads.normal_bf16((E, N, K), 11 + N)
+    w[0, 0:32, 3] = 0                                           # zero block
+    w[E - 1, N - 32:N, K - 1] = 0x8000                          # negative zeros, last column
+    q, s = mx_3d_colwise(bf16_dev(w))
+    oq, os_ = oracle_pool.split_op("quantize_mx_3d_colwise", w, align=1)
+    assert_same_bytes(q, oq, "mx 3d many tiles q")
+    assert_same_bytes(s, os_, "mx 3d many tiles scales")
 
 
 @pytest.mark.parametrize("mode", ["floor", "rceil"])

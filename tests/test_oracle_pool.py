@@ -46,6 +46,7 @@ def same(a, b):
     ("quantize_blockwise", (37, 256), (1, 128), 1),
     ("quantize_blockwise", (512, 256), (128, 128), 128),
     ("quantize_blockwise", (512, 40), (128, 1), 128),
+    ("quantize_mx_3d_colwise", (7, 64, 24), None, 1),
 ])
 def test_split_equals_whole(name, shape, extra, align):
     x = adversarial_bits(shape, 17)
