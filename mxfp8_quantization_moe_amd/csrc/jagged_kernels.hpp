@@ -122,9 +122,8 @@ __device__ __forceinline__ uint32_t segment_split(const int32_t *s_offs, int G, 
     return (uint32_t)b | 8u | ((uint32_t)g2 << 4);
 }
 
-// the two maxima of a split segment (sp = segment_split(...) != 0), out of line
-__device__ __attribute__((noinline)) void reduce_split(uint32_t *s_amax, int G, uint4 v, int g1,
-                                                       uint32_t sp)
+// the two maxima of a split segment (sp = segment_split(...) != 0)
+__device__ __forceinline__ void reduce_split_inl(uint32_t *s_amax, int G, uint4 v, int g1, uint32_t sp)
 {
     const int b = (int)(sp & 7u), g2 = (int)(sp >> 4);
     uint32_t m1 = 0u, m2 = 0u;
@@ -145,10 +144,8 @@ __device__ __attribute__((noinline)) void reduce_split(uint32_t *s_amax, int G, 
 // Scale and store a split segment: each element times its own group's
 // multiplier (every element is within its group's amax, so no clamp is
 // needed); 8 bytes at once unless the second part lies past the last group.
-// Out of line: the rare paths would otherwise take registers from the
-// kernels' common path.
-__device__ __attribute__((noinline)) void store_split(uint8_t *qr, const float *s_scale, int G,
-                                                      uint4 v, int g1, uint32_t sp, int e0)
+__device__ __forceinline__ void store_split_inl(uint8_t *qr, const float *s_scale, int G, uint4 v,
+                                                int g1, uint32_t sp, int e0)
 {
     const int b = (int)(sp & 7u), g2 = (int)(sp >> 4);
     const float s1 = s_scale[g1], s2 = g2 < G ? s_scale[g2] : 0.0f;
@@ -167,6 +164,22 @@ __device__ __attribute__((noinline)) void store_split(uint8_t *qr, const float *
             if (j < b)
                 qr[e0 + j] = (uint8_t)((j < 4 ? o.x : o.y) >> (8 * (j & 3)));
     }
+}
+
+// Out-of-line forms for the few-groups kernels, where inlined they would
+// take registers from the common path (128 VGPRs, four waves per SIMD) and
+// spill; a call costs the caller a wait for all its outstanding loads, which
+// the many-groups kernel, where split segments are common, cannot afford.
+__device__ __attribute__((noinline)) void reduce_split(uint32_t *s_amax, int G, uint4 v, int g1,
+                                                       uint32_t sp)
+{
+    reduce_split_inl(s_amax, G, v, g1, sp);
+}
+
+__device__ __attribute__((noinline)) void store_split(uint8_t *qr, const float *s_scale, int G,
+                                                      uint4 v, int g1, uint32_t sp, int e0)
+{
+    store_split_inl(qr, s_scale, G, v, g1, sp, e0);
 }
 
 // Reduce one segment's |x| max into s_amax for every group it touches.
@@ -207,7 +220,9 @@ __device__ __forceinline__ void reduce_segment(uint32_t *s_amax, const int32_t *
         reduce_segment_elementwise(s_amax, s_offs, G, xr, v, si, e0, cols);
 }
 
-// Scale and store one segment (row-major q row qr).
+// Scale and store one segment (row-major q row qr).  INL: split segments
+// inline (the many-groups kernel) rather than through a call.
+template <bool INL = false>
 __device__ __forceinline__ void store_segment(uint8_t *qr, const float *s_scale, const int32_t *s_offs,
                                               int G, const uint16_t *xr, const uint4 &v,
                                               const SegInfo &si, int e0, int cols, uint32_t sp)
@@ -219,7 +234,10 @@ __device__ __forceinline__ void store_segment(uint8_t *qr, const float *s_scale,
         return;
     }
     if (sp != 0u) {
-        store_split(qr, s_scale, G, v, si.g, sp, e0);
+        if constexpr (INL)
+            store_split_inl(qr, s_scale, G, v, si.g, sp, e0);
+        else
+            store_split(qr, s_scale, G, v, si.g, sp, e0);
         return;
     }
     int gj = si.g;
@@ -356,7 +374,7 @@ __device__ __forceinline__ void jagged_contig_body(
                 if (si[i].inb && !si[i].fast && si[i].g < G) {
                     const uint32_t sp = s_split[i * kThreads + t];
                     if (sp != 0u)
-                        reduce_split(s_amax, G, cur[i], si[i].g, sp);
+                        reduce_split_inl(s_amax, G, cur[i], si[i].g, sp);
                     else
                         reduce_segment_elementwise(s_amax, s_offs, G, xr, cur[i], si[i],
                                                    8 * (i * kThreads + t), cols);
@@ -449,8 +467,8 @@ __device__ __forceinline__ void jagged_contig_body(
         } else {
 #pragma unroll
             for (int i = 0; i < NR; ++i)
-                store_segment(qr, s_scale, s_offs, G, xr, cur[i], si[i], 8 * (i * kThreads + t), cols,
-                              si[i].fast ? 0u : s_split[i * kThreads + t]);
+                store_segment<SEG>(qr, s_scale, s_offs, G, xr, cur[i], si[i], 8 * (i * kThreads + t),
+                                   cols, si[i].fast ? 0u : s_split[i * kThreads + t]);
         }
     };
 
