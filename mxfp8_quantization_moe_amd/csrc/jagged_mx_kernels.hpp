@@ -16,7 +16,8 @@
 //    on an 8-element boundary, else the one or two aligned 16-byte chunks
 //    that cover the piece, shifted), a workgroup covers 64 block slots x RW rows,
 //    loads all RW rows before reducing, and reduces each block with a
-//    quad-lane DPP max.
+//    quad-lane DPP max.  Pieces off 8-byte boundaries are stored as aligned
+//    8-byte words shared with the neighbouring lane's piece.
 //  * jagged_mx_colwise_kernel — blocks across rows, output column-major.  A
 //    workgroup covers 128 rows of one group (starting at the group start)
 //    x 256 columns; a lane holds 16 rows x 8 columns, two lanes make a
@@ -53,6 +54,16 @@ __device__ __forceinline__ uint4 shift_piece(const uint4 &lo, const uint4 &hi, i
     o0 &= pn >= 4 ? ~0ull : (1ull << (16 * pn)) - 1;
     o1 &= pn >= 8 ? ~0ull : pn > 4 ? (1ull << (16 * (pn - 4))) - 1 : 0ull;
     return make_uint4((uint32_t)o0, (uint32_t)(o0 >> 32), (uint32_t)o1, (uint32_t)(o1 >> 32));
+}
+
+// Bytes [from, to) of w (byte k of w at base[k]), one byte store each: the
+// ends of a run of contiguous pieces.
+__device__ __forceinline__ void put_bytes(uint8_t *base, uint64_t w, int from, int to)
+{
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        if (k >= from && k < to)
+            base[k] = (uint8_t)(w >> (8 * k));
 }
 
 // x: (rows, cols), row r at x + r*ldx (ldx % 8 == 0), unit column stride;
@@ -106,25 +117,56 @@ __global__ __launch_bounds__(kJmxThreads) void jagged_mx_rowwise_kernel(
     const bool tail = pn > 0 && p0 + pn > (cols & ~7);
     const bool shifted = pn > 0 && !fast && !tail;
     const int a0 = p0 & ~7, sh = p0 & 7;
+    // Stores of pieces off 8-byte boundaries.  Within a group the pieces of
+    // consecutive lanes are contiguous, so a lane whose piece runs from
+    // a0 + sh into the next aligned word [a0 + 8, a0 + 16) writes that whole
+    // word, its last sh bytes followed by the next lane's first 8 - sh
+    // (`joined`), when the next lane's piece continues it far enough; the
+    // next lane then leaves its first word alone.  Bytes at the ends of such
+    // runs (group ends, the wave's last lane) go out one by one.
+    const int lane = t & 63;
+    const int p0n = (int)from_next_lane((uint32_t)p0), pnn = (int)from_next_lane((uint32_t)pn);
+    const bool joined = sh > 0 && pn == 8 && lane < 63 && p0n == p0 + 8 && pnn >= 8 - sh;
+    const bool prev_joined = __shfl_up(joined ? 1 : 0, 1, 64) != 0 && lane > 0;
 
+    // Loads: every fast or shifted lane reads the aligned chunk at a0 of
+    // each row.  A shifted piece that reaches past it (sh + pn > 8) needs the
+    // chunk at a0 + 8 too, which the next lane has read when its piece
+    // continues this one (its a0 is a0 + 8): taken from it by a lane
+    // shuffle, else (group ends, the wave's last lane) read here, issued with
+    // the first loads.  The second chunk lies before cols & ~7 as well.
+    const bool chunk = fast || shifted;
+    const bool chunk_next = from_next_lane(chunk ? 1u : 0u) != 0u;
+    const bool need_hi = shifted && sh + pn > 8;
+    const bool own_hi = need_hi && !(lane < 63 && chunk_next && (p0n & ~7) == a0 + 8);
+    // wave-uniform: waves with no shifted piece (or no joined store) skip
+    // the exchanges
+    const bool wave_shifted = __ballot(shifted) != 0;
+    const bool wave_joined = __ballot(joined) != 0;
     uint4 v[RW];
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
         const int r = r0 + i;
-        v[i] = (fast && r < rows) ? ld16_nt(x + (int64_t)r * ldx + p0) : make_uint4(0u, 0u, 0u, 0u);
+        v[i] = (chunk && r < rows) ? ld16_nt(x + (int64_t)r * ldx + a0) : make_uint4(0u, 0u, 0u, 0u);
     }
-    if (shifted) {
-        // the piece is p0 + [0, pn) with sh = p0 - a0; a second chunk is
-        // needed when sh + pn > 8, and then lies before cols & ~7 as well
+    if (wave_shifted) {
+        uint4 h[RW];
 #pragma unroll
         for (int i = 0; i < RW; ++i) {
             const int r = r0 + i;
-            if (r < rows) {
-                const uint16_t *xp = x + (int64_t)r * ldx + a0;
-                const uint4 lo = ld16(xp);
-                const uint4 hi = sh + pn > 8 ? ld16(xp + 8) : make_uint4(0u, 0u, 0u, 0u);
-                v[i] = shift_piece(lo, hi, sh, pn);
-            }
+            h[i] = (own_hi && r < rows) ? ld16_nt(x + (int64_t)r * ldx + a0 + 8) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < RW; ++i) {
+            uint4 hi;
+            hi.x = from_next_lane(v[i].x);
+            hi.y = from_next_lane(v[i].y);
+            hi.z = from_next_lane(v[i].z);
+            hi.w = from_next_lane(v[i].w);
+            if (own_hi)
+                hi = h[i];
+            if (shifted)
+                v[i] = shift_piece(v[i], hi, sh, pn);
         }
     }
     if (tail) {
@@ -150,19 +192,31 @@ __global__ __launch_bounds__(kJmxThreads) void jagged_mx_rowwise_kernel(
         const uint32_t m = group_max<4>(fold2(absmax_u4(v[i])));
         const uint32_t code = e8m0_code(m, rceil != 0);
         const float s = e8m0_multiplier(code);
+        const uint2 o = quant8(v[i], s);
+        uint64_t nxt = 0u;
+        if (wave_joined)
+            nxt = (uint64_t)from_next_lane(o.x) | ((uint64_t)from_next_lane(o.y) << 32);
         if (r >= rows || pn == 0)
             continue;
         if (l == 0)
             scales[(int64_t)r * ss_r + (int64_t)j * ss_b] = (uint8_t)code;
-        const uint2 o = quant8(v[i], s);
-        uint8_t *qp = q + (int64_t)r * ldq + p0;
+        uint8_t *qr = q + (int64_t)r * ldq;
         if (fast) {
-            st8_nt(qp, o);
+            st8_nt(qr + p0, o);
         } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (e < pn)
-                    qp[e] = (uint8_t)((e < 4 ? o.x : o.y) >> (8 * (e & 3)));
+            const uint64_t pw = (uint64_t)o.x | ((uint64_t)o.y << 32);
+            // the piece's bytes in the word at a0: positions sh .. sh + pn - 1, up to 7
+            if (!prev_joined)
+                put_bytes(qr + a0, pw << (8 * sh), sh, sh + pn < 8 ? sh + pn : 8);
+            // the rest, in the word at a0 + 8 (positions 0 .. sh + pn - 9; sh > 0 here)
+            if (sh + pn > 8) {
+                const uint64_t rest = pw >> (64 - 8 * sh);
+                if (joined) {
+                    const uint64_t wd = rest | (nxt << (8 * sh));
+                    st8(qr + a0 + 8, make_uint2((uint32_t)wd, (uint32_t)(wd >> 32)));
+                } else
+                    put_bytes(qr + a0 + 8, rest, 0, sh + pn - 8);
+            }
         }
     }
 }

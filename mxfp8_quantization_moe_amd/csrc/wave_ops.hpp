@@ -16,12 +16,17 @@ constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7 - i within each 8
 constexpr int kDppRowMirror = 0x140;    // lane i <-> 15 - i within each 16
+constexpr int kDppWaveShl1 = 0x130;     // lane i reads lane i + 1 (whole wave)
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t v)
 {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
+
+// the value of lane + 1 of the wave (VALU data movement, no LDS); lane 63
+// receives 0
+__device__ __forceinline__ uint32_t from_next_lane(uint32_t v) { return dpp<kDppWaveShl1>(v); }
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
