@@ -309,10 +309,19 @@ mxq_status mxq_relayout_mx_scales_grouped(const uint8_t *scales, int64_t rows, i
  *         cols % block_c == 0.
  * q       (rows, cols) e4m3, strides (sq_r, sq_c).
  * scales  (rows/block_r, cols/block_c) fp32, strides (ss_rb, ss_cb).
- * Blocks and layouts with a kernel:
- *   (1, 128)   sx_c == 1 && sq_c == 1   row-major in and out;
- *   (128, 128) sx_c == 1 && sq_r == 1   row-major in, column-major out;
- *   (128, 1)   sx_c == 1 && sq_r == 1   row-major in, column-major out.
+ * Blocks: (1, 128), (128, 128) or (128, 1); others -> MXQ_ERR_UNSUPPORTED.
+ * Layouts with a kernel, for every block shape:
+ *   x   row-major (sx_c == 1) or a transposed view of a row-major tensor
+ *       (sx_r == 1), read in place: the view is quantized as the underlying
+ *       tensor with the block shape, q strides and scale strides transposed;
+ *   q   row-major (sq_c == 1) or column-major (sq_r == 1).
+ * x and q 16-byte aligned, x's leading stride a multiple of 8 elements,
+ * scales 4-byte aligned.  In the terms of the underlying row-major tensor
+ * (R, C): 1 x 128 blocks into row-major q need q's row stride % 16 == 0;
+ * every other combination runs on 128 x 256 tiles and needs C % 8 == 0,
+ * R % 16 == 0 and q's leading stride % 8 == 0 (row-major) or % 16 == 0
+ * (column-major).  Other layouts -> MXQ_ERR_UNSUPPORTED, unmet alignments ->
+ * MXQ_ERR_INVALID_ARG.
  */
 mxq_status mxq_quantize_blockwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t sx_r,
                                   int64_t sx_c, int32_t block_r, int32_t block_c, uint8_t *q,

@@ -163,7 +163,8 @@ def quantize_jagged_colwise(x, offs, *, workspace=None, stream=None):
 def quantize_mx_3d_colwise(w, *, scale_mode: int = MXQ_SCALE_FLOOR, stream=None):
     """MXFP8 along N of expert weights ``w`` (E, N, K).  Returns ``(q,
     scales)``: q (E, N, K) with per-expert column-major strides (N*K, 1, N)
-    (K padded to 16 bytes if needed), scales (E, N/32, K) e8m0 uint8."""
+    (the column stride N rounded up to 16 bytes), scales (E, N/32, K) e8m0
+    uint8."""
     torch = _torch()
     _require_bf16_cuda(w, 3, "w")
     E, N, K = w.shape
