@@ -659,8 +659,10 @@ def output_sha256(torch, launches):
 
 def stream_ceiling(torch, dev, sh, np):
     """Practical HBM ceiling of the quantizers' traffic: the streaming probes
-    (tests/ceiling) on 2^31 bf16 elements (4 GiB read, 2 GiB written), median
-    of 5 launches each, and the runtime's 4 GiB device-to-device copy."""
+    (tests/ceiling: 2 reads : 1 write with nontemporal stores and with
+    nontemporal device-scope stores, read only, write only) on 2^31 bf16
+    elements (4 GiB read, 2 GiB written), median of 5 launches each, and the
+    runtime's 4 GiB device-to-device copy."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import ceiling
 
@@ -841,7 +843,11 @@ def main(argv=None):
     if not args.no_ceiling:
         print("[bench] streaming ceiling", file=sys.stderr, flush=True)
         ceiling = stream_ceiling(torch, dev, sh, np)
-        ceiling["frac_of_read2_write1"] = round(achieved / ceiling["read2_write1_GBps"], 4)
+        # the faster of the two 2:1 probes (nontemporal stores, or nontemporal
+        # at device scope) is the ceiling the kernel is held to
+        best = max(ceiling["read2_write1_GBps"], ceiling["read2_write1_device_scope_GBps"])
+        ceiling["read2_write1_best_GBps"] = best
+        ceiling["frac_of_read2_write1"] = round(achieved / best, 4)
         ceiling["frac_of_d2d_copy"] = round(achieved / ceiling["d2d_copy_GBps"], 4)
 
     cpu = None

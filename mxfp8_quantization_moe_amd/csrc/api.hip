@@ -53,6 +53,16 @@ int line_aligned(const void *q, int64_t ldq, int64_t sqe)
     return ((reinterpret_cast<uintptr_t>(q) & 127u) == 0 && ldq % 128 == 0 && sqe % 128 == 0) ? 1 : 0;
 }
 
+// q stores of the MX 3D kernel: nontemporal at device scope when q is on
+// 128-byte lines and every offset inside one expert fits in 32 bits (the
+// last column's run ends at (K - 1) * ldq + N), else as line_aligned says
+int mx3d_store_mode(const void *q, int64_t N, int64_t K, int64_t ldq, int64_t sqe)
+{
+    if (!line_aligned(q, ldq, sqe))
+        return 0;
+    return (K - 1) * ldq + N <= (int64_t)UINT32_MAX ? 2 : 1;
+}
+
 mxq_status launch_status()
 {
     hipError_t e = hipGetLastError();
@@ -510,7 +520,7 @@ mxq_status mxq_quantize_mx_3d_colwise(const uint16_t *w, int64_t E, int64_t N, i
     block_strided_kernel<32, 1, true><<<dim3((unsigned)nblocks), dim3(kBlockThreads), 0,
                                          reinterpret_cast<hipStream_t>(stream)>>>(
         w, sw_e, sw_n, (int)N, (int)K, q, sq_e, sq_k, scales, ss_e, ss_nb, ss_k, (int)tiles_r,
-        (int)tiles_c, scale_mode == MXQ_SCALE_RCEIL, line_aligned(q, sq_k, sq_e), tile_chunk(nblocks));
+        (int)tiles_c, scale_mode == MXQ_SCALE_RCEIL, mx3d_store_mode(q, N, K, sq_k, sq_e), tile_chunk(nblocks));
     return launch_status();
 }
 

@@ -116,12 +116,14 @@ __global__ __launch_bounds__(kBlockThreads) void block_contig_kernel(
 // reads are 1 KB row pieces and its column-major writes run down whole
 // columns, which measured faster than the plain order on grids of many
 // residency rounds (the 64-expert weights) and no faster on small ones.
-// nt: nontemporal q stores, for a column-major launch whose 128-row column
-// runs start on 128-byte lines; with runs off the lines, plain stores let L2
-// merge the two parts of a line before it goes to HBM, where a partial
-// nontemporal write of a line costs a read-modify-write of a memory burst.
-// Row-major q is written in 64-byte halves of lines by two waves, so it
-// takes plain stores (nt = 0).
+// nt: the q stores.  0: plain.  1: nontemporal, for a column-major launch
+// whose 128-row column runs start on 128-byte lines; with runs off the
+// lines, plain stores let L2 merge the two parts of a line before it goes to
+// HBM, where a partial nontemporal write of a line costs a read-modify-write
+// of a memory burst.  2: as 1, at device scope through a buffer descriptor
+// per batch entry (written through the XCD's L2); the host picks it when
+// every q offset of a batch entry fits in 32 bits.  Row-major q is written
+// in 64-byte halves of lines by two waves, so it takes plain stores (nt = 0).
 template <int BR, int BC, bool E8M0, bool QROW = false>
 __global__ __launch_bounds__(kBlockThreads) void block_strided_kernel(
     const uint16_t *__restrict__ x, int64_t sxe, int64_t ldx, int rows, int cols,
@@ -301,6 +303,9 @@ __global__ __launch_bounds__(kBlockThreads) void block_strided_kernel(
         // column-major q: the lane owns 16 consecutive bytes of each of its
         // 8 output columns (the transpose happens in registers)
         uint8_t *qp = q + e * sqe + (int64_t)c0 * ldq + r0;
+        // nt == 2: offsets from the batch entry's base, below 2^32 (host-checked)
+        const auto rq = buffer_rsrc(q + e * sqe, 0xFFFFFFFFu);
+        const uint32_t qoff = (uint32_t)c0 * (uint32_t)ldq + (uint32_t)r0;
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
             uint4 o;
@@ -308,7 +313,9 @@ __global__ __launch_bounds__(kBlockThreads) void block_strided_kernel(
             o.y = cvt4_sel<E8M0>(mul(4, jj), mul(5, jj), mul(6, jj), mul(7, jj));
             o.z = cvt4_sel<E8M0>(mul(8, jj), mul(9, jj), mul(10, jj), mul(11, jj));
             o.w = cvt4_sel<E8M0>(mul(12, jj), mul(13, jj), mul(14, jj), mul(15, jj));
-            if (nt)
+            if (nt == 2)
+                stbuf16_nt_device(rq, qoff + (uint32_t)jj * (uint32_t)ldq, o);
+            else if (nt)
                 st16_nt(qp + (int64_t)jj * ldq, o);
             else
                 st16(qp + (int64_t)jj * ldq, o);

@@ -195,6 +195,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
+// 16-byte store through a buffer descriptor, nontemporal at device scope
+// (aux 18: nt sc1), so the line is written through the XCD's L2 rather than
+// left dirty in it: the 3D kernel's column runs measured 1% faster so.
+__device__ __forceinline__ void stbuf16_nt_device(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint4 v)
+{
+    u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)byte_off, 0, 18);
+}
 __device__ __forceinline__ uint4 ldbuf16_nt(__amdgpu_buffer_rsrc_t r, uint32_t byte_off)
 {
     u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 2);

@@ -13,7 +13,7 @@ SRC = os.path.join(HERE, "stream_ceiling.hip")
 LIB = os.path.join(HERE, "libstream_ceiling.so")
 HIPCC = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
 
-MODES = {"read2_write1": 0, "read_only": 1, "write_only": 2}
+MODES = {"read2_write1": 0, "read_only": 1, "write_only": 2, "read2_write1_device_scope": 3}
 
 
 def build(verbose: bool = False) -> str:
@@ -43,4 +43,5 @@ def load() -> ctypes.CDLL:
 
 
 def bytes_moved(n: int, mode: str) -> int:
-    return {"read2_write1": 3 * n, "read_only": 2 * n, "write_only": n}[mode]
+    return {"read2_write1": 3 * n, "read_only": 2 * n, "write_only": n,
+            "read2_write1_device_scope": 3 * n}[mode]
