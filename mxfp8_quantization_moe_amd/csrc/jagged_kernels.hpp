@@ -122,6 +122,48 @@ __device__ __forceinline__ uint32_t segment_split(const int32_t *s_offs, int G, 
     return (uint32_t)b | 8u | ((uint32_t)g2 << 4);
 }
 
+// The group of every element of a segment that is not wholly inside one
+// group, for the many-groups kernel: nibble j = (group of element j) - (group
+// of element 0), 0..14 (groups are ordered, so the nibbles never decrease; a
+// group index of G or more means no group); worked out once per workgroup.
+// 0 for a whole segment or one past every group; kSegByElement for a
+// segment reduced and stored element by element (the row's partial last
+// segment, or more than 14 groups inside 8 elements).
+constexpr uint32_t kSegByElement = 0xFFFFFFFFu;
+
+// A segment_groups word with one boundary inside (two groups): the boundary
+// b (its first element of the second group) and the second group's offset
+// d; false for more boundaries.  The nibbles never decrease and nibble 0 is
+// 0, so b is the lowest nonzero nibble and d the top one.
+__device__ __forceinline__ bool one_boundary(uint32_t sg, int &b, int &d)
+{
+    b = __builtin_ctz(sg) >> 2;
+    d = (int)(sg >> 28);
+    return sg == (((uint32_t)d * 0x11111111u) << (4 * b));
+}
+__device__ __forceinline__ uint32_t segment_groups(const int32_t *s_offs, int G, const SegInfo &si,
+                                                   int e0, int cols)
+{
+    if (!si.inb || si.fast || si.g >= G)
+        return 0u;
+    if (e0 + 8 > cols)
+        return kSegByElement;
+    // each group end p inside the segment (0 < p < 8) moves elements p..7 on
+    // by one group: one LDS read per end, at most 14 ends (no nibble carries)
+    uint32_t d = 0u;
+    int n = 0;
+#pragma unroll 1
+    for (int g = si.g; g < G; ++g) {
+        const int p = s_offs[g] - e0;
+        if (p >= 8)
+            break;
+        if (++n > 14)
+            return kSegByElement;
+        d += 0x11111111u << (4 * p);
+    }
+    return d;
+}
+
 // the two maxima of a split segment (sp = segment_split(...) != 0)
 __device__ __forceinline__ void reduce_split_inl(uint32_t *s_amax, int G, uint4 v, int g1, uint32_t sp)
 {
@@ -169,7 +211,8 @@ __device__ __forceinline__ void store_split_inl(uint8_t *qr, const float *s_scal
 // Out-of-line forms for the few-groups kernels, where inlined they would
 // take registers from the common path (128 VGPRs, four waves per SIMD) and
 // spill; a call costs the caller a wait for all its outstanding loads, which
-// the many-groups kernel, where split segments are common, cannot afford.
+// the many-groups kernel, where split segments are common, cannot afford
+// (it reduces and stores them inline, in its own form).
 __device__ __attribute__((noinline)) void reduce_split(uint32_t *s_amax, int G, uint4 v, int g1,
                                                        uint32_t sp)
 {
@@ -220,9 +263,7 @@ __device__ __forceinline__ void reduce_segment(uint32_t *s_amax, const int32_t *
         reduce_segment_elementwise(s_amax, s_offs, G, xr, v, si, e0, cols);
 }
 
-// Scale and store one segment (row-major q row qr).  INL: split segments
-// inline (the many-groups kernel) rather than through a call.
-template <bool INL = false>
+// Scale and store one segment (row-major q row qr) in the few-groups kernel.
 __device__ __forceinline__ void store_segment(uint8_t *qr, const float *s_scale, const int32_t *s_offs,
                                               int G, const uint16_t *xr, const uint4 &v,
                                               const SegInfo &si, int e0, int cols, uint32_t sp)
@@ -234,10 +275,7 @@ __device__ __forceinline__ void store_segment(uint8_t *qr, const float *s_scale,
         return;
     }
     if (sp != 0u) {
-        if constexpr (INL)
-            store_split_inl(qr, s_scale, G, v, si.g, sp, e0);
-        else
-            store_split(qr, s_scale, G, v, si.g, sp, e0);
+        store_split(qr, s_scale, G, v, si.g, sp, e0);
         return;
     }
     int gj = si.g;
@@ -247,6 +285,68 @@ __device__ __forceinline__ void store_segment(uint8_t *qr, const float *s_scale,
         if (gj < G)
             qr[e0 + j] = (uint8_t)cvt1(__uint_as_float(seg_elem(xr, v, e0, j, cols) << 16) *
                                        s_scale[gj]);
+    }
+}
+
+// Scale and store one segment in the many-groups kernel (sg = its
+// segment_groups word): whole segments and segments with group boundaries
+// inside share one 8-byte store, each element times its own group's
+// multiplier, so a wave whose lanes hold both kinds issues one store per
+// slot; elements past the last group are left alone (byte stores for such a
+// segment), and kSegByElement segments go element by element.
+__device__ __forceinline__ void store_segment_seg(uint8_t *qr, const float *s_scale, const int32_t *s_offs,
+                                                  int G, const uint16_t *xr, const uint4 &v,
+                                                  const SegInfo &si, int e0, int cols, uint32_t sg)
+{
+    if (!si.inb || si.g >= G)
+        return;
+    if (sg != kSegByElement) {
+        float y[8];
+        uint32_t valid = 0u;
+        if (si.fast) {
+            const float sa = s_scale[si.g];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                y[j] = elem8(v, j) * sa;
+            valid = 0xFFu;
+        } else {
+            int b, d;
+            if (one_boundary(sg, b, d)) {
+                const float sa = s_scale[si.g];
+                const bool second = si.g + d < G;
+                const float sb = second ? s_scale[si.g + d] : 0.0f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    y[j] = elem8(v, j) * (j < b ? sa : sb);
+                valid = second ? 0xFFu : (1u << b) - 1u;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int g = si.g + (int)((sg >> (4 * j)) & 15u);
+                    y[j] = g < G ? elem8(v, j) * s_scale[g] : 0.0f;
+                    valid |= g < G ? 1u << j : 0u;
+                }
+            }
+        }
+        uint2 o;
+        o.x = cvt4_nosat(y[0], y[1], y[2], y[3]);
+        o.y = cvt4_nosat(y[4], y[5], y[6], y[7]);
+        if (valid == 0xFFu) {
+            st8_nt(qr + e0, o);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if ((valid >> j) & 1u)
+                    qr[e0 + j] = (uint8_t)((j < 4 ? o.x : o.y) >> (8 * (j & 3)));
+        }
+        return;
+    }
+    int gj = si.g;
+#pragma unroll 1
+    for (int j = 0; j < 8 && e0 + j < cols; ++j) {
+        gj = advance_group(s_offs, G, gj, e0 + j);
+        if (gj < G)
+            qr[e0 + j] = (uint8_t)cvt1(__uint_as_float(seg_elem(xr, v, e0, j, cols) << 16) * s_scale[gj]);
     }
 }
 
@@ -267,10 +367,13 @@ __device__ __forceinline__ void store_segment(uint8_t *qr, const float *s_scale,
 // folds NR consecutive entries of its own wave (NR consecutive segments of
 // one slot, NR*8 columns) into runs of one group, with one LDS atomic per
 // run; a wave's LDS operations complete in order, so this needs no
-// workgroup barrier.  The group of each folded segment is worked out once
-// per workgroup.  Dynamic LDS: 3*G words, rounded up to 4, plus NR*256 words
-// of segment maxima (SEG) and NR*256 words of segment splits (segment_split,
-// for every lane's segments).
+// workgroup barrier.  A segment with group boundaries inside enters the fold
+// with the elements of its first group and sends each later group's
+// elements to it by one atomic; its per-element groups (segment_groups) are
+// worked out once per workgroup, like the group of each folded segment.
+// Dynamic LDS: 3*G words, rounded up to 4, plus NR*256 words of segment
+// maxima (SEG) and NR*256 words of per-segment boundary words (SEG:
+// segment_groups, else segment_split) for every lane's segments.
 template <int NR, bool SEG>
 __device__ __forceinline__ void jagged_contig_body(
     const uint16_t *__restrict__ x, int64_t ldx, int rows, int cols,
@@ -282,7 +385,7 @@ __device__ __forceinline__ void jagged_contig_body(
     uint32_t *s_amax = smem + G;
     float *s_scale = reinterpret_cast<float *>(smem + 2 * G);
     uint32_t *s_seg = smem + ((3 * G + 3) & ~3);   // SEG: NR*256 segment maxima in column order
-    uint32_t *s_split = s_seg + (SEG ? NR * kThreads : 0);   // NR*256 segment splits
+    uint32_t *s_split = s_seg + (SEG ? NR * kThreads : 0);   // NR*256 boundary words
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -334,7 +437,8 @@ __device__ __forceinline__ void jagged_contig_body(
         for (int i = 0; i < NR; ++i) {
             const int e0 = 8 * (i * kThreads + t);
             si[i] = seg_info(s_offs, G, g, e0, cols);
-            s_split[i * kThreads + t] = segment_split(s_offs, G, si[i], e0, cols);
+            s_split[i * kThreads + t] = SEG ? segment_groups(s_offs, G, si[i], e0, cols)
+                                            : segment_split(s_offs, G, si[i], e0, cols);
             g = si[i].g;
             gw[i] = __builtin_amdgcn_readfirstlane(si[i].g);
             const bool same = si[i].fast && si[i].g == gw[i];
@@ -343,6 +447,8 @@ __device__ __forceinline__ void jagged_contig_body(
             lane_fast = lane_fast && si[i].fast;
         }
     }
+    // SEG: every lane of the wave has only whole segments
+    const bool wave_fast = __ballot(!lane_fast) == 0ull;
 
     // SEG: groups of this thread's NR consecutive segments (G where a
     // segment is not wholly inside one group: those are reduced element by
@@ -359,7 +465,7 @@ __device__ __forceinline__ void jagged_contig_body(
         for (int j = 0; j < NR; ++j) {
             const SegInfo sj = seg_info(s_offs, G, g, 8 * (fold_seg + j), cols);
             g = sj.g;
-            sgv[j] = sj.fast ? sj.g : G;
+            sgv[j] = sj.inb ? sj.g : G;   // the group of the segment's first element
         }
     }
 
@@ -370,15 +476,56 @@ __device__ __forceinline__ void jagged_contig_body(
             uint32_t *const wseg = s_seg + wv * (NR * 64);   // this wave's entries
 #pragma unroll
             for (int i = 0; i < NR; ++i) {
-                wseg[i * 64 + lane] = si[i].fast ? fold2(absmax_u4(cur[i])) : 0u;
-                if (si[i].inb && !si[i].fast && si[i].g < G) {
-                    const uint32_t sp = s_split[i * kThreads + t];
-                    if (sp != 0u)
-                        reduce_split_inl(s_amax, G, cur[i], si[i].g, sp);
-                    else
+                // a whole segment's max, or the max of the elements in the
+                // segment's first group (the fold's group for the entry); the
+                // elements of each later group go to it by one atomic per
+                // group; kSegByElement segments reduce element by element and
+                // contribute 0 here
+                uint32_t m = 0u;
+                if (si[i].fast) {
+                    m = fold2(absmax_u4(cur[i]));
+                } else if (si[i].inb && si[i].g < G) {
+                    const uint32_t sg = s_split[i * kThreads + t];
+                    int b, d;
+                    if (sg != kSegByElement && one_boundary(sg, b, d)) {
+                        uint32_t m2 = 0u;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const uint32_t a = elem8_bits(cur[i], j) & 0x7fffu;
+                            if (j < b)
+                                m = a > m ? a : m;
+                            else
+                                m2 = a > m2 ? a : m2;
+                        }
+                        if (si[i].g + d < G && m2 != 0u)
+                            atomicMax(&s_amax[si[i].g + d], m2);
+                    } else if (sg != kSegByElement) {
+                        uint32_t acc = 0u;
+                        int run = 0;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const int dj = (int)((sg >> (4 * j)) & 15u);
+                            const uint32_t a = elem8_bits(cur[i], j) & 0x7fffu;
+                            if (dj == 0) {
+                                m = a > m ? a : m;
+                            } else {
+                                if (dj != run) {
+                                    if (run > 0 && acc != 0u && si[i].g + run < G)
+                                        atomicMax(&s_amax[si[i].g + run], acc);
+                                    acc = 0u;
+                                    run = dj;
+                                }
+                                acc = a > acc ? a : acc;
+                            }
+                        }
+                        if (run > 0 && acc != 0u && si[i].g + run < G)
+                            atomicMax(&s_amax[si[i].g + run], acc);
+                    } else {
                         reduce_segment_elementwise(s_amax, s_offs, G, xr, cur[i], si[i],
                                                    8 * (i * kThreads + t), cols);
+                    }
                 }
+                wseg[i * 64 + lane] = m;
             }
             // this wave's writes are done before its reads (LDS operations of
             // a wave complete in order; the wait and the memory clobber keep
@@ -456,7 +603,7 @@ __device__ __forceinline__ void jagged_contig_body(
         }
         __syncthreads();
         uint8_t *qr = q + (int64_t)r * ldq;
-        if (lane_fast) {
+        if (SEG ? wave_fast : lane_fast) {
             float sc[NR];
 #pragma unroll
             for (int i = 0; i < NR; ++i)
@@ -464,11 +611,16 @@ __device__ __forceinline__ void jagged_contig_body(
 #pragma unroll
             for (int i = 0; i < NR; ++i)
                 st8_nt(qr + 8 * (i * kThreads + t), quant8_fp32scale(cur[i], sc[i]));
+        } else if constexpr (SEG) {
+#pragma unroll
+            for (int i = 0; i < NR; ++i)
+                store_segment_seg(qr, s_scale, s_offs, G, xr, cur[i], si[i], 8 * (i * kThreads + t), cols,
+                                  si[i].fast ? 0u : s_split[i * kThreads + t]);
         } else {
 #pragma unroll
             for (int i = 0; i < NR; ++i)
-                store_segment<SEG>(qr, s_scale, s_offs, G, xr, cur[i], si[i], 8 * (i * kThreads + t),
-                                   cols, si[i].fast ? 0u : s_split[i * kThreads + t]);
+                store_segment(qr, s_scale, s_offs, G, xr, cur[i], si[i], 8 * (i * kThreads + t), cols,
+                              si[i].fast ? 0u : s_split[i * kThreads + t]);
         }
     };
 

@@ -66,6 +66,45 @@ def test_jagged_rowwise_ragged(rows, cols, G, mult, tail, seed):
     check_rowwise(bits, offs)
 
 
+def _pileup_offsets(cols):
+    """Group ends for the many-groups rowwise kernel's per-element group
+    words: 13, 14, 15 and 16 groups ending inside one 8-column segment (empty
+    groups piled on one column and one-column groups), a segment with two
+    boundaries that also holds the last group's end (elements past it belong
+    to no group), and random groups of about 16 columns elsewhere."""
+    ends = []
+    base = 1000
+    for k in (13, 14, 15, 16):
+        start = base + 3                                   # inside the segment [base, base + 8)
+        ends += [start] * (k - 4) + [start + 1, start + 2, start + 3, start + 4]
+        base += 64
+    g = np.random.default_rng(77)
+    ends += list(np.sort(g.integers(base + 8, cols - 40, size=600)))
+    last = (cols - 40) // 8 * 8
+    ends += [last + 2, last + 5]                           # two ends in one segment, then no group
+    return np.maximum.accumulate(np.array(sorted(ends), dtype=np.int64)).astype(np.int32)
+
+
+@pytest.mark.parametrize("rows,cols,seed", [(8, 16384, 47), (700, 16384, 48), (6, 16381, 49),
+                                            (5, 8191, 50)])
+def test_jagged_rowwise_boundary_pileups(rows, cols, seed):
+    bits = adversarial((rows, cols), 100 + seed)
+    offs = _pileup_offsets(cols)
+    assert offs.size > 16 and offs[-1] < cols
+    check_rowwise(bits, offs)
+
+
+@pytest.mark.parametrize("G,cols,tail,seed", [(1024, 16384, 1, 51), (256, 16384, 2, 52),
+                                               (2000, 16384, 3, 53), (300, 16381, 0, 54)])
+def test_jagged_rowwise_random_narrow_groups(G, cols, tail, seed):
+    """Random group ends (about 16, 64, 8 and 55 columns per group) over the
+    full register window: segments with one, two and more boundaries; the
+    last case's last group covers the row's partial last segment."""
+    bits = adversarial((12, cols), 100 + seed)
+    offs = random_offsets(cols, G, seed, short_tail=tail)
+    check_rowwise(bits, offs)
+
+
 def test_jagged_rowwise_empty_extent_writes_empty_group_scales():
     bits = np.zeros((4, 0), dtype=np.uint16)
     x = torch.zeros((4, 8), dtype=torch.bfloat16, device="cuda")[:, :0]
