@@ -332,14 +332,16 @@ def build_moe_bwd_mx(torch, mxq, workloads, gen):
 
 
 def build_mx3d(torch, mxq, workloads, gen, E, sweep, rceil=False):
+    import numpy as np
+
     N, K = 8192, 5120
     w = torch.empty((E, N, K), dtype=torch.bfloat16, device="cuda")
     name = "mx3d_sweep_expert" if sweep else "mx3d_expert"
-    first = None
+    first = []   # the oracle's sample: the first (up to) three experts
     for e, bits in enumerate(gen.map(name, [(e,) for e in range(E)], "W")):
         w[e].copy_(bf16_dev(torch, bits))
-        if e == 0:
-            first = bits
+        if e < 3:
+            first.append(bits)
         if E > 8 and (e + 1) % 16 == 0:
             print(f"[bench] {e + 1} of {E} experts on the device", file=sys.stderr, flush=True)
     q = torch.empty(E * N * K, dtype=torch.uint8, device="cuda")
@@ -356,9 +358,12 @@ def build_mx3d(torch, mxq, workloads, gen, E, sweep, rceil=False):
             "values": "N(0,0.02)" + (", 1% of 32x1 blocks zero, 1% x 2^20" if sweep else ""),
             "scales": f"e8m0 {mode}, (E, N/32, K)", "seeds": seeds}
 
+    sample = np.stack(first)
+    ns = sample.shape[0]
+
     def cpu_sample(oracle):
-        return (lambda: oracle.quantize_mx_3d_colwise(first[None], mode=mode),
-                3 * N * K + (N // 32) * K, f"expert 0 of W, whole ({N},{K})")
+        return (lambda: oracle.quantize_mx_3d_colwise(sample, mode=mode),
+                ns * (3 * N * K + (N // 32) * K), f"experts 0-{ns - 1} of W, whole ({ns},{N},{K})")
 
     return [l], [w, q, s], desc, cpu_sample
 
