@@ -1190,8 +1190,29 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
                                 pq[i] = (uint8_t)(ow[i >> 2] >> (8 * (i & 3)));
                     }
                 }
+            } else if (rb >= plo && rb + 16 <= phi && s_end[gb[tt] - 1] == s_end[ga[tt]]) {
+                // rows of two groups (any groups between them empty), all
+                // inside the pack: the first b rows take group ga's
+                // multipliers, the rest gb's; one 16-byte store per column
+                const int b = s_end[ga[tt]] - rb;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float sa = __uint_as_float(s_pk[ga[tt] - g0][8 * cg + j]);
+                    const float sb = __uint_as_float(s_pk[gb[tt] - g0][8 * cg + j]);
+                    float y[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        y[i] = elem8(v[tt][i], j) * (i < b ? sa : sb);
+                    uint4 o;
+                    o.x = cvt4_nosat(y[0], y[1], y[2], y[3]);
+                    o.y = cvt4_nosat(y[4], y[5], y[6], y[7]);
+                    o.z = cvt4_nosat(y[8], y[9], y[10], y[11]);
+                    o.w = cvt4_nosat(y[12], y[13], y[14], y[15]);
+                    st16(q + (int64_t)(cbase + j) * ldq + rb, o);
+                }
             } else {
-                // rows of several groups: per-row multipliers, byte stores
+                // rows of more groups, or rows outside the pack: per-row
+                // multipliers, byte stores
                 int gc = ga[tt];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
