@@ -996,6 +996,91 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
             }
         }
         __syncthreads();
+    } else if (G <= NTH) {
+        // one group per thread (thread g holds group g): its flags stay in
+        // registers, two scans run across the workgroup, and the thread that
+        // owns this workgroup's item writes it (no search)
+        __shared__ int s_wmax[NW], s_wa[NW], s_wb[NW], s_wfirst[NW];
+        const bool valid = t < G;
+        int hi = rows;
+        if (valid) {
+            const int e = offs[t];
+            hi = e < 0 ? 0 : (e > rows ? rows : e);
+            s_end[t] = hi;
+        }
+        __syncthreads();
+        const int lo = (valid && t > 0) ? s_end[t - 1] : 0;
+        const int lo_prev = (valid && t > 1) ? s_end[t - 2] : 0;   // start of group t - 1
+        const bool lng = valid && hi > lo && hi - (lo & ~15) > TROWS;
+        const bool lng_prev = valid && t > 0 && lo > lo_prev && lo - (lo_prev & ~15) > TROWS;
+        const int brk =
+            (valid && (t == 0 || lng || lng_prev || lo / TROWS != lo_prev / TROWS)) ? t : -1;
+        // run start of group t: inclusive max-scan of the breaks
+        int run = brk;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(run, d, 64);
+            if (lane >= d)
+                run = max(run, y);
+        }
+        if (lane == 63)
+            s_wmax[w] = run;
+        __syncthreads();
+        for (int ww = 0; ww < w; ++ww)
+            run = max(run, s_wmax[ww]);
+        const bool lead = valid && !lng && ((t - run) % kPackMax) == 0;
+        const int nch = lng ? (CH > 0 ? chunk_count(lo, hi, CH) : 1) : 0;
+        // exclusive prefix counts of long-group items and of packs; the
+        // first stop (pack leader or long group) after each group
+        int ia = nch, ib = lead ? 1 : 0;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int ya = __shfl_up(ia, d, 64);
+            const int yb = __shfl_up(ib, d, 64);
+            if (lane >= d) {
+                ia += ya;
+                ib += yb;
+            }
+        }
+        const uint64_t stops = __ballot(lead || lng);
+        if (lane == 63) {
+            s_wa[w] = ia;
+            s_wb[w] = ib;
+        }
+        if (lane == 0)
+            s_wfirst[w] = stops ? 64 * w + __ffsll((unsigned long long)stops) - 1 : G;
+        __syncthreads();
+        int ea = ia - nch, eb = ib - (lead ? 1 : 0), nlong = 0, npack = 0;
+        for (int ww = 0; ww < NW; ++ww) {
+            if (ww < w) {
+                ea += s_wa[ww];
+                eb += s_wb[ww];
+            }
+            nlong += s_wa[ww];
+            npack += s_wb[ww];
+        }
+        const uint64_t above = lane < 63 ? stops & (~0ull << (lane + 1)) : 0ull;
+        int next = above ? 64 * w + __ffsll((unsigned long long)above) - 1 : G;
+        for (int ww = w + 1; ww < NW && !above; ++ww)
+            if (s_wfirst[ww] < G) {
+                next = s_wfirst[ww];
+                break;
+            }
+        const int item = sm.item;
+        if (lng && ea <= item && item < ea + nch) {
+            s_sel[0] = 0;
+            s_sel[1] = t;
+            s_sel[2] = item - ea;
+            s_sel[3] = ea;
+        }
+        if (lead && item == nlong + eb) {
+            s_sel[0] = 1;
+            s_sel[1] = t;
+            s_sel[2] = next;
+        }
+        if (t == 0 && item >= nlong + npack)
+            s_sel[0] = 2;
+        __syncthreads();
     } else {
         strided_table<NTH, TROWS, CH>(offs, G, rows, s_end, s_lead, s_lpre, s_ppre);
         if (t == 0) {
@@ -1111,6 +1196,41 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
                     for (int d = 0; d < 4; ++d) {
                         atomicMax(&s_pk[gw - g0][8 * cg + 2 * d], mx[d] & 0xffffu);
                         atomicMax(&s_pk[gw - g0][8 * cg + 2 * d + 1], mx[d] >> 16);
+                    }
+                }
+            } else if (__all(ga[tt] == gb[tt])) {
+                // every lane's rows in one group (16-row aligned groups):
+                // the lane's column maxima, then a segmented max scan down
+                // the wave's row pieces (lanes 8 apart, runs of one group),
+                // so the last lane of each run issues its group's atomics
+                const int gme = ga[tt];
+                uint32_t mx[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    mx[0] = absmax2(mx[0], v[tt][i].x);
+                    mx[1] = absmax2(mx[1], v[tt][i].y);
+                    mx[2] = absmax2(mx[2], v[tt][i].z);
+                    mx[3] = absmax2(mx[3], v[tt][i].w);
+                }
+                // every shuffle runs on all lanes (a lane shuffle reads 0
+                // from a lane that is switched off), the tests after it
+#pragma unroll
+                for (int k = 1; k < 8; k <<= 1) {
+                    const int gprev = __shfl_up(gme, 8 * k, 64);
+                    const bool take = qd >= k && gprev == gme;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const uint32_t pv = (uint32_t)__shfl_up((int)mx[d], 8 * k, 64);
+                        mx[d] = take ? pkmax(mx[d], pv) : mx[d];
+                    }
+                }
+                const int gnext = __shfl_down(gme, 8, 64);
+                const bool last = qd == 7 || gnext != gme;
+                if (last && gme < g1 && col_ok) {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        atomicMax(&s_pk[gme - g0][8 * cg + 2 * d], mx[d] & 0xffffu);
+                        atomicMax(&s_pk[gme - g0][8 * cg + 2 * d + 1], mx[d] >> 16);
                     }
                 }
             } else if (ga[tt] < g1 && col_ok) {

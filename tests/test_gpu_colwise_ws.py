@@ -63,6 +63,9 @@ def test_waiting_fallback(spin):
 @pytest.mark.parametrize("rows,cols,G,mult,tail,seed", [
     (16384, 512, 8, 16, 0, 11), (10000, 200, 64, 1, 7, 12), (40000, 16, 300, 1, 0, 13),
     (30000, 8, 4096, 1, 3, 14), (4096, 4096, 3, 16, 0, 15),
+    # the one-group-per-thread table (up to 256 groups with 4-wave workgroups), and one past it
+    (20000, 24, 65, 1, 0, 16), (30000, 16, 200, 16, 5, 17), (12000, 8, 256, 1, 0, 18),
+    (12000, 8, 257, 1, 0, 19),
 ])
 def test_random_groups(rows, cols, G, mult, tail, seed):
     offs = random_offsets(rows, G, seed, multiple=mult, short_tail=tail)

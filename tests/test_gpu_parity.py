@@ -134,6 +134,10 @@ def test_jagged_rowwise_empty_extent_writes_empty_group_scales():
     (3000, 16, 1000, 1, 3, 27),    # groups of a few rows, many per lane
     (20000, 24, 30, 16, 0, 28),    # long and short groups interleaved
     (4096, 8, 4096, 1, 0, 29),     # the most groups, most of them empty
+    (20000, 40, 65, 1, 3, 34),     # G just past 64: the one-group-per-thread table
+    (40000, 24, 100, 16, 0, 31),   # long and short groups mixed, the same table
+    (9000, 16, 512, 1, 5, 32),     # G = the workgroup's threads
+    (9000, 16, 513, 1, 0, 33),     # one past: the chunked table
 ])
 def test_jagged_colwise_ragged(rows, cols, G, mult, tail, seed):
     bits = adversarial((rows, cols), 200 + seed)
