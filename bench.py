@@ -9,7 +9,9 @@ all-zero and 1% scaled by 2^20.  One step = one launch over all 64 experts.
 
 Other workloads (``--workload``): ``moe_bwd`` (jagged rowwise quantization
 of grad_out^T (4096, 16384) plus jagged colwise of x (16384, 4096), 8 token
-groups, fp32 scales), ``moe_bwd_mx`` (the same operands as jagged MXFP8),
+groups, fp32 scales), ``moe_bwd_ws`` (the colwise operand with a workspace), ``moe_bwd_g256`` and
+``moe_bwd_g256_ws`` (the same operands in the 256 token groups of a
+fine-grained MoE layer), ``moe_bwd_mx`` (the same operands as jagged MXFP8),
 ``mx3d`` (E = 8, N(0, 0.02)), ``mx3d_e{1,2,4,16,64}`` (the E sweep),
 ``mx3d_rceil``, ``rowwise_g64`` (the jagged rowwise operand with 64 groups of
 256 columns), ``moe_bwd_mx_unaligned`` (jagged MX rowwise with group starts off
@@ -185,11 +187,13 @@ def _sizes(offs):
     return [int(v) for v in np.diff(np.concatenate([[0], offs]))]
 
 
-def build_moe_bwd(torch, mxq, workloads, gen, ws=False):
+def build_moe_bwd(torch, mxq, workloads, gen, ws=False, fine=False):
     """ws: the colwise operand through the call with a workspace (long token
-    groups split across workgroups, every element read once)."""
+    groups split across workgroups, every element read once).  fine: 256
+    token groups of a fine-grained MoE layer (sizes multiples of 16 around
+    64, some empty) instead of the 8 MoE groups."""
     go_t, x = list(gen.map("moe_grad_out_t", [()], "grad_out_t")) + list(gen.map("moe_x", [()], "x"))
-    offs = workloads.moe_offsets()
+    offs = workloads.moe_offsets_fine() if fine else workloads.moe_offsets()
     G = offs.size
     d_go, d_x = bf16_dev(torch, go_t), bf16_dev(torch, x)
     d_offs = torch.from_numpy(offs).cuda()
@@ -200,7 +204,8 @@ def build_moe_bwd(torch, mxq, workloads, gen, ws=False):
     q2 = torch.empty(R2 * C2, dtype=torch.uint8, device="cuda")
     s2 = torch.empty(G * C2, dtype=torch.float32, device="cuda")
     keep = [d_go, d_x, d_offs, q1, s1, q2, s2]
-    l1 = Launch("jagged_rowwise grad_out^T (4096,16384)", "jagged_contig_kernel<8>",
+    l1 = Launch("jagged_rowwise grad_out^T (4096,16384)",
+                "jagged_contig_seg_kernel<8>" if G > 16 else "jagged_contig_kernel<8>",
                 mxq.mxq_quantize_jagged_rowwise,
                 (d_go.data_ptr(), R1, C1, C1, 1, d_offs.data_ptr(), G, q1.data_ptr(), C1, 1,
                  s1.data_ptr(), G, 1), 3 * R1 * C1 + 4 * R1 * G, R1 * C1, (("q1", q1), ("s1", s1)))
@@ -216,12 +221,12 @@ def build_moe_bwd(torch, mxq, workloads, gen, ws=False):
         l2 = Launch("jagged_colwise x (16384,4096)", "jagged_strided_kernel<8, 3, 8, false>",
                     mxq.mxq_quantize_jagged_colwise, cargs,
                     3 * R2 * C2 + 4 * G * C2, R2 * C2, (("q2", q2), ("s2", s2)))
-    desc = {"workload": "moe_bwd_jagged" + ("_ws" if ws else ""),
+    desc = {"workload": "moe_bwd_jagged" + ("_g256" if fine else "") + ("_ws" if ws else ""),
             "tensors": "grad_out^T bf16 (4096,16384) rowwise -> row-major e4m3; "
                        "x bf16 (16384,4096) colwise -> column-major e4m3",
             "groups": int(G), "group_sizes": _sizes(offs),
             "scales": "fp32 per (row, group) and per (group, column)",
-            "seeds": dict(workloads.MOE_SEEDS)}
+            "seeds": dict(workloads.MOE_SEEDS, **({"offs": workloads.MOE_FINE_SEED} if fine else {}))}
 
     def cpu_sample(oracle):
         n = 1024
@@ -230,7 +235,7 @@ def build_moe_bwd(torch, mxq, workloads, gen, ws=False):
         return (lambda: (oracle.quantize_jagged_rowwise(go_t[:n], offs),
                          oracle.quantize_jagged_colwise(xs, offs)),
                 nbytes, f"jagged rowwise on {n} of 4096 rows of grad_out^T and jagged colwise on "
-                        f"{n} of 4096 columns of x (all 16384 tokens, same 8 groups)")
+                        f"{n} of 4096 columns of x (all 16384 tokens, same {G} groups)")
 
     return [l1, l2], keep, desc, cpu_sample
 
@@ -487,7 +492,8 @@ def build_copy(torch, mxq, workloads, gen):
 
 
 WORKLOADS = ("mx3d_e64", "mx3d_e1", "mx3d_e2", "mx3d_e4", "mx3d_e16", "mx3d", "mx3d_rceil",
-             "moe_bwd", "moe_bwd_ws", "moe_bwd_mx", "moe_bwd_mx_unaligned", "rowwise_g64", "blockwise",
+             "moe_bwd", "moe_bwd_ws", "moe_bwd_g256", "moe_bwd_g256_ws", "moe_bwd_mx",
+             "moe_bwd_mx_unaligned", "rowwise_g64", "blockwise",
              "blockwise_t", "relayout", "copy")
 
 
@@ -498,6 +504,10 @@ def build(name, torch, mxq, workloads, gen):
         return build_moe_bwd(torch, mxq, workloads, gen)
     if name == "moe_bwd_ws":
         return build_moe_bwd(torch, mxq, workloads, gen, ws=True)
+    if name == "moe_bwd_g256":
+        return build_moe_bwd(torch, mxq, workloads, gen, fine=True)
+    if name == "moe_bwd_g256_ws":
+        return build_moe_bwd(torch, mxq, workloads, gen, ws=True, fine=True)
     if name == "moe_bwd_mx":
         return build_moe_bwd_mx(torch, mxq, workloads, gen)
     if name == "moe_bwd_mx_unaligned":

@@ -15,8 +15,9 @@ import torch
 import mxfp8_quantization_moe_amd as mxq
 import oracle_pool
 import workloads
-from gpu_helpers import (CANARY, SCALE_MODES, assert_same_bytes, bf16_dev, blockwise, i32_dev,
-                         jagged_colwise, jagged_rowwise, stream_handle)
+from gpu_helpers import (CANARY, SCALE_MODES, assert_same_bytes, bf16_dev, blockwise,
+                         colwise_workspace, i32_dev, jagged_colwise, jagged_colwise_ws, jagged_rowwise,
+                         stream_handle)
 
 pytestmark = pytest.mark.gpu
 
@@ -58,6 +59,29 @@ def test_moe_bwd_colwise_x(moe):
     assert_same_bytes(q, oq, "moe_bwd colwise q")
     assert_same_bytes(s, os_, "moe_bwd colwise scales")
     _no_nan_codes(q)
+
+
+def test_moe_bwd_fine_groups():
+    """The MoE operands in the 256 token groups of a fine-grained MoE layer
+    (sizes multiples of 16, a few empty): jagged rowwise of grad_out^T and
+    jagged colwise of x, with and without a workspace, every byte against
+    the oracle."""
+    go = workloads.moe_grad_out_t()
+    x = workloads.moe_x()
+    offs = workloads.moe_offsets_fine()
+    assert offs.size == 256 and offs[-1] == x.shape[0]
+    q, s = jagged_rowwise(bf16_dev(go), i32_dev(offs))
+    oq, os_ = oracle_pool.split_op("quantize_jagged_rowwise", go, offs, canary=CANARY)
+    assert_same_bytes(q, oq, "fine rowwise q")
+    assert_same_bytes(s, os_, "fine rowwise scales")
+    del q, s, oq, os_
+    oq, os_ = oracle_pool.split_op("quantize_jagged_colwise", x, offs, canary=CANARY)
+    q, s = jagged_colwise(bf16_dev(x), i32_dev(offs))
+    assert_same_bytes(q, oq, "fine colwise q")
+    assert_same_bytes(s, os_, "fine colwise scales")
+    q, s = jagged_colwise_ws(bf16_dev(x), i32_dev(offs), colwise_workspace(*x.shape, offs.size))
+    assert_same_bytes(q, oq, "fine colwise (workspace) q")
+    assert_same_bytes(s, os_, "fine colwise (workspace) scales")
 
 
 def _mx3d_launch(dev_w, E, mode):

@@ -141,6 +141,23 @@ def moe_offsets() -> np.ndarray:
     return offsets_moe(MOE_SEEDS["offs"])
 
 
+MOE_FINE_SEED = 2104
+
+
+def offsets_fine(seed, tokens: int = 16384, groups: int = 256) -> np.ndarray:
+    """Many token groups (a fine-grained MoE layer) in units of 16 tokens:
+    multinomial shares with Dirichlet(4) weights, so sizes spread around
+    tokens / groups and a few groups are empty."""
+    g = rng(seed)
+    units = tokens // 16
+    share = g.multinomial(units, g.dirichlet(np.full(groups, 4.0)))
+    return (np.cumsum(share) * 16).astype(np.int32)
+
+
+def moe_offsets_fine(groups: int = 256) -> np.ndarray:
+    return offsets_fine(MOE_FINE_SEED, groups=groups)
+
+
 def moe_grad_out_t() -> np.ndarray:
     """grad_out^T (4096, 16384) bits, row-major; groups along dim 1."""
     return _moe_values((4096, 16384), MOE_SEEDS["go_vals"])
