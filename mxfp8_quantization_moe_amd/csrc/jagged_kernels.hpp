@@ -741,7 +741,7 @@ __global__ __launch_bounds__(kThreads) void jagged_contig_long_kernel(
 // item owns at least one group, so a strip has at most G items.  Long
 // groups come first, largest first when G <= 64 (ranked on the device by
 // one wave, lane g holding group g), then the packs in group order.
-constexpr int kPackMax = 16;
+constexpr int kPackMax = 64;
 
 // Split path (a caller's workspace): a long group's 16-row-aligned span
 // [lo & ~15, hi) is cut into nc = ceil(span / CH) chunks of

@@ -1,7 +1,7 @@
 """Host check of the jagged colwise grid size: the number of work items per
-column strip (long groups, and packs of up to 16 consecutive short groups
+column strip (long groups, and packs of up to 64 consecutive short groups
 whose starts fall in one 1024-row block) must never exceed the bound the
-library sizes its grid with, min(G, ext // 1010 + ext // 1024 + G // 16 + 1),
+library sizes its grid with, min(G, ext // 1010 + ext // 1024 + G // 64 + 1),
 for any non-decreasing offsets.  With a workspace (split mode) a long group
 of span n rows from its 16-row-aligned start makes ceil(n / 1536) items, and
 the bound (with 512-row tiles, 4-wave workgroups) grows by
@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 TROWS = 1024
-PACK = 16
+PACK = 64
 
 
 SPLIT_TROWS = 512             # 4-wave workgroups with a workspace
@@ -114,11 +114,12 @@ def test_worst_cases():
             ends += [min(ext, e + k) for k in range(1, 40)]
         ends = np.maximum.accumulate(np.array(ends or [ext], dtype=np.int64))
         check(ends, ext)
-    # one short group starting in every block, and runs of exactly 16 + 1
+    # one short group starting in every block, and runs of exactly one pack
+    # plus one group (empty groups piled on one row)
     for ext in (4096, 65536):
         ends = np.arange(1, ext // TROWS + 1) * TROWS - 1
         check(ends, ext)
-        ends = np.repeat(np.arange(0, ext, 512), 17)[: 4096]
+        ends = np.repeat(np.arange(0, ext, 512), PACK + 1)[: 4096]
         ends = np.maximum.accumulate(ends)
         check(ends, ext)
     # long groups whose spans each just exceed a chunk multiple, from a
