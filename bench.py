@@ -36,7 +36,8 @@ Timing:
     of that kernel alone, divided by K (inputs partly in the caches when they
     fit).
 The extra workloads (``--extras``, default the MoE jagged operands without
-and with a workspace, the E=8 MX 3D weights and the blockwise operands) are
+and with a workspace, the same operands in 256 fine-grained token groups
+with a workspace, the E=8 MX 3D weights and the blockwise operands) are
 timed the same way and reported under ``workloads``; the
 streaming probes under ``stream_ceiling`` give the practical HBM ceiling of
 the same traffic mix.
@@ -59,7 +60,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_GBPS = 8000.0
 METRIC = "achieved HBM GB/s (bf16 read + fp8/scale write) and % of MI355X peak"
-DEFAULT_EXTRAS = "moe_bwd,moe_bwd_ws,mx3d,blockwise"
+DEFAULT_EXTRAS = "moe_bwd,moe_bwd_ws,moe_bwd_g256_ws,mx3d,blockwise"
 FLUSH_BYTES = 1 << 30
 
 

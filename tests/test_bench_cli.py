@@ -25,4 +25,4 @@ def test_workload_table_names_every_configuration():
     assert callable(bench.build)
     args = bench.parse([])
     assert args.workload == "mx3d_e64" and args.gpus == 1
-    assert set(args.extras.split(",")) == {"moe_bwd", "moe_bwd_ws", "mx3d", "blockwise"}
+    assert set(args.extras.split(",")) == {"moe_bwd", "moe_bwd_ws", "moe_bwd_g256_ws", "mx3d", "blockwise"}
