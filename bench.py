@@ -14,8 +14,8 @@ groups, fp32 scales), ``moe_bwd_ws`` (the colwise operand with a workspace), ``m
 fine-grained MoE layer), ``moe_bwd_mx`` (the same operands as jagged MXFP8),
 ``mx3d`` (E = 8, N(0, 0.02)), ``mx3d_e{1,2,4,16,64}`` (the E sweep),
 ``mx3d_rceil``, ``rowwise_g64`` (the jagged rowwise operand with 64 groups of
-256 columns), ``moe_bwd_mx_unaligned`` (jagged MX rowwise with group starts off
-8-element boundaries), ``blockwise`` (1 x 128 activations (8192, 4096) + 128 x 128
+256 columns), ``moe_bwd_mx_unaligned`` (both jagged MX operands with group starts off
+8- and 16-element boundaries), ``blockwise`` (1 x 128 activations (8192, 4096) + 128 x 128
 weights (4096, 4096)), ``blockwise_t`` (the transposed operands of the
 blockwise backward), ``relayout`` (per-group re-layout of (8192, 32768)
 e8m0 scales into scaled-MFMA tiles), ``copy`` (counter calibration).
@@ -264,38 +264,15 @@ def build_rowwise_groups(torch, mxq, workloads, gen, G=64):
     return [l], [d_go, d_offs, q, s], desc, None
 
 
-def build_moe_bwd_mx_unaligned(torch, mxq, workloads, gen):
-    """Jagged MX rowwise on grad_out^T with the MoE groups moved off
-    8-element boundaries (ends 6016, 8947, 9189, 9189, 10113, 13671, 14322,
-    16384): blocks whose starts are not multiples of 8."""
-    import numpy as np
-
-    go_t = gen.one("moe_grad_out_t", "grad_out_t")
-    R, C = go_t.shape
-    offs = np.minimum(workloads.moe_offsets() + np.array([0, 3, 5, 5, 1, 7, 2, 0]), C).astype(np.int32)
-    G = offs.size
-    d_go = bf16_dev(torch, go_t)
-    d_offs = torch.from_numpy(offs).cuda()
-    nb1 = mxq.jagged_mx_scale_capacity(C, G)
-    nb = int(sum((n + 31) // 32 for n in _sizes(offs)))
-    q = torch.empty(R * C, dtype=torch.uint8, device="cuda")
-    s = torch.empty(R * nb1, dtype=torch.uint8, device="cuda")
-    l = Launch("jagged_mx_rowwise grad_out^T (4096,16384), starts off 8", "jagged_mx_rowwise_kernel<8>",
-               mxq.mxq_quantize_jagged_mx_rowwise,
-               (d_go.data_ptr(), R, C, C, 1, d_offs.data_ptr(), G, q.data_ptr(), C, 1, s.data_ptr(), nb1, 1, 0),
-               3 * R * C + R * nb, R * C, (("q", q),))
-    desc = {"workload": "moe_bwd_mx_unaligned", "tensors": "grad_out^T bf16 (4096,16384) 1x32 blocks per group",
-            "groups": int(G), "group_sizes": _sizes(offs), "scales": f"e8m0 floor, {nb} blocks per row",
-            "seeds": dict(workloads.MOE_SEEDS)}
-    return [l], [d_go, d_offs, q, s], desc, None
-
-
-def build_moe_bwd_mx(torch, mxq, workloads, gen):
+def build_moe_bwd_mx(torch, mxq, workloads, gen, unaligned=False):
     """The MX variant of the MoE backward grad_weight operands: jagged MXFP8
     (32-element blocks restarting at each token-group start, e8m0 floor
-    scales) of grad_out^T rowwise and x colwise, the same 8 groups."""
+    scales) of grad_out^T rowwise and x colwise, the same 8 groups.  With
+    ``unaligned`` the group ends move by a few tokens (ends 6016, 8947,
+    9189, 9189, 10113, 13671, 14322, 16384): group starts off 8- and
+    16-element boundaries, so blocks start anywhere in a 16-byte chunk."""
     go_t, x = list(gen.map("moe_grad_out_t", [()], "grad_out_t")) + list(gen.map("moe_x", [()], "x"))
-    offs = workloads.moe_offsets()
+    offs = workloads.moe_offsets_unaligned() if unaligned else workloads.moe_offsets()
     G = offs.size
     d_go, d_x = bf16_dev(torch, go_t), bf16_dev(torch, x)
     d_offs = torch.from_numpy(offs).cuda()
@@ -309,15 +286,16 @@ def build_moe_bwd_mx(torch, mxq, workloads, gen):
     q2 = torch.empty(R2 * C2, dtype=torch.uint8, device="cuda")
     s2 = torch.empty(nb2 * C2, dtype=torch.uint8, device="cuda")
     keep = [d_go, d_x, d_offs, q1, s1, q2, s2]
-    l1 = Launch("jagged_mx_rowwise grad_out^T (4096,16384)", "jagged_mx_rowwise_kernel<8>",
+    off = ", starts off 8" if unaligned else ""
+    l1 = Launch(f"jagged_mx_rowwise grad_out^T (4096,16384){off}", "jagged_mx_rowwise_kernel<8>",
                 mxq.mxq_quantize_jagged_mx_rowwise,
                 (d_go.data_ptr(), R1, C1, C1, 1, d_offs.data_ptr(), G, q1.data_ptr(), C1, 1,
                  s1.data_ptr(), nb1, 1, 0), 3 * R1 * C1 + R1 * nb, R1 * C1, (("q1", q1),))
-    l2 = Launch("jagged_mx_colwise x (16384,4096)", "jagged_mx_colwise_kernel",
+    l2 = Launch(f"jagged_mx_colwise x (16384,4096){off}", "jagged_mx_colwise_kernel",
                 mxq.mxq_quantize_jagged_mx_colwise,
                 (d_x.data_ptr(), R2, C2, C2, 1, d_offs.data_ptr(), G, q2.data_ptr(), 1, R2,
                  s2.data_ptr(), C2, 1, 0), 3 * R2 * C2 + nb * C2, R2 * C2, (("q2", q2),))
-    desc = {"workload": "moe_bwd_jagged_mx",
+    desc = {"workload": "moe_bwd_jagged_mx_unaligned" if unaligned else "moe_bwd_jagged_mx",
             "tensors": "grad_out^T bf16 (4096,16384) 1x32 blocks per group -> row-major e4m3; "
                        "x bf16 (16384,4096) 32x1 blocks per group -> column-major e4m3",
             "groups": int(G), "group_sizes": _sizes(offs),
@@ -512,7 +490,7 @@ def build(name, torch, mxq, workloads, gen):
     if name == "moe_bwd_mx":
         return build_moe_bwd_mx(torch, mxq, workloads, gen)
     if name == "moe_bwd_mx_unaligned":
-        return build_moe_bwd_mx_unaligned(torch, mxq, workloads, gen)
+        return build_moe_bwd_mx(torch, mxq, workloads, gen, unaligned=True)
     if name.startswith("rowwise_g") and name[len("rowwise_g"):].isdigit():
         return build_rowwise_groups(torch, mxq, workloads, gen, int(name[len("rowwise_g"):]))
     if name == "mx3d":

@@ -56,6 +56,71 @@ __device__ __forceinline__ uint4 shift_piece(const uint4 &lo, const uint4 &hi, i
     return make_uint4((uint32_t)o0, (uint32_t)(o0 >> 32), (uint32_t)o1, (uint32_t)(o1 >> 32));
 }
 
+// 16-byte values as two 64-bit halves, moved by whole bytes (0 < s < 16).
+// bytes_up: byte j of the result is byte j - s of v (0 below s).
+// bytes_down: byte j of the result is byte j + s of v (0 from 16 - s).
+__device__ __forceinline__ uint4 bytes_up(const uint4 &v, int s)
+{
+    const uint64_t a = ((uint64_t)v.y << 32) | v.x, b = ((uint64_t)v.w << 32) | v.z;
+    uint64_t ra, rb;
+    if (s < 8) {
+        ra = a << (8 * s);
+        rb = (b << (8 * s)) | (s ? a >> (64 - 8 * s) : 0ull);
+    } else {
+        ra = 0ull;
+        rb = a << (8 * (s - 8));
+    }
+    return make_uint4((uint32_t)ra, (uint32_t)(ra >> 32), (uint32_t)rb, (uint32_t)(rb >> 32));
+}
+__device__ __forceinline__ uint4 bytes_down(const uint4 &v, int s)
+{
+    const uint64_t a = ((uint64_t)v.y << 32) | v.x, b = ((uint64_t)v.w << 32) | v.z;
+    uint64_t ra, rb;
+    if (s < 8) {
+        ra = (a >> (8 * s)) | (s ? b << (64 - 8 * s) : 0ull);
+        rb = b >> (8 * s);
+    } else {
+        ra = b >> (8 * (s - 8));
+        rb = 0ull;
+    }
+    return make_uint4((uint32_t)ra, (uint32_t)(ra >> 32), (uint32_t)rb, (uint32_t)(rb >> 32));
+}
+
+// Bytes [from, to) of the 16-byte value v (byte k at base[k], base 16-byte
+// aligned), 0 <= from <= to <= 16, as aligned pieces of 1, 2, 4 and 8 bytes
+// (at most four stores on each side of the aligned middle).
+__device__ __forceinline__ void put16_range(uint8_t *base, const uint4 &v, int from, int to)
+{
+    const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+    int k = from;
+    if ((k & 1) && k < to) {
+        base[k] = (uint8_t)(wd[k >> 2] >> (8 * (k & 3)));
+        k += 1;
+    }
+    if ((k & 2) && k + 2 <= to) {
+        *reinterpret_cast<uint16_t *>(base + k) = (uint16_t)(wd[k >> 2] >> (8 * (k & 3)));
+        k += 2;
+    }
+    if ((k & 4) && k + 4 <= to) {
+        *reinterpret_cast<uint32_t *>(base + k) = wd[k >> 2];
+        k += 4;
+    }
+    if (k + 8 <= to) {
+        *reinterpret_cast<uint2 *>(base + k) = make_uint2(wd[k >> 2], wd[(k >> 2) + 1]);
+        k += 8;
+    }
+    if (k + 4 <= to) {
+        *reinterpret_cast<uint32_t *>(base + k) = wd[k >> 2];
+        k += 4;
+    }
+    if (k + 2 <= to) {
+        *reinterpret_cast<uint16_t *>(base + k) = (uint16_t)(wd[k >> 2] >> (8 * (k & 3)));
+        k += 2;
+    }
+    if (k < to)
+        base[k] = (uint8_t)(wd[k >> 2] >> (8 * (k & 3)));
+}
+
 // Bytes [from, to) of w (byte k of w at base[k]), one byte store each: the
 // ends of a run of contiguous pieces.
 __device__ __forceinline__ void put_bytes(uint8_t *base, uint64_t w, int from, int to)
@@ -315,7 +380,54 @@ __global__ __launch_bounds__(kJmxThreads) void jagged_mx_colwise_kernel(
         }
     }
 
-    const bool full = (rb & 15) == 0 && rb + 16 <= hi;
+    // A group start off a 16-row boundary (sh = rb mod 16, the same for
+    // every lane of the tile): the 8 lanes of a column (lane bits 3..5) hold
+    // consecutive 16-row pieces, so a lane stores the aligned 16-byte word
+    // that holds its last sh rows and the next lane's first 16 - sh rows
+    // (`joined`, when all of them lie in the group); the first lane's head
+    // and the last lane's tail, and pieces at the group's end, go out as
+    // aligned parts.
+    const int sh = rb & 15;
+    if (sh != 0) {
+        const int nval = hi - rb;   // this lane's rows inside the group (>= 1)
+        const bool joined = qd < 7 && rb + 32 - sh <= hi;
+        const bool prev_joined = qd > 0 && rb + 16 - sh <= hi;
+        uint8_t *qa = q + (int64_t)c0 * ldq + (rb - sh);   // 16-byte aligned
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            uint4 o;
+            o.x = cvt4(elem8(v[0], jj) * sc[jj], elem8(v[1], jj) * sc[jj], elem8(v[2], jj) * sc[jj],
+                       elem8(v[3], jj) * sc[jj]);
+            o.y = cvt4(elem8(v[4], jj) * sc[jj], elem8(v[5], jj) * sc[jj], elem8(v[6], jj) * sc[jj],
+                       elem8(v[7], jj) * sc[jj]);
+            o.z = cvt4(elem8(v[8], jj) * sc[jj], elem8(v[9], jj) * sc[jj], elem8(v[10], jj) * sc[jj],
+                       elem8(v[11], jj) * sc[jj]);
+            o.w = cvt4(elem8(v[12], jj) * sc[jj], elem8(v[13], jj) * sc[jj], elem8(v[14], jj) * sc[jj],
+                       elem8(v[15], jj) * sc[jj]);
+            // the next lane's piece of this column (used only when joined,
+            // i.e. when that lane holds rows of the group and is active)
+            uint4 nx;
+            nx.x = (uint32_t)__shfl_down((int)o.x, 8, 64);
+            nx.y = (uint32_t)__shfl_down((int)o.y, 8, 64);
+            nx.z = (uint32_t)__shfl_down((int)o.z, 8, 64);
+            nx.w = (uint32_t)__shfl_down((int)o.w, 8, 64);
+            uint8_t *p = qa + (int64_t)jj * ldq;
+            if (!prev_joined)
+                put16_range(p, bytes_up(o, sh), sh, sh + nval < 16 ? sh + nval : 16);
+            if (nval > 16 - sh) {
+                // the word after: this lane's last rows, then the next lane's first
+                const uint4 lo = bytes_down(o, 16 - sh), hi2 = bytes_up(nx, sh);
+                const uint4 w2 = make_uint4(lo.x | hi2.x, lo.y | hi2.y, lo.z | hi2.z, lo.w | hi2.w);
+                if (joined)
+                    st16(p + 16, w2);
+                else
+                    put16_range(p + 16, w2, 0, nval - (16 - sh) < sh ? nval - (16 - sh) : sh);
+            }
+        }
+        return;
+    }
+
+    const bool full = rb + 16 <= hi;
     uint8_t *qp = q + (int64_t)c0 * ldq + rb;
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {

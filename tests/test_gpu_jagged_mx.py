@@ -140,3 +140,23 @@ def test_moe_bwd_x_colwise(mode):
     nb = int(sum((n + 31) // 32 for n in sizes))
     assert np.all(s[nb:] == CANARY)
     assert not np.any((q & 0x7F) == 0x7F)
+
+
+@pytest.mark.parametrize("mode", ["floor", "rceil"])
+def test_moe_bwd_unaligned_starts(mode):
+    """Both MoE operands with the group ends moved by a few tokens, so group
+    starts sit off 8- and 16-element boundaries (the bench's unaligned MX
+    workload): every byte against the oracle."""
+    offs = workloads.moe_offsets_unaligned()
+    assert np.any(offs[:-1] % 16 != 0)
+    go = workloads.moe_grad_out_t()
+    q, s = jagged_mx_rowwise(bf16_dev(go), i32_dev(offs), mode)
+    oq, os_ = oracle_pool.split_op("quantize_jagged_mx_rowwise", go, offs, mode=mode, canary=CANARY)
+    assert_same_bytes(q, oq, f"unaligned grad_out^T jagged mx {mode} q")
+    assert_same_bytes(s, os_, f"unaligned grad_out^T jagged mx {mode} scales")
+    del go, q, s, oq, os_
+    x = workloads.moe_x()
+    q, s = jagged_mx_colwise(bf16_dev(x), i32_dev(offs), mode)
+    oq, os_ = oracle_pool.split_op("quantize_jagged_mx_colwise", x, offs, mode=mode, canary=CANARY)
+    assert_same_bytes(q, oq, f"unaligned x jagged mx {mode} q")
+    assert_same_bytes(s, os_, f"unaligned x jagged mx {mode} scales")

@@ -141,6 +141,17 @@ def moe_offsets() -> np.ndarray:
     return offsets_moe(MOE_SEEDS["offs"])
 
 
+# per-group shifts of the MoE group ends (the last end stays at the extent):
+# starts off 8- and 16-element boundaries
+MOE_END_SHIFTS = (0, 3, 5, 5, 1, 7, 2, 0)
+
+
+def moe_offsets_unaligned(extent: int = 16384) -> np.ndarray:
+    """The MoE group ends moved by MOE_END_SHIFTS (ends 6016, 8947, 9189,
+    9189, 10113, 13671, 14322, 16384 at 16384 tokens)."""
+    return np.minimum(moe_offsets() + np.array(MOE_END_SHIFTS), extent).astype(np.int32)
+
+
 MOE_FINE_SEED = 2104
 
 
