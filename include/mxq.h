@@ -120,6 +120,15 @@ mxq_status mxq_quantize_jagged_rowwise(const uint16_t *x, int64_t rows, int64_t 
  * scales  (num_groups, cols) fp32, strides (ss_g, ss_c).
  * Layouts with a kernel: sx_c == 1 && sq_r == 1 (row-major in, column-major
  * out), and sx_r == 1 && sq_r == 1 (column-major in and out).
+ *
+ * Row-major in, with num_groups <= 256, rows <= 391,680 (255 chunks of 1536
+ * rows) and distinct scale slots: token groups longer than the 1536 rows a
+ * workgroup holds are cut into chunks that exchange each column's maximum
+ * through that column's own scale slot of the group, so every element is
+ * read once.  Two kernels run in stream order: one zeroes those slots, the
+ * second quantizes; while it runs the slots hold intermediate words (a
+ * maximum and two counts), and at its end the scales.  Other extents read
+ * the rows of groups longer than 3072 rows twice.
  */
 mxq_status mxq_quantize_jagged_colwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t sx_r,
                                        int64_t sx_c, const int32_t *offs, int32_t num_groups,
@@ -136,8 +145,9 @@ mxq_status mxq_quantize_jagged_colwise(const uint16_t *x, int64_t rows, int64_t 
  * For a row-major x and column-major q, token groups longer than the rows one
  * workgroup holds (3072) are cut into chunks quantized by separate
  * workgroups, which exchange their column maxima through the workspace, so
- * every element is read from memory once (the call without a workspace reads
- * the rows of such groups twice).  The column-major-in layout needs no
+ * every element is read from memory once, in one launch and for up to 4096
+ * groups (the call without a workspace needs a second, clearing launch and
+ * at most 256 groups for the same).  The column-major-in layout needs no
  * workspace and runs as mxq_quantize_jagged_colwise.
  *
  * workspace        device memory of at least
@@ -349,8 +359,10 @@ mxq_status mxq_quantize_blockwise(const uint16_t *x, int64_t rows, int64_t cols,
  * column-major q with the bound on how long a chunk waits for the other
  * chunks of its token group set by the caller (in polls); 0 looks once, a
  * negative value never waits, so the chunks reduce their groups' rows
- * themselves (the path taken when the others do not arrive in time).  Other
- * layouts -> MXQ_ERR_INVALID_ARG.
+ * themselves (the path taken when the others do not arrive in time).  A
+ * NULL workspace selects the exchange through the scale slots of
+ * mxq_quantize_jagged_colwise (extents it does not cover ->
+ * MXQ_ERR_INVALID_ARG).  Other layouts -> MXQ_ERR_INVALID_ARG.
  */
 mxq_status mxq_debug_jagged_colwise_ws_spin(const uint16_t *x, int64_t rows, int64_t cols,
                                             int64_t sx_r, int64_t sx_c, const int32_t *offs,

@@ -179,13 +179,39 @@ ColwisePlan colwise_plan(int64_t ext, int64_t ncols, int64_t G, bool split)
     return p;
 }
 
+// The scale slots (g, c), g < G, c < ncols, are distinct words: the
+// workspace-free split path keeps one column's exchange in each.
+bool distinct_scale_slots(int64_t G, int64_t ncols, int64_t ss_g, int64_t ss_c)
+{
+    const int64_t ag = ss_g < 0 ? -ss_g : ss_g, ac = ss_c < 0 ? -ss_c : ss_c;
+    if (G == 1)
+        return ncols == 1 || ac != 0;
+    if (ncols == 1)
+        return ag != 0;
+    if (ag == 0 || ac == 0)
+        return false;
+    return ag / ncols >= ac || ac / G >= ag;   // one stride spans the other's whole extent
+}
+
+// The split path without a workspace applies: few enough groups for the
+// 4-wave workgroups' table (one group per thread), at most kSlotMaxChunks
+// chunks per group (the slot's 8-bit counts), distinct scale slots.
+bool colwise_in_slots(int64_t ext, int64_t ncols, int64_t G, int64_t ss_g, int64_t ss_c)
+{
+    const int64_t chunk = (int64_t)kSplitTiles * 16 * kSplitWaves * (64 / kJaggedStridedCG);
+    return G <= 64 * kSplitWaves && ext <= kSlotMaxChunks * chunk &&
+           distinct_scale_slots(G, ncols, ss_g, ss_c);
+}
+
 // jagged, reduction across rows of a (ext, ncols) row-major view, column-major
-// q; split mode exchanges column maxima through ws (zero between calls)
+// q; split mode exchanges column maxima through ws (zero between calls) or,
+// with no ws and `slots`, through the long groups' scale slots (cleared by a
+// small kernel launched first)
 mxq_status run_jagged_strided(const uint16_t *x, int64_t ext, int64_t ncols, int64_t ldx,
                               const int32_t *offs, int32_t G, uint8_t *q, int64_t ldq,
                               float *scales, int64_t ss_g, int64_t ss_col, hipStream_t st,
                               uint32_t *ws = nullptr, int64_t ws_bytes = 0,
-                              int spin_limit = kColwiseSpinLimit)
+                              int spin_limit = kColwiseSpinLimit, bool slots = false)
 {
     if (ncols == 0)
         return MXQ_OK;
@@ -193,14 +219,20 @@ mxq_status run_jagged_strided(const uint16_t *x, int64_t ext, int64_t ncols, int
         return MXQ_ERR_INVALID_ARG;
     constexpr int CG = kJaggedStridedCG, NW = kJaggedStridedWaves, T = kJaggedStridedTiles;
     constexpr int NWS = kSplitWaves, TS = kSplitTiles;
-    const bool split = ws != nullptr;
+    const bool split = ws != nullptr || slots;
     const ColwisePlan p = colwise_plan(ext, ncols, G, split);
     if (p.nblocks > INT32_MAX || p.items > INT32_MAX)
         return MXQ_ERR_INVALID_ARG;
-    if (split && ws_bytes < p.ws_bytes)
+    if (ws && ws_bytes < p.ws_bytes)
         return MXQ_ERR_WORKSPACE;
     const size_t lds = G > 64 ? (3 * (size_t)G + 2) * sizeof(int) + (size_t)G : 0;
     const dim3 grid((unsigned)p.nblocks), block(64 * (split ? NWS : NW));
+    if (!ws && slots) {
+        const int ch = TS * 16 * NWS * (64 / CG);
+        const dim3 cgrid((unsigned)std::min<int64_t>((ncols + 255) / 256, 64), (unsigned)G);
+        jagged_colwise_clear_kernel<<<cgrid, dim3(256), 0, st>>>(offs, G, (int)ext, (int)ncols, scales,
+                                                                 ss_g, ss_col, ch);
+    }
     if (split)
         jagged_strided_kernel<CG, TS, NWS, true><<<grid, block, lds, st>>>(
             x, ldx, (int)ext, (int)ncols, offs, G, q, ldq, scales, ss_g, ss_col, (int)p.nsuper,
@@ -420,7 +452,9 @@ mxq_status mxq_quantize_jagged_colwise(const uint16_t *x, int64_t rows, int64_t 
     if (sx_c == 1 && sq_r == 1) {
         if (sx_r % 8 != 0 || sq_c % 16 != 0)
             return MXQ_ERR_INVALID_ARG;
-        return run_jagged_strided(x, rows, cols, sx_r, offs, num_groups, q, sq_c, scales, ss_g, ss_c, st);
+        return run_jagged_strided(x, rows, cols, sx_r, offs, num_groups, q, sq_c, scales, ss_g, ss_c, st,
+                                  nullptr, 0, kColwiseSpinLimit,
+                                  colwise_in_slots(rows, cols, num_groups, ss_g, ss_c));
     }
     if (sx_r == 1 && sq_r == 1) {
         // column-major in and out: the rowwise pattern on the transpose
@@ -790,12 +824,16 @@ extern "C" mxq_status mxq_debug_jagged_colwise_ws_spin(
     mxq_status s = check_jagged_common(x, rows, cols, offs, num_groups, q, scales);
     if (s != MXQ_OK)
         return s;
-    if (!(sx_c == 1 && sq_r == 1) || !workspace || workspace_bytes < 0 ||
+    if (!(sx_c == 1 && sq_r == 1) || workspace_bytes < 0 ||
         (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0 || sx_r % 8 != 0 || sq_c % 16 != 0)
+        return MXQ_ERR_INVALID_ARG;
+    // no workspace: the exchange in the scale slots, where it applies
+    if (!workspace && !colwise_in_slots(rows, cols, num_groups, ss_g, ss_c))
         return MXQ_ERR_INVALID_ARG;
     return run_jagged_strided(x, rows, cols, sx_r, offs, num_groups, q, sq_c, scales, ss_g, ss_c,
                               reinterpret_cast<hipStream_t>(stream),
-                              reinterpret_cast<uint32_t *>(workspace), workspace_bytes, spin_limit);
+                              reinterpret_cast<uint32_t *>(workspace), workspace_bytes, spin_limit,
+                              workspace == nullptr);
 }
 
 extern "C" mxq_status mxq_debug_cast4_e4m3(const float *y, int64_t n, uint8_t *out, int32_t unclamped,

@@ -769,6 +769,39 @@ constexpr int kSetWords = 72;
 constexpr int kSetArrive = 64;
 constexpr int kSetDepart = 65;
 
+// Split path without a workspace: the chunks of a (group, strip) exchange
+// each column's maximum through that column's own fp32 scale slot of the
+// group, zeroed beforehand by jagged_colwise_clear_kernel.  While the
+// exchange runs a slot holds the column maximum (|bf16| bits, bits 0-14),
+// the arrival count (bits 15-23) and the departure count (bits 24-31); an
+// arrival merges the maximum and counts itself in one compare-and-swap, and
+// the last chunk to leave writes the scale over the word.  So a group may
+// have at most 255 chunks (the host checks the extent).
+constexpr uint32_t kSlotMax = 0x7FFFu;
+constexpr uint32_t kSlotArrive = 1u << 15;
+constexpr uint32_t kSlotDepart = 1u << 24;
+constexpr int kSlotMaxChunks = 255;
+__device__ __forceinline__ uint32_t slot_arrivals(uint32_t w) { return (w >> 15) & 0x1FFu; }
+
+// Zeroes the scale slots the workspace-free split path exchanges through:
+// every column of each group cut into more than one chunk of ch rows (the
+// main kernel's rule: clamped ends, span from the 16-row-aligned start).
+// Grid (column blocks, G); 256 threads.
+__global__ __launch_bounds__(256) void jagged_colwise_clear_kernel(
+    const int32_t *__restrict__ offs, int G, int rows, int cols, float *__restrict__ scales,
+    int64_t ss_g, int64_t ss_c, int ch)
+{
+    const int g = blockIdx.y;
+    auto clamp_end = [&](int e) { return e < 0 ? 0 : (e > rows ? rows : e); };
+    const int lo = g ? clamp_end(offs[g - 1]) : 0;
+    int hi = clamp_end(offs[g]);
+    hi = hi < lo ? lo : hi;
+    if (chunk_count(lo, hi, ch) <= 1)
+        return;
+    for (int c = blockIdx.x * 256 + threadIdx.x; c < cols; c += gridDim.x * 256)
+        scales[(int64_t)g * ss_g + (int64_t)c * ss_c] = 0.0f;
+}
+
 // Workgroup -> (item, column strip).  SPS = 8 / CG strips of 8*CG columns
 // (16*CG bytes of a row) make one 128-byte "superstrip"; the SPS workgroups
 // of a superstrip get block ids that differ by 8, so with the round-robin
@@ -1474,6 +1507,12 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
         for (int ww = 0; ww < NW; ++ww)
             acol = umax(acol, s_red[ww][t]);
     }
+    // in split mode without a workspace, column t's scale slot of group g
+    // carries the exchange (see kSlotMax)
+    const bool in_slots = SPLIT && nc > 1 && ws == nullptr;
+    uint32_t *const slot =
+        reinterpret_cast<uint32_t *>(scales + (int64_t)g * ss_g + (int64_t)(strip * SW + t) * ss_c);
+    const bool has_col = t < SW && strip * SW + t < cols;
     if constexpr (SPLIT) {
         if (nc > 1) {
             // Every global access of the exchange hands its result to LDS
@@ -1483,28 +1522,63 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
             // before another thread's arrival or departure.
             __shared__ int s_flag;
             __shared__ uint32_t s_col[SW];
-            uint32_t *const set = ws + ((int64_t)s_sel[3] * nsuper + strip) * kSetWords;
-            if (t < SW)
-                s_col[t] = umax(acol, __hip_atomic_fetch_max(set + t, acol, __ATOMIC_RELAXED,
-                                                             __HIP_MEMORY_SCOPE_AGENT));
-            __syncthreads();   // all of this workgroup's maxima are in
-            if (t == 0) {
-                __hip_atomic_fetch_add(set + kSetArrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                // a negative limit takes the fallback without looking
-                int n = 0;
-                bool all = false;
-                while (spin_limit >= 0 &&
-                       !(all = __hip_atomic_load(set + kSetArrive, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)nc) &&
-                       n < spin_limit) {
-                    __builtin_amdgcn_s_sleep(2);
-                    ++n;
+            uint32_t *const set =
+                ws ? ws + ((int64_t)s_sel[3] * nsuper + strip) * kSetWords : nullptr;
+            if (in_slots) {
+                static_assert(!SPLIT || SW == 64, "the slot exchange runs on wave 0, one lane per column");
+                if (w == 0) {
+                    // arrive: merge this chunk's maximum and count it in one
+                    // compare-and-swap (each chunk changes a slot at most
+                    // twice, so the loop ends), then poll until every chunk
+                    // has arrived; a negative limit takes the fallback
+                    // without looking, 0 looks once
+                    bool done = true;
+                    uint32_t cur = 0u;
+                    if (has_col) {
+                        cur = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        uint32_t want;
+                        do {
+                            want = ((cur & ~kSlotMax) + kSlotArrive) | umax(cur & kSlotMax, acol);
+                        } while (!__hip_atomic_compare_exchange_strong(
+                            slot, &cur, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT));
+                        cur = want;
+                        done = spin_limit >= 0 && slot_arrivals(cur) >= (uint32_t)nc;
+                        for (int n = 0; !done && spin_limit >= 0 && n < spin_limit; ++n) {
+                            __builtin_amdgcn_s_sleep(2);
+                            cur = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            done = slot_arrivals(cur) >= (uint32_t)nc;
+                        }
+                    }
+                    const bool all = __all(done);
+                    s_col[t] = cur & kSlotMax;
+                    if (t == 0)
+                        s_flag = all ? 1 : 0;
                 }
-                s_flag = all ? 1 : 0;
+            } else {
+                if (t < SW)
+                    s_col[t] = umax(acol, __hip_atomic_fetch_max(set + t, acol, __ATOMIC_RELAXED,
+                                                                 __HIP_MEMORY_SCOPE_AGENT));
+                __syncthreads();   // all of this workgroup's maxima are in
+                if (t == 0) {
+                    __hip_atomic_fetch_add(set + kSetArrive, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    // a negative limit takes the fallback without looking
+                    int n = 0;
+                    bool all = false;
+                    while (spin_limit >= 0 &&
+                           !(all = __hip_atomic_load(set + kSetArrive, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)nc) &&
+                           n < spin_limit) {
+                        __builtin_amdgcn_s_sleep(2);
+                        ++n;
+                    }
+                    s_flag = all ? 1 : 0;
+                }
             }
             __syncthreads();
             if (s_flag) {
-                if (t < SW)
+                if (!in_slots && t < SW)
                     s_col[t] = __hip_atomic_load(set + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             } else {
                 // the other chunks did not arrive in time: reduce every row of
@@ -1531,14 +1605,16 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
                 }
             }
             __syncthreads();   // every read of the set has returned
-            if (t == 0) {
-                const uint32_t prev = __hip_atomic_fetch_add(set + kSetDepart, 1u, __ATOMIC_RELAXED,
-                                                             __HIP_MEMORY_SCOPE_AGENT);
-                s_flag = prev == (uint32_t)nc - 1 ? 2 : 0;
+            if (!in_slots) {
+                if (t == 0) {
+                    const uint32_t prev = __hip_atomic_fetch_add(set + kSetDepart, 1u, __ATOMIC_RELAXED,
+                                                                 __HIP_MEMORY_SCOPE_AGENT);
+                    s_flag = prev == (uint32_t)nc - 1 ? 2 : 0;
+                }
+                __syncthreads();
+                if (s_flag == 2 && t < kSetWords)
+                    __hip_atomic_store(set + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            __syncthreads();
-            if (s_flag == 2 && t < kSetWords)
-                __hip_atomic_store(set + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (t < SW)
                 acol = s_col[t];
         }
@@ -1546,9 +1622,19 @@ __global__ __launch_bounds__(64 * NW) void jagged_strided_kernel(
     if (t < SW) {
         const float s = fp32_scale(acol);
         s_scale[t] = s;
-        const int c = strip * SW + t;
-        if (c < cols && k == 0)
-            scales[(int64_t)g * ss_g + (int64_t)c * ss_c] = s;
+        if (in_slots) {
+            // depart (this lane's reads of the slot have returned: their
+            // values were used above); the last chunk out writes the scale
+            if (has_col) {
+                const uint32_t prev = __hip_atomic_fetch_add(slot, kSlotDepart, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT);
+                if ((prev >> 24) == (uint32_t)nc - 1)
+                    __hip_atomic_store(slot, __float_as_uint(s), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+        } else if (has_col && k == 0) {
+            scales[(int64_t)g * ss_g + (int64_t)(strip * SW + t) * ss_c] = s;
+        }
     }
     __syncthreads();
 
