@@ -145,9 +145,9 @@ mxq_status mxq_quantize_jagged_colwise(const uint16_t *x, int64_t rows, int64_t 
  * For a row-major x and column-major q, token groups longer than the rows one
  * workgroup holds (3072) are cut into chunks quantized by separate
  * workgroups, which exchange their column maxima through the workspace, so
- * every element is read from memory once, in one launch and for up to 4096
- * groups (the call without a workspace needs a second, clearing launch and
- * at most 256 groups for the same).  The column-major-in layout needs no
+ * every element is read from memory once, in one launch, for up to 256
+ * groups (the call without a workspace needs a second, clearing launch for
+ * the same).  More groups run the kernel without chunks.  The column-major-in layout needs no
  * workspace and runs as mxq_quantize_jagged_colwise.
  *
  * workspace        device memory of at least
@@ -166,7 +166,9 @@ mxq_status mxq_quantize_jagged_colwise_ws(const uint16_t *x, int64_t rows, int64
                                           void *workspace, int64_t workspace_bytes, void *stream);
 
 /* Workspace bytes mxq_quantize_jagged_colwise_ws needs for these extents (a
- * bound that holds for any offsets); -1 for invalid arguments. */
+ * bound that holds for any offsets); 0 for more than 256 groups (the call
+ * then runs the kernel without chunks, which is as fast there, and needs no
+ * workspace: it may be NULL); -1 for invalid arguments. */
 int64_t mxq_jagged_colwise_workspace_bytes(int64_t rows, int64_t cols, int32_t num_groups);
 
 /*

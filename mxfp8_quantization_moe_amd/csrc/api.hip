@@ -159,8 +159,16 @@ struct ColwisePlan {
     int64_t nsuper, items, nblocks, ws_bytes;
 };
 
+// The split kernel's 4-wave workgroups build the group table one group per
+// thread up to this many groups; beyond it every workgroup scans the whole
+// table, and the 8-wave kernel without chunks is as fast or faster (random
+// 16-row-aligned groups of the MoE x operand: 257-512 groups 73-76 against
+// 84-89 us, 2048 groups 182 against 211 us, 4096 groups 410 against 650 us).
+constexpr int64_t kSplitMaxGroups = 64 * kSplitWaves;
+
 ColwisePlan colwise_plan(int64_t ext, int64_t ncols, int64_t G, bool split)
 {
+    split = split && G <= kSplitMaxGroups;
     constexpr int CG = kJaggedStridedCG, SPS = 8 / CG;
     const int NW = split ? kSplitWaves : kJaggedStridedWaves;
     const int64_t trows = 16 * NW * (64 / CG);
@@ -199,7 +207,7 @@ bool distinct_scale_slots(int64_t G, int64_t ncols, int64_t ss_g, int64_t ss_c)
 bool colwise_in_slots(int64_t ext, int64_t ncols, int64_t G, int64_t ss_g, int64_t ss_c)
 {
     const int64_t chunk = (int64_t)kSplitTiles * 16 * kSplitWaves * (64 / kJaggedStridedCG);
-    return G <= 64 * kSplitWaves && ext <= kSlotMaxChunks * chunk &&
+    return G <= kSplitMaxGroups && ext <= kSlotMaxChunks * chunk &&
            distinct_scale_slots(G, ncols, ss_g, ss_c);
 }
 
@@ -219,7 +227,9 @@ mxq_status run_jagged_strided(const uint16_t *x, int64_t ext, int64_t ncols, int
         return MXQ_ERR_INVALID_ARG;
     constexpr int CG = kJaggedStridedCG, NW = kJaggedStridedWaves, T = kJaggedStridedTiles;
     constexpr int NWS = kSplitWaves, TS = kSplitTiles;
-    const bool split = ws != nullptr || slots;
+    const bool split = (ws != nullptr || slots) && G <= kSplitMaxGroups;
+    if (!split)
+        ws = nullptr;   // many groups: the kernel without chunks needs no workspace
     const ColwisePlan p = colwise_plan(ext, ncols, G, split);
     if (p.nblocks > INT32_MAX || p.items > INT32_MAX)
         return MXQ_ERR_INVALID_ARG;
@@ -516,6 +526,9 @@ mxq_status mxq_quantize_jagged_colwise_ws(const uint16_t *x, int64_t rows, int64
     if (sx_c == 1 && sq_r == 1) {
         if (sx_r % 8 != 0 || sq_c % 16 != 0)
             return MXQ_ERR_INVALID_ARG;
+        if (num_groups > kSplitMaxGroups)   // no chunks, no workspace
+            return run_jagged_strided(x, rows, cols, sx_r, offs, num_groups, q, sq_c, scales, ss_g,
+                                      ss_c, st);
         if (!workspace)
             return MXQ_ERR_WORKSPACE;
         return run_jagged_strided(x, rows, cols, sx_r, offs, num_groups, q, sq_c, scales, ss_g, ss_c,

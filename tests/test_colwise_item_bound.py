@@ -74,10 +74,13 @@ def test_library_agrees_on_the_workspace_size():
         lib = _capi.load()
     except _capi.LibraryMissing:
         pytest.skip("library not built")
-    for ext, cols, G in ((16384, 4096, 8), (1000, 64, 1), (65536, 8, 4096), (0, 8, 3)):
+    for ext, cols, G in ((16384, 4096, 8), (1000, 64, 1), (65536, 8, 256), (0, 8, 3)):
         nstrips = -(-cols // 64)
         want = bound(ext, G, True) * nstrips * 72 * 4
         assert lib.mxq_jagged_colwise_workspace_bytes(ext, cols, G) == want
+    # more than 256 groups: the kernel without chunks, no workspace
+    for G in (257, 4096):
+        assert lib.mxq_jagged_colwise_workspace_bytes(65536, 8, G) == 0
     assert lib.mxq_jagged_colwise_workspace_bytes(-1, 8, 1) == -1
     assert lib.mxq_jagged_colwise_workspace_bytes(8, 8, 0) == -1
 
