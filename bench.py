@@ -206,7 +206,7 @@ def build_moe_bwd(torch, mxq, workloads, gen, ws=False, fine=False):
     s2 = torch.empty(G * C2, dtype=torch.float32, device="cuda")
     keep = [d_go, d_x, d_offs, q1, s1, q2, s2]
     l1 = Launch("jagged_rowwise grad_out^T (4096,16384)",
-                "jagged_contig_seg_kernel<8>" if G > 16 else "jagged_contig_kernel<8>",
+                "jagged_contig_seg_kernel<8>" if G > 1 else "jagged_contig_kernel<8>",
                 mxq.mxq_quantize_jagged_rowwise,
                 (d_go.data_ptr(), R1, C1, C1, 1, d_offs.data_ptr(), G, q1.data_ptr(), C1, 1,
                  s1.data_ptr(), G, 1), 3 * R1 * C1 + 4 * R1 * G, R1 * C1, (("q1", q1), ("s1", s1)))

@@ -27,10 +27,14 @@ constexpr int kJaggedStridedWaves = 8;  // waves per workgroup: tile = 8*16*64/C
 constexpr int kSplitTiles = 3;
 constexpr int kSplitWaves = 4;
 // the rowwise kernel folds segment maxima through LDS (one atomic per run of
-// a group per thread) above this many groups; at most this many it reduces
-// each 512-column wave slot with one wave maximum when the slot lies in one
-// group
-constexpr int kContigSegGroups = 16;
+// a group per thread) above this many groups; at most this many (one group:
+// no boundary inside a row) it reduces each 512-column wave slot with one
+// wave maximum.  With 2-16 groups the fold is as fast or faster wherever
+// boundaries fall off the 512-column slots (MoE grad_out^T 40.6 against
+// 42.8 us cold, its ends moved off 8 elements 45.3 against 53.8, 16 random
+// groups 52.6 against 71.2) and 1-2 us slower on equal groups of 2048 or
+// 8192 columns
+constexpr int kContigSegGroups = 1;
 // tile order of the 128 x 256 tile kernel: grids of at least this many
 // workgroups (about 13 rounds of the 1280 that are resident at once) take
 // XCD chunks of kTileChunk tiles in column-pair order; smaller grids keep the
