@@ -1,5 +1,6 @@
 """Streaming probes for the practical HBM ceiling of the quantization
-kernels' traffic mix (2 bytes read + 1 byte written per element), built by
+kernels' traffic mixes (2 bytes read + 1 byte written per element; 1:1 for the
+scale re-layout), built by
 ``build()`` and timed by ``bench.py`` next to the kernels.  Bench and test
 infrastructure: not part of the library."""
 from __future__ import annotations
@@ -13,7 +14,8 @@ SRC = os.path.join(HERE, "stream_ceiling.hip")
 LIB = os.path.join(HERE, "libstream_ceiling.so")
 HIPCC = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
 
-MODES = {"read2_write1": 0, "read_only": 1, "write_only": 2, "read2_write1_device_scope": 3}
+MODES = {"read2_write1": 0, "read_only": 1, "write_only": 2, "read2_write1_device_scope": 3,
+         "read1_write1": 4}
 
 
 def build(verbose: bool = False) -> str:
@@ -44,4 +46,4 @@ def load() -> ctypes.CDLL:
 
 def bytes_moved(n: int, mode: str) -> int:
     return {"read2_write1": 3 * n, "read_only": 2 * n, "write_only": n,
-            "read2_write1_device_scope": 3 * n}[mode]
+            "read2_write1_device_scope": 3 * n, "read1_write1": 4 * n}[mode]

@@ -12,7 +12,9 @@
 //   mode 2  1 byte written per element;
 //   mode 3  as mode 0, the stores nontemporal at device scope (written
 //           through the XCD's L2; the MX 3D kernel's store form), through a
-//           buffer descriptor over the output.
+//           buffer descriptor over the output;
+//   mode 4  2 bytes read + 2 bytes written per element, 16-byte nontemporal
+//           stores (the 1:1 mix of the scale re-layout).
 // A workgroup of 256 threads handles 4 x 2048 consecutive elements, each
 // thread issuing its four loads before its first store.
 #include <hip/hip_runtime.h>
@@ -44,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const uint16_t *__rest
 {
     const int64_t base = (int64_t)blockIdx.x * kPerBlock + 8 * threadIdx.x;
     u32x4 v[kUnroll];
-    if constexpr (MODE != 2) {   // modes 0, 1, 3 read
+    if constexpr (MODE != 2) {   // modes 0, 1, 3, 4 read
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int64_t e = base + (int64_t)u * kThreads * 8;
@@ -70,6 +72,14 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const uint16_t *__rest
                 __builtin_amdgcn_raw_buffer_store_b64(w, rs, (int)(uint32_t)e, 0, 18);
             }
         }
+    } else if constexpr (MODE == 4) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t e = base + (int64_t)u * kThreads * 8;
+            if (e < n)
+                __builtin_nontemporal_store(v[u] ^ u32x4{1u, 1u, 1u, 1u},
+                                            reinterpret_cast<u32x4 *>(out + 2 * e));
+        }
     } else if constexpr (MODE == 1) {
         uint32_t acc = 0u;
 #pragma unroll
@@ -92,12 +102,12 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(const uint16_t *__rest
 }  // namespace
 
 // n: elements, a multiple of 8 (below 2^32 for mode 3); in: 2n bytes (modes
-// 0, 1, 3), out: n bytes (modes 0, 2, 3) or 1024 bytes (mode 1); both
-// 16-byte aligned.  Returns 0, or
+// 0, 1, 3, 4), out: n bytes (modes 0, 2, 3), 2n bytes (mode 4) or 1024
+// bytes (mode 1); both 16-byte aligned.  Returns 0, or
 // -1 for bad arguments, or the HIP error of the launch.
 extern "C" int ceiling_stream(const void *in, void *out, int64_t n, int mode, void *stream)
 {
-    if (n <= 0 || n % 8 != 0 || mode < 0 || mode > 3 || !out || (mode != 2 && !in))
+    if (n <= 0 || n % 8 != 0 || mode < 0 || mode > 4 || !out || (mode != 2 && !in))
         return -1;
     if (mode == 3 && n > (int64_t)UINT32_MAX)
         return -1;
@@ -113,6 +123,8 @@ extern "C" int ceiling_stream(const void *in, void *out, int64_t n, int mode, vo
         stream_kernel<1><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(x, y, n);
     else if (mode == 3)
         stream_kernel<3><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(x, y, n);
+    else if (mode == 4)
+        stream_kernel<4><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(x, y, n);
     else
         stream_kernel<2><<<dim3((unsigned)blocks), dim3(kThreads), 0, st>>>(x, y, n);
     return (int)hipGetLastError();

@@ -67,11 +67,12 @@ def test_default_headline_line():
         check_kernel(k)
     ceil = d["stream_ceiling"]
     for key in ("read2_write1_GBps", "read2_write1_device_scope_GBps", "read_only_GBps",
-                "write_only_GBps", "d2d_copy_GBps"):
+                "write_only_GBps", "read1_write1_GBps", "d2d_copy_GBps"):
         assert 500 < ceil[key] < 8000, key
     assert ceil["read2_write1_best_GBps"] == max(ceil["read2_write1_GBps"],
                                                  ceil["read2_write1_device_scope_GBps"])
     assert abs(ceil["frac_of_read2_write1"] - roof["achieved"] / ceil["read2_write1_best_GBps"]) < 1e-3
+    assert abs(ceil["frac_of_read1_write1"] - roof["achieved"] / ceil["read1_write1_GBps"]) < 1e-3
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["cores"] == 1 and cpu["value"] > 0 and cpu["runs"] == 3
     assert len(d["inputs"]["sha256"]["W"]) == 64
