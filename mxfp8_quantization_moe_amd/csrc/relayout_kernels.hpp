@@ -45,6 +45,7 @@
 
 #include "group_tables.hpp"
 #include "mxq_device.hpp"
+#include "wave_ops.hpp"
 
 namespace mxq {
 
@@ -83,43 +84,67 @@ __host__ __device__ constexpr int relayout_lds_bytes(int G)
     return 4 * relayout_table_ints(G, LAYOUT) + 16 * RelayoutShape<LAYOUT, SEG>::PITCH;
 }
 
-// The 16 bytes at p (nvalid of them wanted, 1..16; the rest read as zero)
-// from the aligned 16-byte chunk holding p and, when the wanted bytes run
-// into it, the next one; both chunks hold a wanted byte.  The byte shift
-// p % 16 is the same for every lane of a wave that reads one row piece, so
-// the select on it does not diverge.
-__device__ __forceinline__ uint4 load_shifted16(const uint8_t *p, int nvalid)
-{
-    if (nvalid <= 0)
-        return make_uint4(0u, 0u, 0u, 0u);
-    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-    const int sh = (int)(a & 15);
-    // nontemporal: the same speed warm and cold (8192 x 32770 scales: 121 /
-    // 121 us), where plain loads run 107 us warm from the memory-side cache
-    // but 147 us cold; taking the second chunk from the next lane with a
-    // shuffle instead of loading it was slower (131 us)
-    const uint16_t *c = reinterpret_cast<const uint16_t *>(a & ~uintptr_t(15));
-    const uint4 c0 = ld16_nt(c);
-    const uint4 c1 = nvalid > 16 - sh ? ld16_nt(c + 8) : make_uint4(0u, 0u, 0u, 0u);
-    const uint32_t d[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-    const int q = sh >> 2, b = sh & 3;
-    uint32_t o[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const uint32_t lo = q == 0 ? d[w] : q == 1 ? d[w + 1] : q == 2 ? d[w + 2] : d[w + 3];
-        const uint32_t hi = q == 0 ? d[w + 1] : q == 1 ? d[w + 2] : q == 2 ? d[w + 3] : d[w + 4];
-        o[w] = (uint32_t)((((uint64_t)hi << 32) | lo) >> (8 * b));
+// Shifted 16-byte pieces for a wave whose lanes read consecutive pieces p =
+// base + 16 * lane (so the byte shift p % 16 is the same for every lane and
+// the select on it does not diverge); nvalid bytes of a piece are wanted (up
+// to 16), the rest read as zero.  Each lane loads only the aligned 16-byte
+// chunk holding p and takes the chunk after it from the next lane by a DPP
+// whole-wave shift (a VALU move); lane 63 loads that chunk itself.  A lane
+// loads its chunk when it wants bytes of it or when the previous lane's
+// wanted bytes run into it (nvalid_prev: the previous lane's count, 0 for
+// lane 0).  issue() only loads, so a caller issues the loads of all its
+// pieces before the first combine() waits for any; combine() needs all
+// lanes of the wave.
+// Nontemporal loads: the same speed warm and cold (8192 x 32770 scales: 121 /
+// 121 us), where plain loads run 107 us warm from the memory-side cache but
+// 147 us cold.
+struct ShiftedPiece {
+    uint4 c0, c63;
+    int sh, nvalid;
+
+    __device__ __forceinline__ void issue(const uint8_t *p, int nv, int nvalid_prev, int lane)
+    {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+        sh = (int)(a & 15);
+        nvalid = nv;
+        const uint16_t *c = reinterpret_cast<const uint16_t *>(a & ~uintptr_t(15));
+        c0 = make_uint4(0u, 0u, 0u, 0u);
+        c63 = make_uint4(0u, 0u, 0u, 0u);
+        if (nv > 0 || (sh != 0 && nvalid_prev > 16 - sh))
+            c0 = ld16_nt(c);
+        if (lane == 63 && nv > 16 - sh)
+            c63 = ld16_nt(c + 8);
     }
-    if (nvalid < 16) {
+
+    __device__ __forceinline__ uint4 combine(int lane) const
+    {
+        uint4 c1 = make_uint4(from_next_lane(c0.x), from_next_lane(c0.y), from_next_lane(c0.z),
+                              from_next_lane(c0.w));
+        if (lane == 63)
+            c1 = c63;
+        if (nvalid <= 0)
+            return make_uint4(0u, 0u, 0u, 0u);
+        const uint32_t d[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const int q = sh >> 2, b = sh & 3;
+        uint32_t o[4];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            const int keep = nvalid - 4 * w;
-            const uint32_t mask = keep >= 4 ? 0xFFFFFFFFu : (keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u));
-            o[w] &= mask;
+            const uint32_t lo = q == 0 ? d[w] : q == 1 ? d[w + 1] : q == 2 ? d[w + 2] : d[w + 3];
+            const uint32_t hi = q == 0 ? d[w + 1] : q == 1 ? d[w + 2] : q == 2 ? d[w + 3] : d[w + 4];
+            o[w] = (uint32_t)((((uint64_t)hi << 32) | lo) >> (8 * b));
         }
+        if (nvalid < 16) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int keep = nvalid - 4 * w;
+                const uint32_t mask =
+                    keep >= 4 ? 0xFFFFFFFFu : (keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u));
+                o[w] &= mask;
+            }
+        }
+        return make_uint4(o[0], o[1], o[2], o[3]);
     }
-    return make_uint4(o[0], o[1], o[2], o[3]);
-}
+};
 
 __device__ __forceinline__ uint32_t byte_of(uint32_t v, int k) { return (v >> (8 * k)) & 0xFFu; }
 
@@ -220,23 +245,29 @@ __global__ __launch_bounds__(kRelayoutThreads) void relayout_mx_scales_kernel(
     const int lane = t & 63;
     const int wv = t >> 6;
     uint4 v[4];
+    ShiftedPiece pc[4];   // LAYOUT 0 / 1: every piece's loads, then the combines
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int hr = 4 * wv + it;
+        // bytes this lane wants (and the previous lane: 16 more of the same
+        // run), clamped to a 16-byte piece
+        auto clamp16 = [](int n) { return n < 0 ? 0 : (n > 16 ? 16 : n); };
         if (LAYOUT == 1) {
             const int blk = 16 * kc + hr;                    // block within the group
             const int r0 = 1024 * rc + 16 * lane;
-            int nv = rows - r0;
-            nv = blk < nb ? (nv < 0 ? 0 : (nv > 16 ? 16 : nv)) : 0;
-            v[it] = load_shifted16(scales + (B + blk) * ss_b + r0, nv);
+            const bool any = blk < nb;
+            const int nv = any ? clamp16(rows - r0) : 0;
+            const int nvp = any && lane ? clamp16(rows - r0 + 16) : 0;
+            pc[it].issue(scales + (B + blk) * ss_b + r0, nv, nvp, lane);
         } else {
             const int r = 16 * rc + hr;
             const int b0 = 1024 * kc + 16 * lane;            // first block within the group
-            int nv = nb - b0;
-            nv = r < rows ? (nv < 0 ? 0 : (nv > 16 ? 16 : nv)) : 0;
+            const bool any = r < rows;
+            const int nv = any ? clamp16(nb - b0) : 0;
+            const int nvp = any && lane ? clamp16(nb - b0 + 16) : 0;
             const uint8_t *p = scales + (int64_t)r * ss_r + (B + b0) * ss_b;
             if (LAYOUT == 0) {
-                v[it] = load_shifted16(p, nv);
+                pc[it].issue(p, nv, nvp, lane);
             } else {
                 uint32_t o[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -246,6 +277,11 @@ __global__ __launch_bounds__(kRelayoutThreads) void relayout_mx_scales_kernel(
                 v[it] = make_uint4(o[0], o[1], o[2], o[3]);
             }
         }
+    }
+    if (LAYOUT != 2) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+            v[it] = pc[it].combine(lane);
     }
 #pragma unroll
     for (int it = 0; it < 4; ++it)
