@@ -61,3 +61,16 @@ def test_refuses_extents_beyond_the_array():
                                                    1, q.data_ptr(), 1, rows, s.data_ptr(), cols, 1,
                                                    stream_handle())
     assert code == mxq.MXQ_ERR_WORKSPACE
+
+
+def test_many_groups_need_no_scratch():
+    """More than 256 groups run the kernel without chunks: no scratch is
+    needed, any extent is accepted, and the result is the oracle's."""
+    bits = adversarial((9000, 64), 4002)
+    offs = np.sort(np.random.default_rng(4002).integers(0, 9001, 300)).astype(np.int32)
+    offs[-1] = 9000
+    assert mxq.mxq_jagged_colwise_workspace_bytes(9000, 64, 300) == 0
+    q, s = noalloc(bf16_dev(bits), i32_dev(offs))
+    oq, os_ = oracle.quantize_jagged_colwise(bits, offs, canary=CANARY)
+    assert_same_bytes(q, oq, "many groups q")
+    assert_same_bytes(s, os_, "many groups scales")
