@@ -215,13 +215,13 @@ def build_moe_bwd(torch, mxq, workloads, gen, ws=False, fine=False):
         nws = mxq.mxq_jagged_colwise_workspace_bytes(R2, C2, G)
         d_ws = torch.zeros(max(nws, 4) // 4, dtype=torch.int32, device="cuda")
         keep.append(d_ws)
-        l2 = Launch("jagged_colwise (workspace) x (16384,4096)", "jagged_strided_kernel<8, 3, 4, true>",
+        l2 = Launch("jagged_colwise (workspace) x (16384,4096)", "jagged_colwise_tile_kernel<2>",
                     mxq.mxq_quantize_jagged_colwise_ws, cargs + (d_ws.data_ptr(), nws),
                     3 * R2 * C2 + 4 * G * C2, R2 * C2, (("q2", q2), ("s2", s2)))
     else:
-        # two launches: jagged_colwise_clear_kernel zeroes the long groups'
-        # scale slots, then the split kernel exchanges maxima through them
-        l2 = Launch("jagged_colwise x (16384,4096), clear + split", "jagged_strided_kernel<8, 3, 4, true>",
+        # two launches: jagged_colwise_tile_clear_kernel zeroes the long
+        # groups' scale slots, then the tile kernel exchanges maxima through them
+        l2 = Launch("jagged_colwise x (16384,4096), clear + tile", "jagged_colwise_tile_kernel<2>",
                     mxq.mxq_quantize_jagged_colwise, cargs,
                     3 * R2 * C2 + 4 * G * C2, R2 * C2, (("q2", q2), ("s2", s2)))
     desc = {"workload": "moe_bwd_jagged" + ("_g256" if fine else "") + ("_ws" if ws else ""),

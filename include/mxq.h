@@ -121,13 +121,14 @@ mxq_status mxq_quantize_jagged_rowwise(const uint16_t *x, int64_t rows, int64_t 
  * Layouts with a kernel: sx_c == 1 && sq_r == 1 (row-major in, column-major
  * out), and sx_r == 1 && sq_r == 1 (column-major in and out).
  *
- * Row-major in, with num_groups <= 256, rows <= 391,680 (255 chunks of 1536
- * rows) and distinct scale slots: token groups longer than the 1536 rows a
- * workgroup holds are cut into chunks that exchange each column's maximum
- * through that column's own scale slot of the group, so every element is
- * read once.  Two kernels run in stream order: one zeroes those slots, the
- * second quantizes; while it runs the slots hold intermediate words (a
- * maximum and two counts), and at its end the scales.  Other extents read
+ * Row-major in, with num_groups <= 256 and distinct scale slots: token
+ * groups longer than the rows one workgroup holds are cut into chunks that
+ * exchange each column's maximum through the group's own scale slots, so
+ * every element is read once.  Chunks are 256 rows x 256 columns when
+ * rows <= 65,280 and rows <= 4096 * num_groups, else 1536 rows x 64 columns
+ * when rows <= 391,680.  Two kernels run in stream order: one zeroes those
+ * slots, the second quantizes; while it runs the slots hold intermediate
+ * words (maxima and counts), and at its end the scales.  Other extents read
  * the rows of groups longer than 3072 rows twice.
  */
 mxq_status mxq_quantize_jagged_colwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t sx_r,
@@ -143,12 +144,13 @@ mxq_status mxq_quantize_jagged_colwise(const uint16_t *x, int64_t rows, int64_t 
  * columns on a few of them.
  *
  * For a row-major x and column-major q, token groups longer than the rows one
- * workgroup holds (3072) are cut into chunks quantized by separate
- * workgroups, which exchange their column maxima through the workspace, so
- * every element is read from memory once, in one launch, for up to 256
- * groups (the call without a workspace needs a second, clearing launch for
- * the same).  More groups run the kernel without chunks.  The column-major-in layout needs no
- * workspace and runs as mxq_quantize_jagged_colwise.
+ * workgroup holds are cut into chunks (as above: 256 x 256 or 1536 x 64)
+ * quantized by separate workgroups, which exchange their column maxima
+ * through the workspace, so every element is read from memory once, in one
+ * launch, for up to 256 groups (the call without a workspace needs a second,
+ * clearing launch for the same).  More groups run the kernel without chunks.
+ * The column-major-in layout needs no workspace and runs as
+ * mxq_quantize_jagged_colwise.
  *
  * workspace        device memory of at least
  *                  mxq_jagged_colwise_workspace_bytes(rows, cols, num_groups)
@@ -181,7 +183,7 @@ int64_t mxq_jagged_colwise_workspace_bytes(int64_t rows, int64_t cols, int32_t n
  * at load, and every call leaves it zero).  Extents whose
  * workspace (mxq_jagged_colwise_workspace_bytes) exceeds it ->
  * MXQ_ERR_WORKSPACE before any launch (e.g. 16384 x 4096 with 8 groups needs
- * 331,776 bytes).  Calls on one GPU share the array: calls that overlap in
+ * 135,168 bytes).  Calls on one GPU share the array: calls that overlap in
  * time on one GPU race and must be serialized (e.g. issued on one stream).
  * The array's device address is looked up on the first call on each device
  * (MXQ_ERR_LAUNCH if that fails).

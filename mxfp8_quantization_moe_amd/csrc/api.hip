@@ -10,6 +10,7 @@
 
 #include "mxq.h"
 #include "block_kernels.hpp"
+#include "colwise_tile_kernels.hpp"
 #include "jagged_kernels.hpp"
 #include "jagged_mx_kernels.hpp"
 #include "relayout_kernels.hpp"
@@ -213,6 +214,74 @@ bool colwise_in_slots(int64_t ext, int64_t ncols, int64_t G, int64_t ss_g, int64
     const int64_t chunk = (int64_t)kSplitTiles * 16 * kSplitWaves * (64 / kJaggedStridedCG);
     return G <= kSplitMaxGroups && ext <= kSlotMaxChunks * chunk &&
            distinct_scale_slots(G, ncols, ss_g, ss_c);
+}
+
+// The colwise tile kernel: chunks of kTileT 128-row tiles x 256 columns.
+// It takes the column-major colwise calls with at most kTileMaxGroups groups,
+// at most kSlotMaxChunks chunks per group (so any offsets keep every exchange
+// set within a block of resident workgroups) and groups of at most
+// kTileMaxAvgRows rows on average.  Longer groups make sets of many chunks,
+// and the split kernel's 1536-row chunks are faster there (x (16384, 4096),
+// cold, with / without a workspace: one group 57 / 69 us against 67 / 83,
+// groups of 4096 and 12288 rows 59 / 64 against 57 / 72; eight MoE groups
+// 51 / 61 against 58 / 63).
+constexpr int kTileT = 2;
+constexpr int64_t kTileChunkRows = 128 * kTileT;
+constexpr int64_t kTileMaxAvgRows = 4096;
+
+bool tile_applies(int64_t ext, int64_t G)
+{
+    return G <= kTileMaxGroups && ext <= kSlotMaxChunks * kTileChunkRows && ext <= kTileMaxAvgRows * G;
+}
+
+// Grid and workspace of the tile kernel.  Every group has
+// max(1, ceil(n / CH)) chunks per column tile, at most G + ext / CH in all;
+// a group of more than one chunk has more than CH rows, so there are at most
+// min(G, ext / (CH + 1)) of them, one workspace set per column tile each.
+struct TilePlan {
+    int64_t tiles_c, nblocks, ws_bytes;
+};
+TilePlan tile_plan(int64_t ext, int64_t ncols, int64_t G)
+{
+    TilePlan p;
+    p.tiles_c = (ncols + 255) / 256;
+    p.nblocks = p.tiles_c * (G + ext / kTileChunkRows);
+    p.ws_bytes = std::min<int64_t>(G, ext / (kTileChunkRows + 1)) * p.tiles_c * kTileSetWords *
+                 (int64_t)sizeof(uint32_t);
+    return p;
+}
+
+// workspace of the workspace call (the tile kernel's, else the split kernel's)
+int64_t colwise_ws_bytes(int64_t ext, int64_t ncols, int64_t G)
+{
+    return tile_applies(ext, G) ? tile_plan(ext, ncols, G).ws_bytes : colwise_plan(ext, ncols, G, true).ws_bytes;
+}
+
+// jagged colwise on the tile kernel (tile_applies holds): exchange through
+// ws, or with no ws through the long groups' scale slots, cleared by a small
+// kernel launched first (distinct_scale_slots must hold)
+mxq_status run_jagged_colwise_tile(const uint16_t *x, int64_t ext, int64_t ncols, int64_t ldx,
+                                   const int32_t *offs, int32_t G, uint8_t *q, int64_t ldq, float *scales,
+                                   int64_t ss_g, int64_t ss_c, hipStream_t st, uint32_t *ws,
+                                   int64_t ws_bytes, int spin_limit = kColwiseSpinLimit)
+{
+    if (ncols == 0)
+        return MXQ_OK;
+    if (ncols % 8 != 0 || ncols > INT32_MAX)
+        return MXQ_ERR_INVALID_ARG;
+    const TilePlan p = tile_plan(ext, ncols, G);
+    if (p.nblocks > INT32_MAX)
+        return MXQ_ERR_INVALID_ARG;
+    if (ws && ws_bytes < p.ws_bytes)
+        return MXQ_ERR_WORKSPACE;
+    if (!ws) {
+        const dim3 cgrid((unsigned)std::min<int64_t>((ncols + 255) / 256, 64), (unsigned)G);
+        jagged_colwise_tile_clear_kernel<<<cgrid, dim3(256), 0, st>>>(offs, G, (int)ext, (int)ncols, scales,
+                                                                      ss_g, ss_c, (int)kTileChunkRows);
+    }
+    jagged_colwise_tile_kernel<kTileT><<<dim3((unsigned)p.nblocks), dim3(256), 0, st>>>(
+        x, ldx, (int)ext, (int)ncols, offs, G, q, ldq, scales, ss_g, ss_c, (int)p.tiles_c, ws, spin_limit);
+    return launch_status();
 }
 
 // jagged, reduction across rows of a (ext, ncols) row-major view, column-major
@@ -466,6 +535,9 @@ mxq_status mxq_quantize_jagged_colwise(const uint16_t *x, int64_t rows, int64_t 
     if (sx_c == 1 && sq_r == 1) {
         if (sx_r % 8 != 0 || sq_c % 16 != 0)
             return MXQ_ERR_INVALID_ARG;
+        if (tile_applies(rows, num_groups) && distinct_scale_slots(num_groups, cols, ss_g, ss_c))
+            return run_jagged_colwise_tile(x, rows, cols, sx_r, offs, num_groups, q, sq_c, scales, ss_g,
+                                           ss_c, st, nullptr, 0);
         return run_jagged_strided(x, rows, cols, sx_r, offs, num_groups, q, sq_c, scales, ss_g, ss_c, st,
                                   nullptr, 0, kColwiseSpinLimit,
                                   colwise_in_slots(rows, cols, num_groups, ss_g, ss_c));
@@ -494,11 +566,14 @@ mxq_status mxq_quantize_jagged_colwise_noalloc(const uint16_t *x, int64_t rows, 
     if (sx_c == 1 && sq_r == 1) {
         if (sx_r % 8 != 0 || sq_c % 16 != 0)
             return MXQ_ERR_INVALID_ARG;
-        if (colwise_plan(rows, cols, num_groups, true).ws_bytes > kScratchBytes)
+        if (colwise_ws_bytes(rows, cols, num_groups) > kScratchBytes)
             return MXQ_ERR_WORKSPACE;
         uint32_t *ws = scratch_on(stream_device(st));
         if (!ws)
             return MXQ_ERR_LAUNCH;
+        if (tile_applies(rows, num_groups))
+            return run_jagged_colwise_tile(x, rows, cols, sx_r, offs, num_groups, q, sq_c, scales, ss_g,
+                                           ss_c, st, ws, kScratchBytes);
         return run_jagged_strided(x, rows, cols, sx_r, offs, num_groups, q, sq_c, scales, ss_g, ss_c,
                                   st, ws, kScratchBytes);
     }
@@ -510,7 +585,7 @@ int64_t mxq_jagged_colwise_workspace_bytes(int64_t rows, int64_t cols, int32_t n
 {
     if (rows < 0 || cols < 0 || num_groups < 1 || num_groups > MXQ_MAX_GROUPS)
         return -1;
-    return colwise_plan(rows, cols, num_groups, true).ws_bytes;
+    return colwise_ws_bytes(rows, cols, num_groups);
 }
 
 mxq_status mxq_quantize_jagged_colwise_ws(const uint16_t *x, int64_t rows, int64_t cols,
@@ -535,6 +610,10 @@ mxq_status mxq_quantize_jagged_colwise_ws(const uint16_t *x, int64_t rows, int64
                                       ss_c, st);
         if (!workspace)
             return MXQ_ERR_WORKSPACE;
+        if (tile_applies(rows, num_groups))
+            return run_jagged_colwise_tile(x, rows, cols, sx_r, offs, num_groups, q, sq_c, scales, ss_g,
+                                           ss_c, st, reinterpret_cast<uint32_t *>(workspace),
+                                           workspace_bytes);
         return run_jagged_strided(x, rows, cols, sx_r, offs, num_groups, q, sq_c, scales, ss_g, ss_c,
                                   st, reinterpret_cast<uint32_t *>(workspace), workspace_bytes);
     }
@@ -844,7 +923,14 @@ extern "C" mxq_status mxq_debug_jagged_colwise_ws_spin(
     if (!(sx_c == 1 && sq_r == 1) || workspace_bytes < 0 ||
         (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0 || sx_r % 8 != 0 || sq_c % 16 != 0)
         return MXQ_ERR_INVALID_ARG;
-    // no workspace: the exchange in the scale slots, where it applies
+    if (tile_applies(rows, num_groups)) {
+        // no workspace: the exchange in the scale slots, where it applies
+        if (!workspace && !distinct_scale_slots(num_groups, cols, ss_g, ss_c))
+            return MXQ_ERR_INVALID_ARG;
+        return run_jagged_colwise_tile(x, rows, cols, sx_r, offs, num_groups, q, sq_c, scales, ss_g, ss_c,
+                                       reinterpret_cast<hipStream_t>(stream),
+                                       reinterpret_cast<uint32_t *>(workspace), workspace_bytes, spin_limit);
+    }
     if (!workspace && !colwise_in_slots(rows, cols, num_groups, ss_g, ss_c))
         return MXQ_ERR_INVALID_ARG;
     return run_jagged_strided(x, rows, cols, sx_r, offs, num_groups, q, sq_c, scales, ss_g, ss_c,

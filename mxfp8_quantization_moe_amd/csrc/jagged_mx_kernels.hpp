@@ -286,6 +286,89 @@ __global__ __launch_bounds__(kJmxThreads) void jagged_mx_rowwise_kernel(
     }
 }
 
+// Column jj of a lane's 16 rows x 8 columns, times s, as 16 e4m3 bytes
+// (row i in byte i); SAT as in cvt4_sel
+template <bool SAT>
+__device__ __forceinline__ uint4 tile_column_bytes(const uint4 (&v)[16], int jj, float s)
+{
+    uint4 o;
+    o.x = cvt4_sel<SAT>(elem8(v[0], jj) * s, elem8(v[1], jj) * s, elem8(v[2], jj) * s, elem8(v[3], jj) * s);
+    o.y = cvt4_sel<SAT>(elem8(v[4], jj) * s, elem8(v[5], jj) * s, elem8(v[6], jj) * s, elem8(v[7], jj) * s);
+    o.z = cvt4_sel<SAT>(elem8(v[8], jj) * s, elem8(v[9], jj) * s, elem8(v[10], jj) * s, elem8(v[11], jj) * s);
+    o.w = cvt4_sel<SAT>(elem8(v[12], jj) * s, elem8(v[13], jj) * s, elem8(v[14], jj) * s,
+                        elem8(v[15], jj) * s);
+    return o;
+}
+
+// Column-major e4m3 stores (q + c * ldq + r) of one lane's 16 rows x 8
+// columns of a 128-row tile anchored at a group start: rows rb .. rb + 15
+// (rb < hi, the group end), columns c0 .. c0 + 7, each value times its
+// column's multiplier sc[j], clamped to +-448 when SAT (e8m0 multipliers)
+// and not otherwise (fp32 multipliers, see cvt4_nosat).  The 8 lanes of a
+// column (lane bits 3..5, qd) hold the tile's consecutive 16-row pieces;
+// every lane of the tile that holds rows of the group calls this.
+template <bool SAT>
+__device__ __forceinline__ void store_tile_columns(const uint4 (&v)[16], const float (&sc)[8],
+                                                   uint8_t *__restrict__ q, int64_t ldq, int c0,
+                                                   int rb, int hi, int qd)
+{
+    // A group start off a 16-row boundary (sh = rb mod 16, the same for
+    // every lane of the tile): the 8 lanes of a column (lane bits 3..5) hold
+    // consecutive 16-row pieces, so a lane stores the aligned 16-byte word
+    // that holds its last sh rows and the next lane's first 16 - sh rows
+    // (`joined`, when all of them lie in the group); the first lane's head
+    // and the last lane's tail, and pieces at the group's end, go out as
+    // aligned parts.
+    const int sh = rb & 15;
+    if (sh != 0) {
+        const int nval = hi - rb;   // this lane's rows inside the group (>= 1)
+        const bool joined = qd < 7 && rb + 32 - sh <= hi;
+        const bool prev_joined = qd > 0 && rb + 16 - sh <= hi;
+        uint8_t *qa = q + (int64_t)c0 * ldq + (rb - sh);   // 16-byte aligned
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const uint4 o = tile_column_bytes<SAT>(v, jj, sc[jj]);
+            // the next lane's piece of this column (used only when joined,
+            // i.e. when that lane holds rows of the group and is active)
+            uint4 nx;
+            nx.x = (uint32_t)__shfl_down((int)o.x, 8, 64);
+            nx.y = (uint32_t)__shfl_down((int)o.y, 8, 64);
+            nx.z = (uint32_t)__shfl_down((int)o.z, 8, 64);
+            nx.w = (uint32_t)__shfl_down((int)o.w, 8, 64);
+            uint8_t *p = qa + (int64_t)jj * ldq;
+            if (!prev_joined)
+                put16_range(p, bytes_up(o, sh), sh, sh + nval < 16 ? sh + nval : 16);
+            if (nval > 16 - sh) {
+                // the word after: this lane's last rows, then the next lane's first
+                const uint4 lo = bytes_down(o, 16 - sh), hi2 = bytes_up(nx, sh);
+                const uint4 w2 = make_uint4(lo.x | hi2.x, lo.y | hi2.y, lo.z | hi2.z, lo.w | hi2.w);
+                if (joined)
+                    st16(p + 16, w2);
+                else
+                    put16_range(p + 16, w2, 0, nval - (16 - sh) < sh ? nval - (16 - sh) : sh);
+            }
+        }
+        return;
+    }
+
+    const bool full = rb + 16 <= hi;
+    uint8_t *qp = q + (int64_t)c0 * ldq + rb;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+        const uint4 o = tile_column_bytes<SAT>(v, jj, sc[jj]);
+        uint8_t *p = qp + (int64_t)jj * ldq;
+        if (full) {
+            st16(p, o);
+        } else {
+            const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (rb + i < hi)
+                    p[i] = (uint8_t)(ow[i >> 2] >> (8 * (i & 3)));
+        }
+    }
+}
+
 // x: (rows, cols), row r at x + r*ldx (ldx % 8 == 0), unit column stride,
 // cols % 8 == 0; groups along the rows.  q column-major: (r, c) at
 // q[c*ldq + r], ldq % 16 == 0.  scales[j*ss_b + c*ss_c] for block j.
@@ -380,77 +463,7 @@ __global__ __launch_bounds__(kJmxThreads) void jagged_mx_colwise_kernel(
         }
     }
 
-    // A group start off a 16-row boundary (sh = rb mod 16, the same for
-    // every lane of the tile): the 8 lanes of a column (lane bits 3..5) hold
-    // consecutive 16-row pieces, so a lane stores the aligned 16-byte word
-    // that holds its last sh rows and the next lane's first 16 - sh rows
-    // (`joined`, when all of them lie in the group); the first lane's head
-    // and the last lane's tail, and pieces at the group's end, go out as
-    // aligned parts.
-    const int sh = rb & 15;
-    if (sh != 0) {
-        const int nval = hi - rb;   // this lane's rows inside the group (>= 1)
-        const bool joined = qd < 7 && rb + 32 - sh <= hi;
-        const bool prev_joined = qd > 0 && rb + 16 - sh <= hi;
-        uint8_t *qa = q + (int64_t)c0 * ldq + (rb - sh);   // 16-byte aligned
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            uint4 o;
-            o.x = cvt4(elem8(v[0], jj) * sc[jj], elem8(v[1], jj) * sc[jj], elem8(v[2], jj) * sc[jj],
-                       elem8(v[3], jj) * sc[jj]);
-            o.y = cvt4(elem8(v[4], jj) * sc[jj], elem8(v[5], jj) * sc[jj], elem8(v[6], jj) * sc[jj],
-                       elem8(v[7], jj) * sc[jj]);
-            o.z = cvt4(elem8(v[8], jj) * sc[jj], elem8(v[9], jj) * sc[jj], elem8(v[10], jj) * sc[jj],
-                       elem8(v[11], jj) * sc[jj]);
-            o.w = cvt4(elem8(v[12], jj) * sc[jj], elem8(v[13], jj) * sc[jj], elem8(v[14], jj) * sc[jj],
-                       elem8(v[15], jj) * sc[jj]);
-            // the next lane's piece of this column (used only when joined,
-            // i.e. when that lane holds rows of the group and is active)
-            uint4 nx;
-            nx.x = (uint32_t)__shfl_down((int)o.x, 8, 64);
-            nx.y = (uint32_t)__shfl_down((int)o.y, 8, 64);
-            nx.z = (uint32_t)__shfl_down((int)o.z, 8, 64);
-            nx.w = (uint32_t)__shfl_down((int)o.w, 8, 64);
-            uint8_t *p = qa + (int64_t)jj * ldq;
-            if (!prev_joined)
-                put16_range(p, bytes_up(o, sh), sh, sh + nval < 16 ? sh + nval : 16);
-            if (nval > 16 - sh) {
-                // the word after: this lane's last rows, then the next lane's first
-                const uint4 lo = bytes_down(o, 16 - sh), hi2 = bytes_up(nx, sh);
-                const uint4 w2 = make_uint4(lo.x | hi2.x, lo.y | hi2.y, lo.z | hi2.z, lo.w | hi2.w);
-                if (joined)
-                    st16(p + 16, w2);
-                else
-                    put16_range(p + 16, w2, 0, nval - (16 - sh) < sh ? nval - (16 - sh) : sh);
-            }
-        }
-        return;
-    }
-
-    const bool full = rb + 16 <= hi;
-    uint8_t *qp = q + (int64_t)c0 * ldq + rb;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-        uint4 o;
-        o.x = cvt4(elem8(v[0], jj) * sc[jj], elem8(v[1], jj) * sc[jj], elem8(v[2], jj) * sc[jj],
-                   elem8(v[3], jj) * sc[jj]);
-        o.y = cvt4(elem8(v[4], jj) * sc[jj], elem8(v[5], jj) * sc[jj], elem8(v[6], jj) * sc[jj],
-                   elem8(v[7], jj) * sc[jj]);
-        o.z = cvt4(elem8(v[8], jj) * sc[jj], elem8(v[9], jj) * sc[jj], elem8(v[10], jj) * sc[jj],
-                   elem8(v[11], jj) * sc[jj]);
-        o.w = cvt4(elem8(v[12], jj) * sc[jj], elem8(v[13], jj) * sc[jj], elem8(v[14], jj) * sc[jj],
-                   elem8(v[15], jj) * sc[jj]);
-        uint8_t *p = qp + (int64_t)jj * ldq;
-        if (full) {
-            st16(p, o);
-        } else {
-            const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (rb + i < hi)
-                    p[i] = (uint8_t)(ow[i >> 2] >> (8 * (i & 3)));
-        }
-    }
+    store_tile_columns<true>(v, sc, q, ldq, c0, rb, hi, qd);
 }
 
 }  // namespace mxq

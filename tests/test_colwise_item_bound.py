@@ -8,7 +8,13 @@ the bound (with 512-row tiles, 4-wave workgroups) grows by
 (ext + 15 * min(G, ext // 498)) // 1536; the workspace
 holds one set per item number.  Items are counted here the way the kernel
 forms them; a bound that fell short would leave items without a workgroup
-(their bytes and scales unwritten)."""
+(their bytes and scales unwritten).
+
+The tile kernel (chunks of 256 rows x 256 columns, at most 256 groups,
+65,280 rows and 4096 rows per group on average) gives every group
+max(1, ceil(n / 256)) chunks per column tile, at most G + ext // 256 in all,
+and needs one workspace set per group of more than 256 rows and column tile,
+at most min(G, ext // 257) groups; checked the same way."""
 import numpy as np
 import pytest
 
@@ -51,6 +57,7 @@ def bound(ext, G, split=False):
 
 
 def check(offs, ext):
+    check_tile(offs, ext)
     G = len(offs)
     assert count_items(offs, ext) <= bound(ext, G)
     assert count_items(offs, ext, True) <= bound(ext, G, True)
@@ -68,16 +75,46 @@ def test_split_chunks_fit_their_rows():
         assert (nc - 1) * csz < span          # the last chunk holds rows
 
 
+TILE_CH = 256
+
+
+def tile_applies(ext, G):
+    return G <= 256 and ext <= 255 * TILE_CH and ext <= 4096 * G
+
+
+def tile_counts(offs, ext):
+    """(chunks, groups of more than one chunk) by the tile kernel's rules:
+    clamped ends, an empty group keeps one chunk."""
+    ends = np.clip(np.asarray(offs, dtype=np.int64), 0, ext)
+    los = np.concatenate([[0], ends[:-1]])
+    n = np.maximum(ends - los, 0)
+    chunks = np.where(n > TILE_CH, (n + TILE_CH - 1) // TILE_CH, 1)
+    return int(chunks.sum()), int((n > TILE_CH).sum()), int(chunks.max(initial=1))
+
+
+def check_tile(offs, ext):
+    G = len(offs)
+    chunks, nlong, most = tile_counts(offs, ext)
+    assert chunks <= G + ext // TILE_CH
+    assert nlong <= min(G, ext // (TILE_CH + 1))
+    if tile_applies(ext, G):
+        assert most <= 255
+
+
 def test_library_agrees_on_the_workspace_size():
     from mxfp8_quantization_moe_amd import _capi
     try:
         lib = _capi.load()
     except _capi.LibraryMissing:
         pytest.skip("library not built")
-    for ext, cols, G in ((16384, 4096, 8), (1000, 64, 1), (65536, 8, 256), (0, 8, 3)):
-        nstrips = -(-cols // 64)
-        want = bound(ext, G, True) * nstrips * 72 * 4
-        assert lib.mxq_jagged_colwise_workspace_bytes(ext, cols, G) == want
+    cases = ((16384, 4096, 8), (1000, 64, 1), (65536, 8, 256), (0, 8, 3), (65280, 264, 16),
+             (65281, 264, 16), (16384, 4096, 2), (16384, 4100, 4))
+    for ext, cols, G in cases:
+        if tile_applies(ext, G):
+            want = min(G, ext // (TILE_CH + 1)) * (-(-cols // 256)) * 264 * 4
+        else:
+            want = bound(ext, G, True) * (-(-cols // 64)) * 72 * 4
+        assert lib.mxq_jagged_colwise_workspace_bytes(ext, cols, G) == want, (ext, cols, G)
     # more than 256 groups: the kernel without chunks, no workspace
     for G in (257, 4096):
         assert lib.mxq_jagged_colwise_workspace_bytes(65536, 8, G) == 0

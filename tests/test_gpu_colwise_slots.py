@@ -1,11 +1,14 @@
 """GPU parity of the jagged colwise call WITHOUT a workspace on long token
-groups: chunks of one (group, 64-column strip) exchange their column maxima
-through the group's own fp32 scale slots (cleared by a small kernel first),
-so no row is read twice.  Byte for byte against the oracle: one group of
-every row, groups at and past chunk multiples, starts off 16-row
-boundaries, empty groups, rows past the last group, up to 256 groups, the
-most chunks a group may have (255) and one row more (the call then takes the
-path that reads long groups twice), scale strides other than row-major, the
+groups: chunks of one long group exchange their column maxima through the
+group's own fp32 scale slots (cleared by a small kernel first), so no row is
+read twice.  Up to 65,280 rows the call runs the tile kernel (chunks of 256
+rows x 256 columns, at most 255 per group); longer extents run the split
+kernel (chunks of 1536 rows x 64 columns, at most 255 per group).  Byte for
+byte against the oracle: one group of every row, groups at and past chunk
+multiples, starts off 16-row boundaries, empty groups, rows past the last
+group, up to 256 groups, the most chunks a group may have in either kernel
+and one row more (the split kernel, resp. the path that reads long groups
+twice, then takes the call), scale strides other than row-major, the
 waiting chunks' fallback (forced from the host), scale buffers holding the
 previous call's scales, and graph replays."""
 import numpy as np
@@ -22,7 +25,8 @@ from gpu_helpers import (CANARY, DEV, _gather_f32, _gather_u8, adversarial, asse
 
 pytestmark = pytest.mark.gpu
 
-CHUNK = 1536            # rows per chunk of the split path (3 tiles of 512 rows)
+CHUNK = 1536            # rows per chunk of the split kernel (3 tiles of 512 rows)
+TILE_CHUNK = 256        # rows per chunk of the tile kernel (2 tiles of 128 rows)
 MAX_CHUNKS = 255        # chunks a group may have when the scale slots carry the counts
 
 
@@ -71,13 +75,16 @@ def test_moe_backward_operand():
 
 
 @pytest.mark.parametrize("rows,cols,ends,seed", [
-    (16384, 256, [16384], 1),                       # one group: 11 chunks per strip
+    (16384, 256, [16384], 1),                       # one group (the split kernel): 11 chunks per strip
     (12000, 192, [6145, 12000], 2),
     (9300, 64, [3072, 3073, 6145, 9216, 9300], 3),
     (7000, 136, [17, 3100, 3100, 6999], 4),         # starts off 16, an empty group, a tail
     (20000, 8, [3, 19999], 6),                      # a tiny group, a long one off 16
     (6000, 64, [1536, 1537, 3073, 4608, 4609, 6000], 7),   # at and past chunk multiples
     (3000, 200, [499, 998, 1011, 1523, 3000], 8),
+    (3000, 264, [256, 257, 513, 640, 768, 769, 3000], 9),   # at and past 256-row chunks and 128-row tiles
+    (2000, 520, [5, 261, 777, 2000], 10),           # chunks and tiles of groups starting off 16 rows
+    (16384, 264, [0, 0, 0, 16384], 11),             # the tile kernel: 64 chunks per column tile
 ])
 def test_long_groups(rows, cols, ends, seed):
     check(adversarial((rows, cols), 5000 + seed), np.array(ends, np.int32), what=str(ends))
@@ -114,6 +121,17 @@ def test_most_chunks(extra):
     rows = MAX_CHUNKS * CHUNK + extra
     bits = adversarial((rows, 8), 5400 + extra)
     check(bits, np.array([rows], np.int32), what=f"{rows} rows")
+
+
+@pytest.mark.parametrize("extra", [0, 1])
+def test_tile_kernel_most_chunks(extra):
+    """255 chunks of 256 rows in one group, the tile kernel's limit (after 15
+    empty groups, which keep the average group within the tile kernel's; a
+    second 256-column tile of 8 columns), and one row more, where the call
+    takes the split kernel instead."""
+    rows = MAX_CHUNKS * TILE_CHUNK + extra
+    bits = adversarial((rows, 264), 5450 + extra)
+    check(bits, np.array([0] * 15 + [rows], np.int32), what=f"{rows} rows")
 
 
 def test_previous_scales_in_the_slots():

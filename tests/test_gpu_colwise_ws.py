@@ -1,6 +1,7 @@
 """GPU parity of the jagged colwise call with a workspace (long token groups
 cut into chunks that exchange their column maxima through the workspace)
-against the oracle, byte for byte: the MoE backward operand at full size,
+against the oracle, byte for byte (the tile kernel up to 65,280 rows, the
+split kernel beyond): the MoE backward operand at full size,
 one group of every row, groups just past chunk and tile multiples, starts off
 16-row boundaries, empty groups, rows past the last group, many groups, a
 column count off the strip width; the waiting chunks' fallback (forced from
@@ -39,7 +40,7 @@ def test_moe_backward_operand():
 
 
 @pytest.mark.parametrize("rows,cols,ends,seed", [
-    (16384, 256, [16384], 1),                       # one group: 6 chunks per strip
+    (16384, 256, [16384], 1),                       # one group (the split kernel): 6 chunks per strip
     (12000, 192, [6145, 12000], 2),                 # two groups just past 2 chunks
     (9300, 64, [3072, 3073, 6145, 9216, 9300], 3),  # at and past chunk multiples
     (7000, 136, [17, 3100, 3100, 6999], 4),         # starts off 16, an empty group, a tail
@@ -47,6 +48,9 @@ def test_moe_backward_operand():
     (20000, 8, [3, 19999], 6),                      # a tiny group, a long one off 16
     (6000, 64, [1536, 1537, 3073, 4608, 4609, 6000], 7),   # at and past 1536-row chunks
     (3000, 200, [499, 998, 1011, 1523, 3000], 8),   # just past a 512-row tile, off 16
+    (3000, 264, [256, 257, 513, 640, 768, 769, 3000], 9),   # at and past 256-row chunks and 128-row tiles
+    (2000, 520, [5, 261, 777, 2000], 10),           # chunks and tiles of groups starting off 16 rows
+    (16384, 264, [0, 0, 0, 16384], 11),             # the tile kernel: 64 chunks per column tile
 ])
 def test_long_groups(rows, cols, ends, seed):
     check(adversarial((rows, cols), 3000 + seed), np.array(ends, np.int32), what=str(ends))
@@ -70,6 +74,15 @@ def test_waiting_fallback(spin):
 def test_random_groups(rows, cols, G, mult, tail, seed):
     offs = random_offsets(rows, G, seed, multiple=mult, short_tail=tail)
     check(adversarial((rows, cols), 3200 + seed), offs, what=f"G={G}")
+
+
+@pytest.mark.parametrize("rows,ends", [
+    (65280, [0] * 15 + [65280]),      # the tile kernel's limit: 255 chunks of 256 rows
+    (65281, [0] * 15 + [65281]),      # past it: the split kernel with the workspace
+    (70000, [100, 69000, 70000]),     # long groups: the split kernel
+])
+def test_kernel_limits(rows, ends):
+    check(adversarial((rows, 72), 3300 + rows % 7), np.array(ends, np.int32), what=f"{rows} rows")
 
 
 def test_repeated_calls_and_smaller_second_call():
