@@ -57,6 +57,36 @@ __device__ __forceinline__ int advance_group(const int32_t *s_offs, int G, int g
     return lo;
 }
 
+// The groups of NQ elements at once: g[q] = the number of ends s_offs[j]
+// <= e[q] (j < G), i.e. the group holding element e[q] for non-decreasing
+// ends (G past the last end), always in [0, G].  A fixed-step search
+// (powers of two from the largest <= G down to 1) advanced for all queries
+// together, so each step's NQ LDS reads are independent and overlap, where
+// one search after another would wait on every read in turn.
+template <int NQ>
+__device__ __forceinline__ void groups_of(const int32_t *s_offs, int G, const int (&e)[NQ], int (&g)[NQ])
+{
+    int step = 1;
+    while (2 * step <= G)
+        step *= 2;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+        g[q] = 0;
+    for (; step > 0; step >>= 1) {
+        int v[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int p = g[q] + step;
+            v[q] = s_offs[(p <= G ? p : G) - 1];
+        }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int p = g[q] + step;
+            g[q] = (p <= G && v[q] <= e[q]) ? p : g[q];
+        }
+    }
+}
+
 // ---------------------------------------------------------------- contig
 
 // Per-segment group bookkeeping of the contig kernels.  A segment is the
@@ -67,13 +97,19 @@ struct SegInfo {
     bool fast;   // the whole segment lies inside group g (and inside cols)
 };
 
-__device__ __forceinline__ SegInfo seg_info(const int32_t *s_offs, int G, int g_hint, int e0, int cols)
+// the segment [e0, e0 + 8) given g, the group of element e0
+__device__ __forceinline__ SegInfo seg_info_at(const int32_t *s_offs, int G, int g, int e0, int cols)
 {
     SegInfo si;
     si.inb = e0 < cols;
-    si.g = advance_group(s_offs, G, g_hint, e0);
+    si.g = g;
     si.fast = si.inb && si.g < G && e0 + 8 <= s_offs[si.g] && e0 + 8 <= cols;
     return si;
+}
+
+__device__ __forceinline__ SegInfo seg_info(const int32_t *s_offs, int G, int g_hint, int e0, int cols)
+{
+    return seg_info_at(s_offs, G, advance_group(s_offs, G, g_hint, e0), e0, cols);
 }
 
 // Element j of a segment that is not wholly inside one group: from the
@@ -427,19 +463,34 @@ __device__ __forceinline__ void jagged_contig_body(
     }
     __syncthreads();
 
+    // the groups of this lane's segments (and, SEG, of the NR consecutive
+    // segments it folds, see fold_seg below), all searched at once
+    const int wv = t >> 6;
+    const int fold_seg = 256 * ((NR * lane) / 64) + 64 * wv + (NR * lane) % 64;
+    constexpr int NQ = SEG ? 2 * NR : NR;
+    int gq[NQ];
+    {
+        int eq[NQ];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            eq[i] = 8 * (i * kThreads + t);
+            if constexpr (SEG)
+                eq[NR + i] = 8 * (fold_seg + i);
+        }
+        groups_of<NQ>(s_offs, G, eq, gq);
+    }
+
     SegInfo si[NR];
     uint32_t uni = 0u;   // bit i: every lane of this wave has a fast segment i of one group
     bool lane_fast = true;  // every segment of this lane is fast
     int gw[NR];
     {
-        int g = advance_group(s_offs, G, 0, 8 * t);
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
             const int e0 = 8 * (i * kThreads + t);
-            si[i] = seg_info(s_offs, G, g, e0, cols);
+            si[i] = seg_info_at(s_offs, G, gq[i], e0, cols);
             s_split[i * kThreads + t] = SEG ? segment_groups(s_offs, G, si[i], e0, cols)
                                             : segment_split(s_offs, G, si[i], e0, cols);
-            g = si[i].g;
             gw[i] = __builtin_amdgcn_readfirstlane(si[i].g);
             const bool same = si[i].fast && si[i].g == gw[i];
             if (__ballot(same) == ~0ull)
@@ -457,16 +508,10 @@ __device__ __forceinline__ void jagged_contig_body(
     auto sg = [&](int j) __attribute__((always_inline)) { return sgv[j]; };
     // the folded entries NR*lane + j of this wave: slot (NR*lane + j) / 64,
     // lane (NR*lane + j) % 64 of that slot, i.e. segment fold_seg + j
-    const int wv = t >> 6;
-    const int fold_seg = 256 * ((NR * lane) / 64) + 64 * wv + (NR * lane) % 64;
     if constexpr (SEG) {
-        int g = advance_group(s_offs, G, 0, 8 * fold_seg);
 #pragma unroll
-        for (int j = 0; j < NR; ++j) {
-            const SegInfo sj = seg_info(s_offs, G, g, 8 * (fold_seg + j), cols);
-            g = sj.g;
-            sgv[j] = sj.inb ? sj.g : G;   // the group of the segment's first element
-        }
+        for (int j = 0; j < NR; ++j)
+            sgv[j] = 8 * (fold_seg + j) < cols ? gq[NR + j] : G;   // the group of the segment's first element
     }
 
     auto process_row = [&](uint4 (&cur)[NR], uint4 (&nxt)[NR], int r) __attribute__((always_inline)) {
