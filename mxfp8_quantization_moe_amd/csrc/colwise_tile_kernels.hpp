@@ -98,18 +98,59 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void j
     const int cg = lane & 7;
     const int qd = lane >> 3;
 
-    load_group_ends<256>(offs, G, rows, s_end);
-    slot_prefix2<256>(
-        G, s_pu, s_pl, [&](int gg) { return tile_chunks(group_len(s_end, gg), CH); },
-        [&](int gg) { return group_len(s_end, gg) > CH ? 1 : 0; });
+    // this workgroup's group g (chunk j of the chunk count), its chunks nu,
+    // their first index pu_g, its index among the groups of more than one
+    // chunk pl_g, and its rows [lo, hi)
     const int j = (int)(blockIdx.x / (unsigned)tiles_c);
-    if (j >= s_pu[G])
-        return;
-    const int g = find_slot(s_pu, G, j);
-    const int nu = s_pu[g + 1] - s_pu[g];
+    int g, nu, pu_g, pl_g, lo, hi;
+    if (G <= 64) {
+        // every wave builds the table in registers (lane l holds group l)
+        // and finds g by a ballot: no barrier and no LDS round trip before
+        // the loads
+        const bool valid = lane < G;
+        int e = valid ? offs[lane] : rows;
+        e = e < 0 ? 0 : (e > rows ? rows : e);
+        int el = __shfl_up(e, 1, 64);
+        el = lane == 0 ? 0 : el;
+        const int n = e > el ? e - el : 0;
+        const int cu = valid ? tile_chunks(n, CH) : 0;
+        const int lg = valid && n > CH ? 1 : 0;
+        int iu = cu, il = lg;   // inclusive prefixes
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int yu = __shfl_up(iu, d, 64);
+            const int yl = __shfl_up(il, d, 64);
+            if (lane >= d) {
+                iu += yu;
+                il += yl;
+            }
+        }
+        if (j >= __builtin_amdgcn_readlane(iu, 63))
+            return;
+        g = (int)__popcll(__ballot(iu <= j));   // groups whose chunks all precede chunk j
+        pu_g = __builtin_amdgcn_readlane(iu - cu, g);
+        nu = __builtin_amdgcn_readlane(cu, g);
+        pl_g = __builtin_amdgcn_readlane(il - lg, g);
+        lo = __builtin_amdgcn_readlane(el, g);
+        hi = __builtin_amdgcn_readlane(e, g);
+    } else {
+        load_group_ends<256>(offs, G, rows, s_end);
+        slot_prefix2<256>(
+            G, s_pu, s_pl, [&](int gg) { return tile_chunks(group_len(s_end, gg), CH); },
+            [&](int gg) { return group_len(s_end, gg) > CH ? 1 : 0; });
+        if (j >= s_pu[G])
+            return;
+        g = find_slot(s_pu, G, j);
+        pu_g = s_pu[g];
+        nu = s_pu[g + 1] - pu_g;
+        pl_g = s_pl[g];
+        lo = g ? s_end[g - 1] : 0;
+        hi = s_end[g];
+    }
+    hi = hi < lo ? lo : hi;
     // column block of B tiles: its chunks, chunk-major (B * nu workgroups,
     // at most kTileSpan, the last block narrower)
-    const int local = (int)blockIdx.x - s_pu[g] * tiles_c;
+    const int local = (int)blockIdx.x - pu_g * tiles_c;
     int B = kTileSpan / nu;
     B = B < 1 ? 1 : (B > tiles_c ? tiles_c : B);
     const int blk = local / (nu * B);
@@ -117,9 +158,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void j
     const int rr = local - blk * nu * B;
     const int k = rr / wb;
     const int tc = blk * B + (rr - k * wb);
-    const int lo = g ? s_end[g - 1] : 0;
-    int hi = s_end[g];
-    hi = hi < lo ? lo : hi;
     const int rt = lo + k * CH;              // first row of this chunk
     const int c0 = tc * 256 + 64 * w + 8 * cg;
     const bool col_ok = c0 < cols;
@@ -184,7 +222,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void j
         // outstanding global operations, only the use of their results does,
         // so this is what orders one thread's atomics before another
         // thread's arrival or departure.
-        uint32_t *const set = ws ? ws + ((int64_t)s_pl[g] * tiles_c + tc) * kTileSetWords : nullptr;
+        uint32_t *const set = ws ? ws + ((int64_t)pl_g * tiles_c + tc) * kTileSetWords : nullptr;
         bool done = true;   // (thread t alone uses s_col[t] until the fallback)
         // A chunk raises a shared maximum only when its own is larger than
         // the value it reads first: the chunks of a set arrive together, and
