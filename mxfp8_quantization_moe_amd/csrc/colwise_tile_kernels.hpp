@@ -14,7 +14,9 @@
 // set of words in a caller's workspace or through the group's own fp32
 // scale slots (zeroed first by jagged_colwise_tile_clear_kernel), then each
 // quantizes its rows with the group's scales.  Every group, an empty one
-// included, has at least one chunk, and chunk 0 writes the group's scales.
+// included, has at least one chunk; chunk 0 writes the group's scales, except
+// in the slot exchange, where the last chunk to leave writes them over the
+// exchange words.
 //
 // Workgroup numbering: group-major, then column blocks (kTileSpan), so a set
 // only waits on workgroups of its own block, at most kTileSpan consecutive
