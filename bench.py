@@ -211,17 +211,20 @@ def build_moe_bwd(torch, mxq, workloads, gen, ws=False, fine=False):
                 (d_go.data_ptr(), R1, C1, C1, 1, d_offs.data_ptr(), G, q1.data_ptr(), C1, 1,
                  s1.data_ptr(), G, 1), 3 * R1 * C1 + 4 * R1 * G, R1 * C1, (("q1", q1), ("s1", s1)))
     cargs = (d_x.data_ptr(), R2, C2, C2, 1, d_offs.data_ptr(), G, q2.data_ptr(), 1, R2, s2.data_ptr(), C2, 1)
+    # the colwise tile kernel takes one-tile chunks for groups of at most 128
+    # rows on average, two-tile chunks otherwise
+    tile_kernel = "jagged_colwise_tile_kernel<%d>" % (1 if R2 <= 128 * G else 2)
     if ws:
         nws = mxq.mxq_jagged_colwise_workspace_bytes(R2, C2, G)
         d_ws = torch.zeros(max(nws, 4) // 4, dtype=torch.int32, device="cuda")
         keep.append(d_ws)
-        l2 = Launch("jagged_colwise (workspace) x (16384,4096)", "jagged_colwise_tile_kernel<2>",
+        l2 = Launch("jagged_colwise (workspace) x (16384,4096)", tile_kernel,
                     mxq.mxq_quantize_jagged_colwise_ws, cargs + (d_ws.data_ptr(), nws),
                     3 * R2 * C2 + 4 * G * C2, R2 * C2, (("q2", q2), ("s2", s2)))
     else:
         # two launches: jagged_colwise_tile_clear_kernel zeroes the long
         # groups' scale slots, then the tile kernel exchanges maxima through them
-        l2 = Launch("jagged_colwise x (16384,4096), clear + tile", "jagged_colwise_tile_kernel<2>",
+        l2 = Launch("jagged_colwise x (16384,4096), clear + tile", tile_kernel,
                     mxq.mxq_quantize_jagged_colwise, cargs,
                     3 * R2 * C2 + 4 * G * C2, R2 * C2, (("q2", q2), ("s2", s2)))
     desc = {"workload": "moe_bwd_jagged" + ("_g256" if fine else "") + ("_ws" if ws else ""),

@@ -216,7 +216,7 @@ bool colwise_in_slots(int64_t ext, int64_t ncols, int64_t G, int64_t ss_g, int64
            distinct_scale_slots(G, ncols, ss_g, ss_c);
 }
 
-// The colwise tile kernel: chunks of kTileT 128-row tiles x 256 columns.
+// The colwise tile kernel: chunks of T 128-row tiles x 256 columns.
 // It takes the column-major colwise calls with at most kTileMaxGroups groups,
 // at most kSlotMaxChunks chunks per group (so any offsets keep every exchange
 // set within a block of resident workgroups) and groups of at most
@@ -224,30 +224,43 @@ bool colwise_in_slots(int64_t ext, int64_t ncols, int64_t G, int64_t ss_g, int64
 // and the split kernel's 1536-row chunks are faster there (x (16384, 4096),
 // cold, with / without a workspace: one group 57 / 69 us against 67 / 83,
 // groups of 4096 and 12288 rows 59 / 64 against 57 / 72; eight MoE groups
-// 51 / 61 against 58 / 63).
-constexpr int kTileT = 2;
-constexpr int64_t kTileChunkRows = 128 * kTileT;
+// 51 / 61 against 58 / 63).  Chunks are two tiles (168 VGPRs, three waves
+// per SIMD), or one tile (102 VGPRs, four waves) for groups of at most
+// kTileShortAvgRows rows on average: 256 fine-grained MoE groups (64 rows
+// on average) 55.5 against 60 us with a workspace, while the 8 MoE groups
+// take 63 against 51 us and 64 groups of 256 rows 44 against 41.
 constexpr int64_t kTileMaxAvgRows = 4096;
+constexpr int64_t kTileShortAvgRows = 128;
 
-bool tile_applies(int64_t ext, int64_t G)
+// tiles per chunk for these extents, 0 when the tile kernel does not apply
+int tile_t(int64_t ext, int64_t G)
 {
-    return G <= kTileMaxGroups && ext <= kSlotMaxChunks * kTileChunkRows && ext <= kTileMaxAvgRows * G;
+    if (G > kTileMaxGroups)
+        return 0;
+    if (ext <= kTileShortAvgRows * G && ext <= kSlotMaxChunks * 128)
+        return 1;
+    if (ext <= kTileMaxAvgRows * G && ext <= kSlotMaxChunks * 256)
+        return 2;
+    return 0;
 }
+
+bool tile_applies(int64_t ext, int64_t G) { return tile_t(ext, G) != 0; }
 
 // Grid and workspace of the tile kernel.  Every group has
 // max(1, ceil(n / CH)) chunks per column tile, at most G + ext / CH in all;
 // a group of more than one chunk has more than CH rows, so there are at most
 // min(G, ext / (CH + 1)) of them, one workspace set per column tile each.
 struct TilePlan {
-    int64_t tiles_c, nblocks, ws_bytes;
+    int64_t t, ch, tiles_c, nblocks, ws_bytes;
 };
 TilePlan tile_plan(int64_t ext, int64_t ncols, int64_t G)
 {
     TilePlan p;
+    p.t = tile_t(ext, G);
+    p.ch = 128 * p.t;
     p.tiles_c = (ncols + 255) / 256;
-    p.nblocks = p.tiles_c * (G + ext / kTileChunkRows);
-    p.ws_bytes = std::min<int64_t>(G, ext / (kTileChunkRows + 1)) * p.tiles_c * kTileSetWords *
-                 (int64_t)sizeof(uint32_t);
+    p.nblocks = p.tiles_c * (G + ext / p.ch);
+    p.ws_bytes = std::min<int64_t>(G, ext / (p.ch + 1)) * p.tiles_c * kTileSetWords * (int64_t)sizeof(uint32_t);
     return p;
 }
 
@@ -270,17 +283,22 @@ mxq_status run_jagged_colwise_tile(const uint16_t *x, int64_t ext, int64_t ncols
     if (ncols % 8 != 0 || ncols > INT32_MAX)
         return MXQ_ERR_INVALID_ARG;
     const TilePlan p = tile_plan(ext, ncols, G);
-    if (p.nblocks > INT32_MAX)
+    if (p.t == 0 || p.nblocks > INT32_MAX)
         return MXQ_ERR_INVALID_ARG;
     if (ws && ws_bytes < p.ws_bytes)
         return MXQ_ERR_WORKSPACE;
     if (!ws) {
         const dim3 cgrid((unsigned)std::min<int64_t>((ncols + 255) / 256, 64), (unsigned)G);
         jagged_colwise_tile_clear_kernel<<<cgrid, dim3(256), 0, st>>>(offs, G, (int)ext, (int)ncols, scales,
-                                                                      ss_g, ss_c, (int)kTileChunkRows);
+                                                                      ss_g, ss_c, (int)p.ch);
     }
-    jagged_colwise_tile_kernel<kTileT><<<dim3((unsigned)p.nblocks), dim3(256), 0, st>>>(
-        x, ldx, (int)ext, (int)ncols, offs, G, q, ldq, scales, ss_g, ss_c, (int)p.tiles_c, ws, spin_limit);
+    const dim3 grid((unsigned)p.nblocks), block(256);
+    if (p.t == 1)
+        jagged_colwise_tile_kernel<1><<<grid, block, 0, st>>>(x, ldx, (int)ext, (int)ncols, offs, G, q, ldq, scales,
+                                                              ss_g, ss_c, (int)p.tiles_c, ws, spin_limit);
+    else
+        jagged_colwise_tile_kernel<2><<<grid, block, 0, st>>>(x, ldx, (int)ext, (int)ncols, offs, G, q, ldq, scales,
+                                                              ss_g, ss_c, (int)p.tiles_c, ws, spin_limit);
     return launch_status();
 }
 

@@ -10,11 +10,12 @@ holds one set per item number.  Items are counted here the way the kernel
 forms them; a bound that fell short would leave items without a workgroup
 (their bytes and scales unwritten).
 
-The tile kernel (chunks of 256 rows x 256 columns, at most 256 groups,
-65,280 rows and 4096 rows per group on average) gives every group
-max(1, ceil(n / 256)) chunks per column tile, at most G + ext // 256 in all,
-and needs one workspace set per group of more than 256 rows and column tile,
-at most min(G, ext // 257) groups; checked the same way."""
+The tile kernel (at most 256 groups; chunks of 128 rows x 256 columns for
+groups of at most 128 rows on average and at most 32,640 rows, else of 256
+rows for at most 4096 rows per group on average and 65,280 rows) gives every
+group max(1, ceil(n / CH)) chunks per column tile, at most G + ext // CH in
+all, and needs one workspace set per group of more than CH rows and column
+tile, at most min(G, ext // (CH + 1)) groups; checked the same way."""
 import numpy as np
 import pytest
 
@@ -75,30 +76,36 @@ def test_split_chunks_fit_their_rows():
         assert (nc - 1) * csz < span          # the last chunk holds rows
 
 
-TILE_CH = 256
+def tile_rows(ext, G):
+    """Rows per chunk of the tile kernel for these extents, 0 if it does not
+    apply."""
+    if G > 256:
+        return 0
+    if ext <= 128 * G and ext <= 255 * 128:
+        return 128
+    if ext <= 4096 * G and ext <= 255 * 256:
+        return 256
+    return 0
 
 
-def tile_applies(ext, G):
-    return G <= 256 and ext <= 255 * TILE_CH and ext <= 4096 * G
-
-
-def tile_counts(offs, ext):
-    """(chunks, groups of more than one chunk) by the tile kernel's rules:
-    clamped ends, an empty group keeps one chunk."""
+def tile_counts(offs, ext, ch):
+    """(chunks, groups of more than one chunk, most chunks of a group) by the
+    tile kernel's rules: clamped ends, an empty group keeps one chunk."""
     ends = np.clip(np.asarray(offs, dtype=np.int64), 0, ext)
     los = np.concatenate([[0], ends[:-1]])
     n = np.maximum(ends - los, 0)
-    chunks = np.where(n > TILE_CH, (n + TILE_CH - 1) // TILE_CH, 1)
-    return int(chunks.sum()), int((n > TILE_CH).sum()), int(chunks.max(initial=1))
+    chunks = np.where(n > ch, (n + ch - 1) // ch, 1)
+    return int(chunks.sum()), int((n > ch).sum()), int(chunks.max(initial=1))
 
 
 def check_tile(offs, ext):
     G = len(offs)
-    chunks, nlong, most = tile_counts(offs, ext)
-    assert chunks <= G + ext // TILE_CH
-    assert nlong <= min(G, ext // (TILE_CH + 1))
-    if tile_applies(ext, G):
-        assert most <= 255
+    for ch in (128, 256):
+        chunks, nlong, most = tile_counts(offs, ext, ch)
+        assert chunks <= G + ext // ch
+        assert nlong <= min(G, ext // (ch + 1))
+        if tile_rows(ext, G) == ch:
+            assert most <= 255
 
 
 def test_library_agrees_on_the_workspace_size():
@@ -108,10 +115,12 @@ def test_library_agrees_on_the_workspace_size():
     except _capi.LibraryMissing:
         pytest.skip("library not built")
     cases = ((16384, 4096, 8), (1000, 64, 1), (65536, 8, 256), (0, 8, 3), (65280, 264, 16),
-             (65281, 264, 16), (16384, 4096, 2), (16384, 4100, 4))
+             (65281, 264, 16), (16384, 4096, 2), (16384, 4100, 4), (16384, 4096, 256),
+             (32640, 264, 256), (32641, 264, 256))
     for ext, cols, G in cases:
-        if tile_applies(ext, G):
-            want = min(G, ext // (TILE_CH + 1)) * (-(-cols // 256)) * 264 * 4
+        ch = tile_rows(ext, G)
+        if ch:
+            want = min(G, ext // (ch + 1)) * (-(-cols // 256)) * 264 * 4
         else:
             want = bound(ext, G, True) * (-(-cols // 64)) * 72 * 4
         assert lib.mxq_jagged_colwise_workspace_bytes(ext, cols, G) == want, (ext, cols, G)

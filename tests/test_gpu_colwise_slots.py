@@ -1,8 +1,8 @@
 """GPU parity of the jagged colwise call WITHOUT a workspace on long token
 groups: chunks of one long group exchange their column maxima through the
 group's own fp32 scale slots (cleared by a small kernel first), so no row is
-read twice.  Up to 65,280 rows the call runs the tile kernel (chunks of 256
-rows x 256 columns, at most 255 per group); longer extents run the split
+read twice.  Up to 65,280 rows the call runs the tile kernel (chunks of 128
+or 256 rows x 256 columns, at most 255 per group); longer extents run the split
 kernel (chunks of 1536 rows x 64 columns, at most 255 per group).  Byte for
 byte against the oracle: one group of every row, groups at and past chunk
 multiples, starts off 16-row boundaries, empty groups, rows past the last
@@ -132,6 +132,16 @@ def test_tile_kernel_most_chunks(extra):
     rows = MAX_CHUNKS * TILE_CHUNK + extra
     bits = adversarial((rows, 264), 5450 + extra)
     check(bits, np.array([0] * 15 + [rows], np.int32), what=f"{rows} rows")
+
+
+@pytest.mark.parametrize("extra", [0, 1])
+def test_tile_kernel_one_tile_chunks_most(extra):
+    """255 chunks of 128 rows in one group after 255 empty groups (groups of
+    at most 128 rows on average take one-tile chunks), and one row more,
+    where the call takes two-tile chunks instead."""
+    rows = MAX_CHUNKS * 128 + extra
+    bits = adversarial((rows, 264), 5460 + extra)
+    check(bits, np.array([0] * 255 + [rows], np.int32), what=f"{rows} rows")
 
 
 def test_previous_scales_in_the_slots():

@@ -77,6 +77,8 @@ def test_random_groups(rows, cols, G, mult, tail, seed):
 
 
 @pytest.mark.parametrize("rows,ends", [
+    (32640, [0] * 255 + [32640]),     # 255 one-tile chunks of 128 rows (short groups on average)
+    (32641, [0] * 255 + [32641]),     # one row more: two-tile chunks
     (65280, [0] * 15 + [65280]),      # the tile kernel's limit: 255 chunks of 256 rows
     (65281, [0] * 15 + [65281]),      # past it: the split kernel with the workspace
     (70000, [100, 69000, 70000]),     # long groups: the split kernel
