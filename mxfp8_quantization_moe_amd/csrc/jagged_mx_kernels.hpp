@@ -392,22 +392,51 @@ __global__ __launch_bounds__(kJmxThreads) void jagged_mx_colwise_kernel(
     const int tc = (int)(blockIdx.x % (unsigned)tiles_c);
     const int tid = (int)(blockIdx.x / (unsigned)tiles_c);
 
+    // this workgroup's group g (tile tid of the tile count), its first tile
+    // pt_g and first 32-row block pb_g, and its rows [lo, hi)
+    int g, pt_g, pb_g, lo, hi;
     if (G <= 64) {
-        if (t < 64)
-            wave_group_tables<7, 5>(offs, G, rows, s_end, s_pt, s_pb);
-        __syncthreads();
+        // every wave builds the table in registers (lane l holds group l)
+        // and finds g by a ballot: no barrier and no LDS round trip before
+        // the loads
+        const bool valid = lane < G;
+        int e = valid ? offs[lane] : rows;
+        e = e < 0 ? 0 : (e > rows ? rows : e);
+        int el = __shfl_up(e, 1, 64);
+        el = lane == 0 ? 0 : el;
+        const int n = valid && e > el ? e - el : 0;
+        const int ut = units_of<7>(n), ub = units_of<5>(n);
+        int it = ut, ib = ub;   // inclusive prefixes
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int yt = __shfl_up(it, d, 64);
+            const int yb = __shfl_up(ib, d, 64);
+            if (lane >= d) {
+                it += yt;
+                ib += yb;
+            }
+        }
+        if (tid >= __builtin_amdgcn_readlane(it, 63))
+            return;
+        g = (int)__popcll(__ballot(it <= tid));   // groups whose tiles all precede tile tid
+        pt_g = __builtin_amdgcn_readlane(it - ut, g);
+        pb_g = __builtin_amdgcn_readlane(ib - ub, g);
+        lo = __builtin_amdgcn_readlane(el, g);
+        hi = __builtin_amdgcn_readlane(e, g);
     } else {
         load_group_ends<kJmxThreads>(offs, G, rows, s_end);
         slot_prefix2<kJmxThreads>(G, s_pt, s_pb,
                                   [&](int gg) { return units_of<7>(group_len(s_end, gg)); },
                                   [&](int gg) { return units_of<5>(group_len(s_end, gg)); });
+        if (tid >= s_pt[G])
+            return;
+        g = find_slot(s_pt, G, tid);
+        pt_g = s_pt[g];
+        pb_g = s_pb[g];
+        lo = g ? s_end[g - 1] : 0;
+        hi = s_end[g];
     }
-    if (tid >= s_pt[G])
-        return;
-    const int g = find_slot(s_pt, G, tid);
-    const int lo = g ? s_end[g - 1] : 0;
-    const int hi = s_end[g];
-    const int k = tid - s_pt[g];
+    const int k = tid - pt_g;
     const int rt = lo + 128 * k;          // first row of this tile
     const int rb = rt + 16 * qd;          // first row of this lane
     const int c0 = tc * 256 + 64 * w + 8 * cg;
@@ -449,7 +478,7 @@ __global__ __launch_bounds__(kJmxThreads) void jagged_mx_colwise_kernel(
         return;
     if ((qd & 1) == 0) {
         // this lane starts a block (rt + 32*(qd/2) < hi, since rb < hi)
-        const int64_t jb = (int64_t)s_pb[g] + 4 * k + (qd >> 1);
+        const int64_t jb = (int64_t)pb_g + 4 * k + (qd >> 1);
         uint8_t *sp = scales + jb * ss_b + (int64_t)c0 * ss_c;
         if (ss_c == 1 && ((reinterpret_cast<uintptr_t>(sp) & 7u) == 0)) {
             uint2 pk;
