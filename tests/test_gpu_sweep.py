@@ -2,7 +2,8 @@
 for byte: many small configurations drawn from a fixed seed (extents not
 multiples of anything the kernels tile by, 1 to 100 groups with empty groups
 and short tails, group starts on and off 8/16/32-element boundaries, both
-scale modes, every layout with a kernel), adversarial bf16 values; bytes
+scale modes, every layout with a kernel, the colwise call with and without
+a workspace), adversarial bf16 values; bytes
 past the last group keep the canary.  It adds breadth to the hand-picked
 cases of the other parity tests."""
 import numpy as np
@@ -10,9 +11,9 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import (CANARY, DEV, adversarial, assert_same_bytes, bf16_dev, blockwise, i32_dev,
-                         jagged_colwise, jagged_mx_colwise, jagged_mx_rowwise, jagged_rowwise,
-                         mx_3d_colwise, mx_rowwise, random_offsets, relayout)
+from gpu_helpers import (CANARY, DEV, adversarial, assert_same_bytes, bf16_dev, blockwise, colwise_workspace,
+                         i32_dev, jagged_colwise, jagged_colwise_ws, jagged_mx_colwise, jagged_mx_rowwise,
+                         jagged_rowwise, mx_3d_colwise, mx_rowwise, random_offsets, relayout)
 import workloads
 
 pytestmark = pytest.mark.gpu
@@ -48,6 +49,12 @@ def test_jagged_fp32(k):
     oq, os_ = oracle.quantize_jagged_colwise(bits, offs, canary=CANARY)
     assert_same_bytes(q, oq, f"colwise case {k} q")
     assert_same_bytes(s, os_, f"colwise case {k} scales")
+    # the same operand through the call with a workspace
+    ws = colwise_workspace(rows, cols, len(offs))
+    q, s = jagged_colwise_ws(bf16_dev(bits), i32_dev(offs), ws)
+    assert_same_bytes(q, oq, f"colwise (workspace) case {k} q")
+    assert_same_bytes(s, os_, f"colwise (workspace) case {k} scales")
+    assert int(torch.count_nonzero(ws)) == 0, f"case {k}: workspace not left zero-filled"
 
 
 @pytest.mark.parametrize("k", range(N_CASES))
