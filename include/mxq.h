@@ -124,7 +124,8 @@ mxq_status mxq_quantize_jagged_rowwise(const uint16_t *x, int64_t rows, int64_t 
  * Row-major in, with num_groups <= 256 and distinct scale slots: token
  * groups longer than the rows one workgroup holds are cut into chunks that
  * exchange each column's maximum through the group's own scale slots, so
- * every element is read once.  Chunks are 256 rows x 256 columns when
+ * every element is read once.  Chunks are 128 rows x 256 columns when
+ * rows <= 32,640 and rows <= 128 * num_groups, 256 rows x 256 columns when
  * rows <= 65,280 and rows <= 4096 * num_groups, else 1536 rows x 64 columns
  * when rows <= 391,680.  Two kernels run in stream order: one zeroes those
  * slots, the second quantizes; while it runs the slots hold intermediate
@@ -144,7 +145,8 @@ mxq_status mxq_quantize_jagged_colwise(const uint16_t *x, int64_t rows, int64_t 
  * columns on a few of them.
  *
  * For a row-major x and column-major q, token groups longer than the rows one
- * workgroup holds are cut into chunks (as above: 256 x 256 or 1536 x 64)
+ * workgroup holds are cut into chunks (as above: 128 or 256 x 256, or
+ * 1536 x 64)
  * quantized by separate workgroups, which exchange their column maxima
  * through the workspace, so every element is read from memory once, in one
  * launch, for up to 256 groups (the call without a workspace needs a second,
