@@ -232,35 +232,41 @@ bool colwise_in_slots(int64_t ext, int64_t ncols, int64_t G, int64_t ss_g, int64
 constexpr int64_t kTileMaxAvgRows = 4096;
 constexpr int64_t kTileShortAvgRows = 128;
 
-// tiles per chunk for these extents, 0 when the tile kernel does not apply
+// tiles per chunk for these extents, 0 when the tile kernel does not apply.
+// A group's chunks cover its rows from its start rounded down to 16 rows,
+// at most ext + 15 rows, so every group has at most kSlotMaxChunks chunks
+// when ext + 15 <= kSlotMaxChunks * CH.
 int tile_t(int64_t ext, int64_t G)
 {
     if (G > kTileMaxGroups)
         return 0;
-    if (ext <= kTileShortAvgRows * G && ext <= kSlotMaxChunks * 128)
+    if (ext <= kTileShortAvgRows * G && ext + 15 <= kSlotMaxChunks * 128)
         return 1;
-    if (ext <= kTileMaxAvgRows * G && ext <= kSlotMaxChunks * 256)
+    if (ext <= kTileMaxAvgRows * G && ext + 15 <= kSlotMaxChunks * 256)
         return 2;
     return 0;
 }
 
 bool tile_applies(int64_t ext, int64_t G) { return tile_t(ext, G) != 0; }
 
-// Grid and workspace of the tile kernel.  Every group has
-// max(1, ceil(n / CH)) chunks per column tile, at most G + ext / CH in all;
-// a group of more than one chunk has more than CH rows, so there are at most
-// min(G, ext / (CH + 1)) of them, one workspace set per column tile each.
+// Grid and workspace of the tile kernel.  A group of n > 0 rows spans
+// s <= n + 15 rows from its 16-row-aligned start and has max(1, ceil(s / CH))
+// <= 1 + (s - 1) / CH chunks per column tile, an empty group one, so there
+// are at most G + (ext + 14 G) / CH in all; a group of more than one chunk
+// spans more than CH rows, i.e. has more than CH - 15, so there are at most
+// min(G, ext / (CH - 14)) of them, one workspace set per column tile each.
 struct TilePlan {
-    int64_t t, ch, tiles_c, nblocks, ws_bytes;
+    int64_t t, ch, tiles_c, nblocks, nsets, ws_bytes;
 };
 TilePlan tile_plan(int64_t ext, int64_t ncols, int64_t G)
 {
     TilePlan p;
     p.t = tile_t(ext, G);
-    p.ch = 128 * p.t;
+    p.ch = 128 * (p.t ? p.t : 1);
     p.tiles_c = (ncols + 255) / 256;
-    p.nblocks = p.tiles_c * (G + ext / p.ch);
-    p.ws_bytes = std::min<int64_t>(G, ext / (p.ch + 1)) * p.tiles_c * kTileSetWords * (int64_t)sizeof(uint32_t);
+    p.nblocks = p.tiles_c * (G + (ext + 14 * G) / p.ch);
+    p.nsets = std::min<int64_t>(G, ext / (p.ch - 14));
+    p.ws_bytes = p.nsets * p.tiles_c * kTileSetWords * (int64_t)sizeof(uint32_t);
     return p;
 }
 
@@ -292,13 +298,18 @@ mxq_status run_jagged_colwise_tile(const uint16_t *x, int64_t ext, int64_t ncols
         jagged_colwise_tile_clear_kernel<<<cgrid, dim3(256), 0, st>>>(offs, G, (int)ext, (int)ncols, scales,
                                                                       ss_g, ss_c, (int)p.ch);
     }
+    // sets per column tile the workspace holds (the plan's count or more)
+    const int64_t nsets =
+        ws ? std::min<int64_t>(ws_bytes / (p.tiles_c * kTileSetWords * (int64_t)sizeof(uint32_t)), INT32_MAX) : 0;
     const dim3 grid((unsigned)p.nblocks), block(256);
     if (p.t == 1)
         jagged_colwise_tile_kernel<1><<<grid, block, 0, st>>>(x, ldx, (int)ext, (int)ncols, offs, G, q, ldq, scales,
-                                                              ss_g, ss_c, (int)p.tiles_c, ws, spin_limit);
+                                                              ss_g, ss_c, (int)p.tiles_c, ws, (int)nsets,
+                                                              spin_limit);
     else
         jagged_colwise_tile_kernel<2><<<grid, block, 0, st>>>(x, ldx, (int)ext, (int)ncols, offs, G, q, ldq, scales,
-                                                              ss_g, ss_c, (int)p.tiles_c, ws, spin_limit);
+                                                              ss_g, ss_c, (int)p.tiles_c, ws, (int)nsets,
+                                                              spin_limit);
     return launch_status();
 }
 

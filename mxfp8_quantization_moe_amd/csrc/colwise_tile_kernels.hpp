@@ -7,8 +7,10 @@
 //
 // A workgroup of four waves side by side covers 256 columns (512 bytes of
 // every row it reads) and a chunk of T 128-row tiles of one group, anchored
-// at the group start; a lane holds 16 rows x 8 columns per tile, in
-// registers, so every element is read from HBM once.  A group longer than
+// at the group start rounded down to 16 rows (the scales are per group, so
+// any tiling will do, and 16-row pieces make whole 16-byte column stores); a
+// lane holds 16 rows x 8 columns per tile, in registers, so every element is
+// read from HBM once.  A group longer than
 // one chunk is cut into nu chunks per 256-column tile; the chunks of one
 // (group, column tile) exchange their 256 column maxima, either through a
 // set of words in a caller's workspace or through the group's own fp32
@@ -53,12 +55,15 @@ constexpr int kTileSetDepart = 257;
 // workgroups, fewer than are resident at once (three per CU).
 constexpr int kTileSpan = 512;
 
-// chunks of ch rows in a group of n rows (an empty group has one)
-__device__ __forceinline__ int tile_chunks(int n, int ch) { return n > ch ? (n + ch - 1) / ch : 1; }
+// The rows a group's chunks cover: from its start rounded down to 16 rows to
+// its end (0 for an empty group), and the chunks of ch rows over them (an
+// empty group has one).
+__device__ __forceinline__ int tile_span(int lo, int hi) { return hi > lo ? hi - (lo & ~15) : 0; }
+__device__ __forceinline__ int tile_chunks(int span, int ch) { return span > ch ? (span + ch - 1) / ch : 1; }
 
 // Zeroes the scale slots the workspace-free exchange runs in: every column
-// of each group longer than one chunk of ch rows (clamped ends as in the
-// main kernel).  Grid (column blocks, G); 256 threads.
+// of each group whose span (tile_span) exceeds one chunk of ch rows (clamped
+// ends as in the main kernel).  Grid (column blocks, G); 256 threads.
 __global__ __launch_bounds__(256) void jagged_colwise_tile_clear_kernel(
     const int32_t *__restrict__ offs, int G, int rows, int cols, float *__restrict__ scales,
     int64_t ss_g, int64_t ss_c, int ch)
@@ -67,7 +72,7 @@ __global__ __launch_bounds__(256) void jagged_colwise_tile_clear_kernel(
     auto clamp_end = [&](int e) { return e < 0 ? 0 : (e > rows ? rows : e); };
     const int lo = g ? clamp_end(offs[g - 1]) : 0;
     const int hi = clamp_end(offs[g]);
-    if (hi - lo <= ch)
+    if (tile_span(lo, hi) <= ch)
         return;
     for (int c = blockIdx.x * 256 + threadIdx.x; c < cols; c += gridDim.x * 256)
         scales[(int64_t)g * ss_g + (int64_t)c * ss_c] = 0.0f;
@@ -78,14 +83,17 @@ __global__ __launch_bounds__(256) void jagged_colwise_tile_clear_kernel(
 // cols a multiple of 8, tiles_c = ceil(cols / 256); grid at least
 // tiles_c * (G + rows / (128 T)) workgroups of 256 threads (spare ones exit).
 // ws: the workspace sets (null: exchange in the scale slots, which the
-// clear kernel has zeroed; then at most kSlotMaxChunks chunks per group).
+// clear kernel has zeroed; then at most kSlotMaxChunks chunks per group),
+// nsets of them per column tile (offsets that break their precondition can
+// make more long groups than the host's bound: those chunks take the
+// fallback instead of writing past the workspace).
 // spin_limit: polls before the fallback (negative: fall back at once).
 template <int T>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void jagged_colwise_tile_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int rows, int cols,
     const int32_t *__restrict__ offs, int G, uint8_t *__restrict__ q, int64_t ldq,
     float *__restrict__ scales, int64_t ss_g, int64_t ss_c, int tiles_c, uint32_t *__restrict__ ws,
-    int spin_limit)
+    int nsets, int spin_limit)
 {
     constexpr int CH = 128 * T;   // rows per chunk
     __shared__ int s_end[kTileMaxGroups];
@@ -114,9 +122,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void j
         e = e < 0 ? 0 : (e > rows ? rows : e);
         int el = __shfl_up(e, 1, 64);
         el = lane == 0 ? 0 : el;
-        const int n = e > el ? e - el : 0;
-        const int cu = valid ? tile_chunks(n, CH) : 0;
-        const int lg = valid && n > CH ? 1 : 0;
+        const int sp = tile_span(el, e);
+        const int cu = valid ? tile_chunks(sp, CH) : 0;
+        const int lg = valid && sp > CH ? 1 : 0;
         int iu = cu, il = lg;   // inclusive prefixes
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
@@ -138,8 +146,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void j
     } else {
         load_group_ends<256>(offs, G, rows, s_end);
         slot_prefix2<256>(
-            G, s_pu, s_pl, [&](int gg) { return tile_chunks(group_len(s_end, gg), CH); },
-            [&](int gg) { return group_len(s_end, gg) > CH ? 1 : 0; });
+            G, s_pu, s_pl, [&](int gg) { return tile_chunks(tile_span(gg ? s_end[gg - 1] : 0, s_end[gg]), CH); },
+            [&](int gg) { return tile_span(gg ? s_end[gg - 1] : 0, s_end[gg]) > CH ? 1 : 0; });
         if (j >= s_pu[G])
             return;
         g = find_slot(s_pu, G, j);
@@ -160,22 +168,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void j
     const int rr = local - blk * nu * B;
     const int k = rr / wb;
     const int tc = blk * B + (rr - k * wb);
-    const int rt = lo + k * CH;              // first row of this chunk
+    const int rt = (lo & ~15) + k * CH;      // first row of this chunk
     const int c0 = tc * 256 + 64 * w + 8 * cg;
     const bool col_ok = c0 < cols;
     const int cl = col_ok ? c0 : 0;
 
-    // loads: 16 rows x 8 columns per lane and tile; rows past the group end
-    // read row hi - 1 (same group, so the maxima are unchanged); tiles wholly
-    // past it are not read
+    // loads: 16 rows x 8 columns per lane and tile; rows before the group
+    // start read row lo, rows past its end row hi - 1 (same group, so the
+    // maxima are unchanged); tiles wholly past the end, and every tile of an
+    // empty group (whose rounded-down start lies below its end), are not read
     uint4 v[T][16];
 #pragma unroll
     for (int tt = 0; tt < T; ++tt) {
         const int rb = rt + 128 * tt + 16 * qd;
-        if (rt + 128 * tt < hi) {
+        if (hi > lo && rt + 128 * tt < hi) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int r = rb + i < hi ? rb + i : hi - 1;
+                const int r = rb + i < lo ? lo : (rb + i < hi ? rb + i : hi - 1);
                 v[tt][i] = ld16_nt(x + (int64_t)r * ldx + cl);
             }
         } else {
@@ -224,54 +233,63 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void j
         // outstanding global operations, only the use of their results does,
         // so this is what orders one thread's atomics before another
         // thread's arrival or departure.
-        uint32_t *const set = ws ? ws + ((int64_t)pl_g * tiles_c + tc) * kTileSetWords : nullptr;
+        const bool in_ws = ws != nullptr && pl_g < nsets;
+        uint32_t *const set = in_ws ? ws + ((int64_t)pl_g * tiles_c + tc) * kTileSetWords : nullptr;
         bool done = true;   // (thread t alone uses s_col[t] until the fallback)
-        // A chunk raises a shared maximum only when its own is larger than
-        // the value it reads first: the chunks of a set arrive together, and
-        // one atomic per chunk and word would queue on the same words.
-        uint32_t *const word = in_slots ? slot : set + t;
-        uint32_t cur = 0u;
-        if (has_col) {
-            cur = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (in_slots && t == 0) {
-                // the control word (the tile's first column): raise its
-                // maximum bits by compare-and-swap, leaving the counts
-                while ((cur & kSlotMax) < acol &&
-                       !__hip_atomic_compare_exchange_strong(word, &cur, (cur & ~kSlotMax) | acol,
-                                                             __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                             __HIP_MEMORY_SCOPE_AGENT)) {
-                }
-            } else if ((cur & kSlotMax) < acol) {
-                cur = __hip_atomic_fetch_max(word, acol, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        s_col[t] = umax(acol, cur & kSlotMax);
-        __syncthreads();   // all of this workgroup's maxima are in
+        // the exchange runs in the scale slots or in a workspace set; a chunk
+        // whose set lies past the workspace reduces its group's rows itself
+        const bool exch = in_slots || in_ws;
         uint32_t *const count = in_slots ? reinterpret_cast<uint32_t *>(scales + (int64_t)g * ss_g +
                                                                         (int64_t)(tc * 256) * ss_c)
-                                         : set + kTileSetArrive;
-        const uint32_t one = in_slots ? kSlotArrive : 1u;
-        if (t == 0) {
-            // arrive, then poll until every chunk has; a negative limit takes
-            // the fallback without looking, 0 looks once
-            uint32_t c = __hip_atomic_fetch_add(count, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + one;
-            auto arrived = [&](uint32_t v) {
-                return (in_slots ? slot_arrivals(v) : v) >= (uint32_t)nu;
-            };
-            bool all = spin_limit >= 0 && arrived(c);
-            for (int n = 0; !all && spin_limit >= 0 && n < spin_limit; ++n) {
-                __builtin_amdgcn_s_sleep(2);
-                all = arrived(__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                                         : (in_ws ? set + kTileSetArrive : nullptr);
+        if (exch) {
+            // A chunk raises a shared maximum only when its own is larger than
+            // the value it reads first: the chunks of a set arrive together, and
+            // one atomic per chunk and word would queue on the same words.
+            uint32_t *const word = in_slots ? slot : set + t;
+            uint32_t cur = 0u;
+            if (has_col) {
+                cur = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (in_slots && t == 0) {
+                    // the control word (the tile's first column): raise its
+                    // maximum bits by compare-and-swap, leaving the counts
+                    while ((cur & kSlotMax) < acol &&
+                           !__hip_atomic_compare_exchange_strong(word, &cur, (cur & ~kSlotMax) | acol,
+                                                                 __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                                 __HIP_MEMORY_SCOPE_AGENT)) {
+                    }
+                } else if ((cur & kSlotMax) < acol) {
+                    cur = __hip_atomic_fetch_max(word, acol, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
-            s_flag = all ? 1 : 0;
+            s_col[t] = umax(acol, cur & kSlotMax);
+            __syncthreads();   // all of this workgroup's maxima are in
+            const uint32_t one = in_slots ? kSlotArrive : 1u;
+            if (t == 0) {
+                // arrive, then poll until every chunk has; a negative limit takes
+                // the fallback without looking, 0 looks once
+                uint32_t c = __hip_atomic_fetch_add(count, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + one;
+                auto arrived = [&](uint32_t v) {
+                    return (in_slots ? slot_arrivals(v) : v) >= (uint32_t)nu;
+                };
+                bool all = spin_limit >= 0 && arrived(c);
+                for (int n = 0; !all && spin_limit >= 0 && n < spin_limit; ++n) {
+                    __builtin_amdgcn_s_sleep(2);
+                    all = arrived(__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                }
+                s_flag = all ? 1 : 0;
+            }
+            __syncthreads();
+            done = s_flag != 0;
+            if (done && has_col)
+                s_col[t] = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kSlotMax;
+        } else {
+            done = false;
         }
-        __syncthreads();
-        done = s_flag != 0;
-        if (done && has_col)
-            s_col[t] = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kSlotMax;
         if (!done) {
-            // the other chunks did not arrive in time: reduce every row of the
-            // group in this column tile here (32 lanes per row, 16 bytes each)
+            // no exchange, or the other chunks did not arrive in time: reduce
+            // every row of the group in this column tile here (32 lanes per
+            // row, 16 bytes each)
             __syncthreads();
             s_col[t] = 0u;
             __syncthreads();
@@ -295,7 +313,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void j
         }
         __syncthreads();   // every read of the set or slots has returned
         acol = s_col[t];
-        if (t == 0) {
+        if (exch && t == 0) {
             const uint32_t dep = in_slots ? kSlotDepart : 1u;
             uint32_t *const dcount = in_slots ? count : set + kTileSetDepart;
             const uint32_t prev =
@@ -303,7 +321,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void j
             s_flag = (in_slots ? prev >> 24 : prev) == (uint32_t)nu - 1 ? 2 : 0;
         }
         __syncthreads();
-        last_out = s_flag == 2;
+        last_out = exch && s_flag == 2;
         if (last_out && !in_slots) {
             // the set is zero again for the next call
             __hip_atomic_store(set + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -333,8 +351,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void j
 #pragma unroll
     for (int tt = 0; tt < T; ++tt) {
         const int rb = rt + 128 * tt + 16 * qd;
-        if (rb < hi)
-            store_tile_columns<false>(v[tt], sc, q, ldq, c0, rb, hi, qd);
+        if (hi <= lo || rb >= hi)
+            continue;
+        // the lane's 16 rows of each column as one 16-byte piece of the column
+        // run; the group's first and last pieces hold only the rows in
+        // [lo, hi), written as aligned parts
+        const int from = lo > rb ? lo - rb : 0, to = hi - rb < 16 ? hi - rb : 16;
+        uint8_t *qp = q + (int64_t)c0 * ldq + rb;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            const uint4 o = tile_column_bytes<false>(v[tt], jj, sc[jj]);
+            if (from == 0 && to == 16)
+                st16(qp + (int64_t)jj * ldq, o);
+            else
+                put16_range(qp + (int64_t)jj * ldq, o, from, to);
+        }
     }
 }
 

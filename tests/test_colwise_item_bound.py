@@ -11,11 +11,13 @@ forms them; a bound that fell short would leave items without a workgroup
 (their bytes and scales unwritten).
 
 The tile kernel (at most 256 groups; chunks of 128 rows x 256 columns for
-groups of at most 128 rows on average and at most 32,640 rows, else of 256
-rows for at most 4096 rows per group on average and 65,280 rows) gives every
-group max(1, ceil(n / CH)) chunks per column tile, at most G + ext // CH in
-all, and needs one workspace set per group of more than CH rows and column
-tile, at most min(G, ext // (CH + 1)) groups; checked the same way."""
+groups of at most 128 rows on average and ext + 15 <= 255 * 128, else of 256
+rows for at most 4096 rows per group on average and ext + 15 <= 255 * 256)
+covers each group from its start rounded down to 16 rows: a group spanning
+s rows that way has max(1, ceil(s / CH)) chunks per column tile, at most
+G + (ext + 14 G) // CH in all, at most 255 each, and needs one workspace set
+per column tile for every group spanning more than CH rows, at most
+min(G, ext // (CH - 14)) groups; checked the same way."""
 import numpy as np
 import pytest
 
@@ -81,9 +83,9 @@ def tile_rows(ext, G):
     apply."""
     if G > 256:
         return 0
-    if ext <= 128 * G and ext <= 255 * 128:
+    if ext <= 128 * G and ext + 15 <= 255 * 128:
         return 128
-    if ext <= 4096 * G and ext <= 255 * 256:
+    if ext <= 4096 * G and ext + 15 <= 255 * 256:
         return 256
     return 0
 
@@ -93,17 +95,17 @@ def tile_counts(offs, ext, ch):
     tile kernel's rules: clamped ends, an empty group keeps one chunk."""
     ends = np.clip(np.asarray(offs, dtype=np.int64), 0, ext)
     los = np.concatenate([[0], ends[:-1]])
-    n = np.maximum(ends - los, 0)
-    chunks = np.where(n > ch, (n + ch - 1) // ch, 1)
-    return int(chunks.sum()), int((n > ch).sum()), int(chunks.max(initial=1))
+    span = np.where(ends > los, ends - (los & ~15), 0)
+    chunks = np.where(span > ch, (span + ch - 1) // ch, 1)
+    return int(chunks.sum()), int((span > ch).sum()), int(chunks.max(initial=1))
 
 
 def check_tile(offs, ext):
     G = len(offs)
     for ch in (128, 256):
         chunks, nlong, most = tile_counts(offs, ext, ch)
-        assert chunks <= G + ext // ch
-        assert nlong <= min(G, ext // (ch + 1))
+        assert chunks <= G + (ext + 14 * G) // ch
+        assert nlong <= min(G, ext // (ch - 14))
         if tile_rows(ext, G) == ch:
             assert most <= 255
 
@@ -116,11 +118,11 @@ def test_library_agrees_on_the_workspace_size():
         pytest.skip("library not built")
     cases = ((16384, 4096, 8), (1000, 64, 1), (65536, 8, 256), (0, 8, 3), (65280, 264, 16),
              (65281, 264, 16), (16384, 4096, 2), (16384, 4100, 4), (16384, 4096, 256),
-             (32640, 264, 256), (32641, 264, 256))
+             (32625, 264, 256), (32626, 264, 256), (65265, 264, 16), (65266, 264, 16))
     for ext, cols, G in cases:
         ch = tile_rows(ext, G)
         if ch:
-            want = min(G, ext // (ch + 1)) * (-(-cols // 256)) * 264 * 4
+            want = min(G, ext // (ch - 14)) * (-(-cols // 256)) * 264 * 4
         else:
             want = bound(ext, G, True) * (-(-cols // 64)) * 72 * 4
         assert lib.mxq_jagged_colwise_workspace_bytes(ext, cols, G) == want, (ext, cols, G)

@@ -125,23 +125,24 @@ def test_most_chunks(extra):
 
 @pytest.mark.parametrize("extra", [0, 1])
 def test_tile_kernel_most_chunks(extra):
-    """255 chunks of 256 rows in one group, the tile kernel's limit (after 15
-    empty groups, which keep the average group within the tile kernel's; a
-    second 256-column tile of 8 columns), and one row more, where the call
-    takes the split kernel instead."""
-    rows = MAX_CHUNKS * TILE_CHUNK + extra
+    """255 chunks of 256 rows in one group, the tile kernel's limit: a
+    15-row group, 14 empty ones (which keep the average group within the
+    tile kernel's) and the long group, starting at row 15 so that its chunks
+    cover it from row 0; a second 256-column tile of 8 columns.  One row more
+    and the call takes the split kernel instead."""
+    rows = MAX_CHUNKS * TILE_CHUNK - 15 + extra
     bits = adversarial((rows, 264), 5450 + extra)
-    check(bits, np.array([0] * 15 + [rows], np.int32), what=f"{rows} rows")
+    check(bits, np.array([15] * 15 + [rows], np.int32), what=f"{rows} rows")
 
 
 @pytest.mark.parametrize("extra", [0, 1])
 def test_tile_kernel_one_tile_chunks_most(extra):
-    """255 chunks of 128 rows in one group after 255 empty groups (groups of
-    at most 128 rows on average take one-tile chunks), and one row more,
-    where the call takes two-tile chunks instead."""
-    rows = MAX_CHUNKS * 128 + extra
+    """255 chunks of 128 rows in one group (a 15-row group and 254 empty ones
+    before it: groups of at most 128 rows on average take one-tile chunks),
+    and one row more, where the call takes two-tile chunks instead."""
+    rows = MAX_CHUNKS * 128 - 15 + extra
     bits = adversarial((rows, 264), 5460 + extra)
-    check(bits, np.array([0] * 255 + [rows], np.int32), what=f"{rows} rows")
+    check(bits, np.array([15] * 255 + [rows], np.int32), what=f"{rows} rows")
 
 
 def test_previous_scales_in_the_slots():

@@ -77,10 +77,10 @@ def test_random_groups(rows, cols, G, mult, tail, seed):
 
 
 @pytest.mark.parametrize("rows,ends", [
-    (32640, [0] * 255 + [32640]),     # 255 one-tile chunks of 128 rows (short groups on average)
-    (32641, [0] * 255 + [32641]),     # one row more: two-tile chunks
-    (65280, [0] * 15 + [65280]),      # the tile kernel's limit: 255 chunks of 256 rows
-    (65281, [0] * 15 + [65281]),      # past it: the split kernel with the workspace
+    (32625, [15] * 255 + [32625]),    # 255 one-tile chunks of 128 rows from row 0 (short groups on average)
+    (32626, [15] * 255 + [32626]),    # one row more: two-tile chunks
+    (65265, [15] * 15 + [65265]),     # the tile kernel's limit: 255 chunks of 256 rows
+    (65266, [15] * 15 + [65266]),     # past it: the split kernel with the workspace
     (70000, [100, 69000, 70000]),     # long groups: the split kernel
 ])
 def test_kernel_limits(rows, ends):
