@@ -125,8 +125,8 @@ mxq_status mxq_quantize_jagged_rowwise(const uint16_t *x, int64_t rows, int64_t 
  * groups longer than the rows one workgroup holds are cut into chunks that
  * exchange each column's maximum through the group's own scale slots, so
  * every element is read once.  Chunks are 128 rows x 256 columns when
- * rows <= 32,640 and rows <= 128 * num_groups, 256 rows x 256 columns when
- * rows <= 65,280 and rows <= 4096 * num_groups, else 1536 rows x 64 columns
+ * rows <= 32,625 and rows <= 128 * num_groups, 256 rows x 256 columns when
+ * rows <= 65,265 and rows <= 4096 * num_groups, else 1536 rows x 64 columns
  * when rows <= 391,680.  Two kernels run in stream order: one zeroes those
  * slots, the second quantizes; while it runs the slots hold intermediate
  * words (maxima and counts), and at its end the scales.  Other extents read

@@ -1,7 +1,7 @@
 """GPU parity of the jagged colwise call WITHOUT a workspace on long token
 groups: chunks of one long group exchange their column maxima through the
 group's own fp32 scale slots (cleared by a small kernel first), so no row is
-read twice.  Up to 65,280 rows the call runs the tile kernel (chunks of 128
+read twice.  Up to 65,265 rows the call runs the tile kernel (chunks of 128
 or 256 rows x 256 columns, at most 255 per group); longer extents run the split
 kernel (chunks of 1536 rows x 64 columns, at most 255 per group).  Byte for
 byte against the oracle: one group of every row, groups at and past chunk

@@ -1,6 +1,6 @@
 """GPU parity of the jagged colwise call with a workspace (long token groups
 cut into chunks that exchange their column maxima through the workspace)
-against the oracle, byte for byte (the tile kernel up to 65,280 rows, the
+against the oracle, byte for byte (the tile kernel up to 65,265 rows, the
 split kernel beyond): the MoE backward operand at full size,
 one group of every row, groups just past chunk and tile multiples, starts off
 16-row boundaries, empty groups, rows past the last group, many groups, a
