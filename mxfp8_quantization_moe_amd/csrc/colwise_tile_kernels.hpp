@@ -10,9 +10,9 @@
 // at the group start rounded down to 16 rows (the scales are per group, so
 // any tiling will do, and 16-row pieces make whole 16-byte column stores); a
 // lane holds 16 rows x 8 columns per tile, in registers, so every element is
-// read from HBM once.  A group longer than
-// one chunk is cut into nu chunks per 256-column tile; the chunks of one
-// (group, column tile) exchange their 256 column maxima, either through a
+// read from HBM once.  A group longer than one chunk is cut into nu chunks
+// per 256-column tile; the chunks of one (group, column tile) exchange
+// their 256 column maxima, either through a
 // set of words in a caller's workspace or through the group's own fp32
 // scale slots (zeroed first by jagged_colwise_tile_clear_kernel), then each
 // quantizes its rows with the group's scales.  Every group, an empty one
@@ -81,7 +81,8 @@ __global__ __launch_bounds__(256) void jagged_colwise_tile_clear_kernel(
 // x (rows, cols) row-major with row pitch ldx; q column-major with column
 // pitch ldq; scales (G, cols) at g * ss_g + c * ss_c.  G <= kTileMaxGroups,
 // cols a multiple of 8, tiles_c = ceil(cols / 256); grid at least
-// tiles_c * (G + rows / (128 T)) workgroups of 256 threads (spare ones exit).
+// tiles_c * (G + (rows + 14 G) / (128 T)) workgroups of 256 threads (spare
+// ones exit).
 // ws: the workspace sets (null: exchange in the scale slots, which the
 // clear kernel has zeroed; then at most kSlotMaxChunks chunks per group),
 // nsets of them per column tile (offsets that break their precondition can
