@@ -40,10 +40,13 @@ def check_kernel(k):
 def test_default_headline_line():
     d = run_bench("--extras", "blockwise", timeout=850)
     for key, want in (("n_gpus", 1), ("steps", 10), ("warmup", 2), ("higher_is_better", True),
-                      ("scaling", "weak"), ("vs_baseline", None), ("data", "synthetic"), ("unit", "GB/s"),
+                      ("scaling", "weak"), ("data", "synthetic"), ("unit", "GB/s"),
                       ("dtype", "f32")):
         assert d[key] == want, key
     assert d["config"]["workload"] == "mx3d_E64_sweep"
+    # against the pages' own figure for this shape and metric (other hardware)
+    assert d["baseline"]["value"] == 4152.11 and d["baseline"]["unit"] == "GB/s"
+    assert abs(d["vs_baseline"] - d["value"] / 4152.11) < 1e-3
     assert d["value"] > 0 and d["ms_per_step"] > 0 and d["gpu_ms_per_step"] > 0
     roof = d["roofline"]
     assert roof["bound"] == "hbm" and roof["peak"] == 8000.0 and roof["unit"] == "GB/s"
@@ -92,4 +95,5 @@ def test_two_kernel_workload_and_options():
     slower = max(kernels.values(), key=lambda k: k["cold_us"]["median"])
     assert d["roofline"]["avg_launch_us"] == slower["cold_us"]["median"]
     assert d["workloads"] == {} and d["stream_ceiling"] is None and d["cpu_baseline"] is None
+    assert d["vs_baseline"] is None and "baseline" not in d   # no page figure for this workload
     assert set(d["inputs"]["sha256"]) == {"grad_out_t", "x"}
