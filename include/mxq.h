@@ -100,7 +100,11 @@ const char *mxq_status_string(int status);
  *         written, an empty group gets 448 / RN32(1e-12).
  * Layouts with a kernel: sx_c == 1 && sq_c == 1 (row-major in and out), and
  * sx_r == 1 && sq_c == 1 (a transposed view of a row-major tensor, e.g.
- * grad_out^T, into a row-major q).
+ * grad_out^T, into a row-major q).  For the second, with num_groups <= 256,
+ * cols <= 391,680 and distinct scale slots, groups longer than 1536 columns
+ * are split into chunks that exchange maxima through the group's scale
+ * slots: two kernels run in stream order (one zeroes those slots), and the
+ * slots hold intermediate words until the second ends.
  */
 mxq_status mxq_quantize_jagged_rowwise(const uint16_t *x, int64_t rows, int64_t cols, int64_t sx_r,
                                        int64_t sx_c, const int32_t *offs, int32_t num_groups,

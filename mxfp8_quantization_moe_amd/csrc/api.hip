@@ -542,10 +542,15 @@ mxq_status mxq_quantize_jagged_rowwise(const uint16_t *x, int64_t rows, int64_t 
     }
     if (sx_r == 1 && sq_c == 1) {
         // x is the transpose of a row-major (cols, rows) tensor: reduce across
-        // its rows, store column-major of that tensor == row-major q
+        // its rows, store column-major of that tensor == row-major q.  Long
+        // groups are split into chunks exchanging through the scale slots
+        // where they apply (the tile kernel's 256-column sets would touch
+        // slots G words apart: slower here), so no row is read twice
         if (sx_c % 8 != 0 || sq_r % 16 != 0)
             return MXQ_ERR_INVALID_ARG;
-        return run_jagged_strided(x, cols, rows, sx_c, offs, num_groups, q, sq_r, scales, ss_g, ss_r, st);
+        return run_jagged_strided(x, cols, rows, sx_c, offs, num_groups, q, sq_r, scales, ss_g, ss_r, st,
+                                  nullptr, 0, kColwiseSpinLimit,
+                                  colwise_in_slots(cols, rows, num_groups, ss_g, ss_r));
     }
     return MXQ_ERR_UNSUPPORTED;
 }

@@ -165,6 +165,23 @@ def test_rowwise_on_transposed_view_matches_row_major():
     assert_same_bytes(s, os_, "rowwise (transposed view) scales")
 
 
+@pytest.mark.parametrize("rows,cols,ends", [
+    (40, 7000, [17, 3100, 3100, 6999]),     # groups split into chunks, an empty group, a tail
+    (24, 20000, [3, 19999]),                # a long group starting off 16 columns
+    (16, 4608, [1536, 1537, 3073, 4608]),   # ends at and past chunk multiples
+])
+def test_rowwise_on_transposed_view_long_groups(rows, cols, ends):
+    """The transposed view with groups longer than a chunk: their chunks
+    exchange maxima through the scale slots."""
+    bits = adversarial((rows, cols), 33 + cols % 97)
+    offs = np.array(ends, np.int32)
+    view = bf16_dev(np.ascontiguousarray(bits.T)).t()
+    q, s = jagged_rowwise(view, i32_dev(offs))
+    oq, os_ = oracle.quantize_jagged_rowwise(bits, offs, canary=CANARY)
+    assert_same_bytes(q, oq, f"rowwise (transposed view) q {ends}")
+    assert_same_bytes(s, os_, f"rowwise (transposed view) scales {ends}")
+
+
 def test_colwise_on_column_major_input():
     rows, cols = 2500, 48
     bits = adversarial((rows, cols), 41)
